@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the ReLU linear self-attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full forward pass (state reduction over token chunks, the
+fixed-order combine, the apply) over one batch of synthetic input already
+resident in HBM. Prints one JSON line: tokens/s (B*N per step), the whole
+path's achieved HBM GB/s, a roofline record for the dominant kernel (its
+duration from HIP events recorded on the launch stream inside the timed
+region) and the CPU float64 oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E spec peak
+METRIC = "linear-attn fwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
+KERNELS_SRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc", "linattn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_latent_4096px.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU work budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNELS_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, budget_s: float):
+    """Time the CPU oracle on whole heads of the workload until the budget is
+    spent; report token-heads/s converted to tokens/s (all H heads of a
+    token)."""
+    import numpy as np
+    import oracle.linattn as L
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    done = 0
+    t0 = time.perf_counter()
+    decode_s = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            ta = time.perf_counter()
+            k = L.to_f64(inputs["k"][b, :, h, :], w.dtype)
+            v = L.to_f64(inputs["v"][b, :, h, :], w.dtype)
+            q = L.to_f64(inputs["q"][b, :, h, :], w.dtype)
+            tb = time.perf_counter()
+            kv, ks = L.kv_state(k, v)
+            L.apply_state(q, kv, ks, w.eps)
+            decode_s += tb - ta
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    token_heads = done * w.N
+    return {
+        "value": token_heads / wall / w.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} (b, h) heads x all {w.N} tokens, float64 NumPy "
+                  f"({wall:.1f} s wall incl. {decode_s:.1f} s bf16 decode); tokens/s = "
+                  f"token-heads/s / H",
+        "seconds": wall,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(the state reduction would shard over heads or tokens, see the "
+                          "design notes)"}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import relu_linear_attention_attn_amd as R
+    from relu_linear_attention_attn_amd import workloads as W
+
+    rank = int(os.environ.get("RANK", "0"))
+    wname = args.workload or W.HEADLINE
+    w = W.WORKLOADS[wname]
+    variant = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}[args.variant]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    R.lib()
+    log(args, f"workload {wname} {w.shape} {w.dtype}: generating inputs")
+    x = W.generate(w)
+    if w.dtype == "bf16":
+        dev = {t: torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).cuda() for t in "qkv"}
+    else:
+        dev = {t: torch.from_numpy(x[t]).cuda() for t in "qkv"}
+    out = torch.empty_like(dev["q"])
+    dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
+    ws = R.binding.alloc_workspace(w.B, w.N, w.H, dt, dev["q"].device)
+    stream = torch.cuda.current_stream()
+
+    def make_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # number of kernels of this variant
+    _, nk = R.forward_profiled(dev["q"], dev["k"], dev["v"], make_events(4), eps=w.eps, out=out,
+                               workspace=ws, variant=variant)
+    log(args, f"warmup {args.warmup} steps ({nk} kernels per step)")
+    for _ in range(args.warmup):
+        R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, out=out, workspace=ws, variant=variant)
+    events = [make_events(nk + 1) for _ in range(args.steps)]
+    for ev in events:  # create the HIP events outside the timed region
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    log(args, f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        R.forward_profiled(dev["q"], dev["k"], dev["v"], events[i], eps=w.eps, out=out,
+                           workspace=ws, variant=variant)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    names = ["fused"] if nk == 1 else ["reduce", "combine", "apply"]
+    per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+                  for j, n in enumerate(names)}
+    elem = w.B * w.N * w.H * w.d * w.itemsize
+    alg_bytes = {"reduce": 2 * elem, "combine": 0, "apply": 2 * elem, "fused": 4 * elem}
+    dominant = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dominant]
+    achieved = alg_bytes[dominant] / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dominant, wname)
+    path_gbps = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = w.B * w.N / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wname, "B": w.B, "N": w.N, "H": w.H, "d": w.d, "D": w.D,
+                   "variant": args.variant, "eps": w.eps},
+        "achieved_hbm_gbps": path_gbps,
+        "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
+        "kernel_ms": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+    }
+    if rank == 0 and args.cpu_seconds > 0:
+        log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    if rank == 0:
+        print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

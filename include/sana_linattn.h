@@ -1,0 +1,175 @@
+/*
+ * sana_linattn.h - C ABI of the ReLU linear self-attention forward pass
+ * (Sana's Linear DiT block) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation, per batch item b and head h, with x_n = x[b, n, h, :]:
+ *
+ *     phi(x)  = max(x, 0)
+ *     KV      = sum_n phi(k_n) v_n^T            (d x d)
+ *     ksum    = sum_n phi(k_n)                  (d)
+ *     out_i   = phi(q_i) KV / (phi(q_i) . ksum + eps)
+ *
+ * Sources: Sana course notes (papers-3lj.pages.dev, "08 Sana 高效高分辨率
+ * 生成"), section "Linear Attention 的原理" (phi = ReLU; KV = phi(K)^T V is a
+ * d x d matrix whatever n is; A = phi(Q) KV); Linear-DiT 4K blog
+ * (blog.hotdry.top), section "核心架构" (the normalised form
+ * phi(Q)(phi(K)^T V) / (phi(Q) phi(K)^T 1)); Sana paper review
+ * (phd-frog.tistory.com/40), section 2.2, "선형 어텐션 블럭" (ReLU linear
+ * attention; the shared terms computed once and reused by every query).
+ * eps is on no page: it is added to the denominator, outside the dot product.
+ * Attention is non-causal; no positional term touches q or k.
+ *
+ * Layout. q, k, v and out are dense, row-major [B][N][H][d] tensors of one
+ * dtype: element (b, n, h, c) sits at index ((b*N + n)*H + h)*d + c. This is
+ * the natural output layout of a (B, N, D = H*d) projection, so no transpose
+ * is needed. bf16 in gives bf16 out (fp32 accumulation, round-to-nearest-even
+ * on the final store); fp32 in gives fp32 out.
+ *
+ * The augmented state of one (b, h) is a d x (d+1) fp32 matrix, row-major:
+ * state[c][j] = KV[c][j] for j < d and state[c][d] = ksum[c]. It is the
+ * contraction phi(K)^T [V | 1]; its size does not depend on N.
+ *
+ * Ownership. Every pointer is a device pointer owned by the caller (q, k, v,
+ * out, state, workspace). The library allocates no device memory and keeps no
+ * per-call state. q, k and v are only read. out must not overlap q, k, v, the
+ * state or the workspace.
+ *
+ * Streams. Every call enqueues its kernels on `stream` (NULL = the default
+ * stream) and returns without synchronising. Results are defined once the
+ * stream reaches that point. Calls that share a workspace must be ordered on
+ * one stream.
+ *
+ * Errors. Calls return a status code and never throw. All argument checks run
+ * on the host before any HIP call, so an invalid call enqueues nothing. A
+ * failed kernel launch returns SANA_ERR_HIP.
+ *
+ * Domain. B, N, H >= 1; d == 32 (other head widths return
+ * SANA_ERR_UNSUPPORTED); B*N*H*d must fit in int64 and every tensor must be
+ * addressable (total bytes < 2^62). eps must be finite and >= 0; with
+ * eps = 0 a query row with phi(q_i) = 0 gives 0/0 = NaN, otherwise such a row
+ * gives exactly 0. Tensor pointers must be 16-byte aligned
+ * (SANA_ERR_ALIGNMENT otherwise). Inputs must be finite.
+ */
+#ifndef SANA_LINATTN_H
+#define SANA_LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SANA_LINATTN_VERSION 1
+
+typedef enum {
+  SANA_DTYPE_F32 = 0,  /* IEEE binary32 in and out */
+  SANA_DTYPE_BF16 = 1  /* bfloat16 in and out, fp32 accumulation */
+} sana_dtype_t;
+
+typedef enum {
+  SANA_OK = 0,
+  SANA_ERR_INVALID_ARG = 1,  /* null pointer, size < 1, overflow, bad eps, overlap */
+  SANA_ERR_UNSUPPORTED = 2,  /* d != 32, unknown dtype or variant */
+  SANA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the query says */
+  SANA_ERR_ALIGNMENT = 4,    /* a tensor pointer is not 16-byte aligned */
+  SANA_ERR_HIP = 5           /* a HIP launch failed */
+} sana_status_t;
+
+typedef enum {
+  SANA_VARIANT_AUTO = 0,   /* library picks by shape */
+  SANA_VARIANT_SPLIT = 1,  /* split-N state reduction, fixed-order combine, apply */
+  SANA_VARIANT_FUSED = 2   /* one launch per (b, head pair): reduce into LDS, then apply */
+} sana_variant_t;
+
+/*
+ * Bytes of device workspace that sana_linattn_fwd, sana_linattn_fwd_variant
+ * and sana_linattn_kv_state need for this shape. The size depends on
+ * (B, N, H, d) only through the number of token chunks of the split
+ * reduction, which stops growing once N is large: it is constant for N at
+ * or above a fixed threshold (the state is independent of n). Every variant
+ * uses at most this many bytes. Writes *bytes; returns SANA_OK or an
+ * argument error (same checks as the forward call).
+ */
+sana_status_t sana_linattn_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
+                                          int dtype, size_t* bytes);
+
+/*
+ * The forward pass: out = phi(Q)(phi(K)^T [V|1]) split into numerator and
+ * normaliser, per (b, h). Equivalent to sana_linattn_fwd_variant with
+ * SANA_VARIANT_AUTO. workspace must hold at least
+ * sana_linattn_workspace_size(...) bytes (it may be NULL only when that size
+ * is 0), be 256-byte aligned, and must not be used by another call in flight.
+ * Its contents on entry do not matter and are undefined on return.
+ */
+sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out,
+                               int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                               int dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Same as sana_linattn_fwd with an explicit kernel variant (sana_variant_t).
+ * Every variant computes the same function; results of one variant are
+ * bitwise repeatable for the same inputs and shape.
+ */
+sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void* v, void* out,
+                                       int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                       int dtype, int variant, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sana_linattn_fwd_variant that also times its kernels: it records events[0]
+ * on `stream` before the first kernel and events[i] right after kernel i, so
+ * hipEventElapsedTime(events[i-1], events[i]) is the duration of kernel i.
+ * The kernels, in order: SPLIT - state reduction over token chunks, fixed-
+ * order combine of the chunk partials, apply; FUSED - the single fused
+ * kernel. *n_kernels (if not NULL) receives that count (3 or 1) even when
+ * the call fails. The events are created by the caller (hipEventCreate);
+ * n_events must be at least *n_kernels + 1, else SANA_ERR_INVALID_ARG.
+ * Computes exactly what sana_linattn_fwd_variant computes.
+ */
+sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void* v, void* out,
+                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                        int dtype, int variant, void* workspace,
+                                        size_t workspace_bytes, hipEvent_t* events,
+                                        int n_events, int* n_kernels, hipStream_t stream);
+
+/*
+ * First half of the forward pass: the augmented state of every (b, h),
+ * written to `state` as fp32 [B][H][d][d+1] (see the layout note above), by
+ * a split-N reduction over token chunks and a fixed-order sum of the chunk
+ * partials (deterministic, no float atomics). workspace as for
+ * sana_linattn_fwd. The state is additive over tokens: states of disjoint
+ * token ranges sum to the state of their union.
+ */
+sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state,
+                                    int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * Second half of the forward pass: out_i = phi(q_i) KV / (phi(q_i) . ksum + eps)
+ * for every token of every (b, h), reading `state` (fp32 [B][H][d][d+1], as
+ * written by sana_linattn_kv_state or computed elsewhere, e.g. summed over
+ * token shards). q and out as for sana_linattn_fwd. Needs no workspace.
+ */
+sana_status_t sana_linattn_apply(const void* q, const float* state, void* out,
+                                 int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                 int dtype, hipStream_t stream);
+
+/* Bytes of one [B][H][d][d+1] fp32 state (0 and SANA_ERR_* on bad arguments). */
+sana_status_t sana_linattn_state_size(int64_t B, int64_t H, int64_t d, size_t* bytes);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* sana_linattn_strerror(int status);
+
+/* SANA_LINATTN_VERSION of the built library. */
+int sana_linattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANA_LINATTN_H */

@@ -2,5 +2,22 @@
 
 The compute runs in hand-written HIP kernels behind a C ABI
 (``libsana_linattn.so``, declared in ``include/sana_linattn.h``); this package
-is a thin ctypes binding plus the seeded workload generator.
+is a thin ctypes binding plus the seeded workload generator. The library is
+loaded on first use and every call raises if it has not been built.
 """
+from .binding import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    VARIANT_AUTO,
+    VARIANT_FUSED,
+    VARIANT_SPLIT,
+    SanaError,
+    apply,
+    forward,
+    forward_profiled,
+    kv_state,
+    lib,
+    state_size,
+    strerror,
+    workspace_size,
+)

@@ -1,0 +1,272 @@
+"""ctypes binding of libsana_linattn.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+declared in include/sana_linattn.h. PyTorch supplies device memory and the
+current stream. There is no fallback: if the library is not built, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+LIB_NAME = "libsana_linattn.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+VARIANT_AUTO = 0
+VARIANT_SPLIT = 1
+VARIANT_FUSED = 2
+HEAD_DIM = 32
+
+STATUS = {
+    0: "SANA_OK",
+    1: "SANA_ERR_INVALID_ARG",
+    2: "SANA_ERR_UNSUPPORTED",
+    3: "SANA_ERR_WORKSPACE",
+    4: "SANA_ERR_ALIGNMENT",
+    5: "SANA_ERR_HIP",
+}
+EXPORTS = (
+    "sana_linattn_workspace_size",
+    "sana_linattn_fwd",
+    "sana_linattn_fwd_variant",
+    "sana_linattn_fwd_profiled",
+    "sana_linattn_kv_state",
+    "sana_linattn_apply",
+    "sana_linattn_state_size",
+    "sana_linattn_strerror",
+    "sana_linattn_version",
+)
+
+
+class SanaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+_lock = threading.Lock()
+_lib: Optional[ctypes.CDLL] = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python relu_linear_attention_attn_amd/csrc/build.py` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sana_linattn_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                                  ctypes.POINTER(_sz)]
+        L.sana_linattn_state_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
+        L.sana_linattn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                       ctypes.c_float, ctypes.c_int, _vp, _sz, _vp]
+        L.sana_linattn_fwd_variant.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                               ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
+                                               _sz, _vp]
+        L.sana_linattn_fwd_profiled.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
+                                                _sz, ctypes.POINTER(_vp), ctypes.c_int,
+                                                ctypes.POINTER(ctypes.c_int), _vp]
+        L.sana_linattn_kv_state.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                            _vp, _sz, _vp]
+        L.sana_linattn_apply.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                         ctypes.c_int, _vp]
+        for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
+                     "sana_linattn_fwd", "sana_linattn_fwd_variant", "sana_linattn_fwd_profiled",
+                     "sana_linattn_kv_state",
+                     "sana_linattn_apply"):
+            getattr(L, name).restype = ctypes.c_int
+        L.sana_linattn_strerror.argtypes = [ctypes.c_int]
+        L.sana_linattn_strerror.restype = ctypes.c_char_p
+        L.sana_linattn_version.argtypes = []
+        L.sana_linattn_version.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def strerror(status: int) -> str:
+    return lib().sana_linattn_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise SanaError(status, where)
+
+
+def workspace_size(B: int, N: int, H: int, d: int = HEAD_DIM, dtype: int = DTYPE_BF16) -> int:
+    n = _sz(0)
+    _check(lib().sana_linattn_workspace_size(B, N, H, d, dtype, ctypes.byref(n)),
+           "sana_linattn_workspace_size")
+    return n.value
+
+
+def state_size(B: int, H: int, d: int = HEAD_DIM) -> int:
+    n = _sz(0)
+    _check(lib().sana_linattn_state_size(B, H, d, ctypes.byref(n)), "sana_linattn_state_size")
+    return n.value
+
+
+# ------------------------------------------------------------ torch glue
+
+
+def _torch():
+    import torch  # imported lazily: the CPU-only tests never need it here
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def _shape(x, heads: Optional[int]) -> Tuple[int, int, int, int]:
+    if x.dim() == 4:
+        B, N, H, d = x.shape
+        if heads is not None and heads != H:
+            raise ValueError("heads does not match the tensor's head axis")
+        return B, N, H, d
+    if x.dim() == 3:
+        if heads is None:
+            raise ValueError("a (B, N, D) tensor needs heads=")
+        B, N, D = x.shape
+        if D % heads:
+            raise ValueError("D is not a multiple of heads")
+        return B, N, heads, D // heads
+    raise ValueError("expected a (B, N, H, d) or (B, N, D) tensor")
+
+
+def _check_tensor(x, name: str, like=None):
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous ([B][N][H][d] row-major)")
+    if like is not None and (x.dtype != like.dtype or x.shape != like.shape or
+                             x.device != like.device):
+        raise ValueError(f"{name} must match q in dtype, shape and device")
+
+
+def _stream(x) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(x.device).cuda_stream
+
+
+def alloc_workspace(B: int, N: int, H: int, dtype: int, device):
+    """A workspace for this shape (torch-owned, 256-byte aligned)."""
+    torch = _torch()
+    n = workspace_size(B, N, H, HEAD_DIM, dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, eps: float = 1e-6, heads: Optional[int] = None, out=None,
+            workspace=None, variant: int = VARIANT_AUTO):
+    """out = phi(Q)(phi(K)^T [V|1]) split into numerator and normaliser, per head.
+
+    q, k, v: contiguous GPU tensors (B, N, H, d) or (B, N, D) with heads=, all
+    bf16 or all fp32. Enqueued on torch's current stream; no synchronisation."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q)
+    _check_tensor(v, "v", q)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q)
+    if workspace is None:
+        workspace = alloc_workspace(B, N, H, dt, q.device)
+    _check(lib().sana_linattn_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), B, N, H, d, float(eps), dt,
+                                          int(variant), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(q)),
+           "sana_linattn_fwd_variant")
+    return out
+
+
+def forward_profiled(q, k, v, events, eps: float = 1e-6, heads: Optional[int] = None,
+                     out=None, workspace=None, variant: int = VARIANT_AUTO):
+    """forward() that records ``events`` (torch.cuda.Event, enable_timing=True)
+    around each kernel it launches: events[0] before the first, events[i]
+    after kernel i. Returns (out, number of kernels)."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q)
+    _check_tensor(v, "v", q)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(B, N, H, dt, q.device)
+    for e in events:
+        if e.cuda_event == 0:  # torch creates the HIP event on first record
+            e.record()
+    arr = (_vp * len(events))(*[e.cuda_event for e in events])
+    nk = ctypes.c_int(0)
+    _check(lib().sana_linattn_fwd_profiled(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), B, N, H, d, float(eps), dt,
+                                           int(variant), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), arr,
+                                           len(events), ctypes.byref(nk), _stream(q)),
+           "sana_linattn_fwd_profiled")
+    return out, nk.value
+
+
+def kv_state(k, v, heads: Optional[int] = None, state=None, workspace=None):
+    """The fp32 [B, H, d, d+1] state phi(K)^T [V | 1] of every (b, h)."""
+    torch = _torch()
+    B, N, H, d = _shape(k, heads)
+    _check_tensor(k, "k")
+    _check_tensor(v, "v", k)
+    dt = _dtype_code(k)
+    if state is None:
+        state = torch.empty((B, H, d, d + 1), dtype=torch.float32, device=k.device)
+    elif state.dtype != torch.float32 or state.numel() != B * H * d * (d + 1) or \
+            not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor of B*H*d*(d+1) elements")
+    if workspace is None:
+        workspace = alloc_workspace(B, N, H, dt, k.device)
+    _check(lib().sana_linattn_kv_state(k.data_ptr(), v.data_ptr(), state.data_ptr(), B, N, H, d,
+                                       dt, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(k)),
+           "sana_linattn_kv_state")
+    return state
+
+
+def apply(q, state, eps: float = 1e-6, heads: Optional[int] = None, out=None):
+    """out_i = phi(q_i) KV / (phi(q_i) . ksum + eps) from a [B, H, d, d+1] state."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    dt = _dtype_code(q)
+    if state.dtype != torch.float32 or state.numel() != B * H * d * (d + 1) or \
+            not state.is_contiguous() or not state.is_cuda:
+        raise ValueError("state must be a contiguous fp32 GPU tensor of B*H*d*(d+1) elements")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q)
+    _check(lib().sana_linattn_apply(q.data_ptr(), state.data_ptr(), out.data_ptr(), B, N, H, d,
+                                    float(eps), dt, _stream(q)),
+           "sana_linattn_apply")
+    return out

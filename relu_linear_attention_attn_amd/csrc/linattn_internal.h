@@ -1,0 +1,48 @@
+// Internal interface between the C ABI (api.cpp) and the HIP kernels
+// (linattn_kernels.hip). Not installed; the public header is
+// include/sana_linattn.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace sana {
+
+constexpr int kHeadDim = 32;                          // d
+constexpr int kStateCols = kHeadDim + 1;              // d + 1: KV columns, then ksum
+constexpr int kStateFloats = kHeadDim * kStateCols;   // 1056 floats = 4224 bytes
+constexpr int kTile = 16;                             // tokens per wave iteration
+constexpr int kHeadsPerBlock = 2;                     // a head pair shares 128-byte lines (bf16)
+
+// Work split of one call, derived from the shape only (so the workspace query
+// and the launch agree).
+struct Plan {
+  int64_t B, N, H;
+  int64_t pairs;          // ceil(H / 2) head pairs per batch item
+  int64_t units;          // B * pairs: blocks per token chunk
+  int64_t red_chunk;      // tokens per reduction chunk (multiple of kTile)
+  int64_t red_chunks;     // chunks actually used (<= red_chunks_max)
+  int64_t red_chunks_max; // chunks the workspace is sized for
+  int64_t app_chunk;      // tokens per apply chunk (multiple of kTile)
+  int64_t app_chunks;
+  size_t partial_bytes;   // workspace bytes for chunk partials
+  size_t state_bytes;     // workspace bytes for the combined state
+  size_t workspace_bytes; // total
+};
+
+Plan make_plan(int64_t B, int64_t N, int64_t H);
+
+// Launchers. They enqueue on `stream` and return the launch status.
+// dtype: 0 = fp32, 1 = bf16 (sana_dtype_t).
+hipError_t launch_reduce(const Plan& p, int dtype, const void* k, const void* v,
+                         float* partials, hipStream_t stream);
+hipError_t launch_combine(const Plan& p, const float* partials, float* state,
+                          hipStream_t stream);
+hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state,
+                        void* out, float eps, hipStream_t stream);
+hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k,
+                        const void* v, void* out, float eps, hipStream_t stream);
+
+}  // namespace sana

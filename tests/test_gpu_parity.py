@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path against the CPU float64 oracle, element by element,
+through the C ABI (ctypes binding), on the same seeded input bits.
+
+Tolerances (written here, derived in the design notes): bf16 max-abs <= 1e-2
+and rel-L2 <= 5e-3; fp32 rel-L2 <= 1e-5 and max-abs <= 1e-5 * max|ref|.
+"""
+import numpy as np
+import pytest
+
+import oracle.linattn as L
+import relu_linear_attention_attn_amd as R
+from relu_linear_attention_attn_amd import workloads as W
+
+from gpu_util import assert_close, decode, metrics, to_device, to_host, torch
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    assert t.cuda.is_available(), "GPU tests need a ROCm GPU"
+    R.lib()  # loud failure if the HIP library is missing
+    yield
+
+
+def _inputs(w):
+    x = W.generate(w)
+    return x, {t: to_device(x[t], w.dtype) for t in "qkv"}
+
+
+def _run(w, dev, variant=R.VARIANT_AUTO):
+    out = R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=variant)
+    torch().cuda.synchronize()
+    return decode(to_host(out, w.dtype), w.dtype)
+
+
+def _oracle(w, x):
+    return L.linattn_from_inputs(x["q"], x["k"], x["v"], w.eps, w.dtype)
+
+
+# ------------------------------------------------------- named workloads
+
+SMALL = ["tiny_f32", "sana06_1024px", "sana16_1024px_b16", "latent_4096px"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_matches_oracle_all_variants(name):
+    w = W.WORKLOADS[name]
+    print(f"\n[case] workload {name} shape {w.shape} {w.dtype}", flush=True)
+    x, dev = _inputs(w)
+    ref = _oracle(w, x)
+    for vname, var in VARIANTS.items():
+        got = _run(w, dev, var)
+        assert_close(got, ref, w.dtype, f"{name}/{vname}")
+
+
+def test_tiny_f32_matches_quadratic_form():
+    """The fp32 workload is small enough for the explicit n x n form too."""
+    w = W.WORKLOADS["tiny_f32"]
+    x, dev = _inputs(w)
+    f = {t: decode(x[t], "f32") for t in "qkv"}
+    ref = L.quadratic_fp64(f["q"], f["k"], f["v"], w.eps)
+    assert_close(_run(w, dev), ref, "f32", "tiny_f32 vs quadratic form")
+
+
+# ----------------------------------------------------------- ragged cases
+
+RAGGED = [
+    (1, 1, 1), (1, 2, 2), (2, 15, 3), (1, 16, 1), (3, 17, 5), (1, 100, 2), (2, 257, 3),
+    (1, 1000, 7), (2, 4099, 4), (1, 33000, 3),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,N,H", RAGGED)
+def test_ragged_shapes(B, N, H, dtype):
+    w = W.custom(f"ragged_{B}_{N}_{H}", B, N, H, dtype=dtype, seed=100 + N + H,
+                 q=W.Dist("normal", 0.1, 1.0), k=W.Dist("normal", 0.1, 1.0))
+    print(f"\n[case] ragged B={B} N={N} H={H} {dtype}", flush=True)
+    x, dev = _inputs(w)
+    ref = _oracle(w, x)
+    for vname, var in VARIANTS.items():
+        assert_close(_run(w, dev, var), ref, dtype, f"B={B} N={N} H={H} {dtype} {vname}")
+
+
+# ------------------------------------------------------ state and apply halves
+
+
+@pytest.mark.parametrize("name", ["sana06_1024px", "latent_4096px"])
+def test_kv_state_matches_oracle(name):
+    w = W.WORKLOADS[name]
+    print(f"\n[case] kv_state {name}", flush=True)
+    x, dev = _inputs(w)
+    st = R.kv_state(dev["k"], dev["v"])
+    torch().cuda.synchronize()
+    got = st.cpu().numpy().astype(np.float64)
+    ref = L.state_from_inputs(x["k"], x["v"], w.dtype)
+    maxabs, rel, refmax = metrics(got, ref)
+    print(f"state rel-L2 {rel:.3e} max-abs {maxabs:.3e} max|ref| {refmax:.3e}", flush=True)
+    # bf16 x bf16 products are exact in fp32; only the fp32 sums round
+    assert rel <= 2e-6 * max(1.0, np.sqrt(w.N / 1024)), rel
+
+
+def test_apply_from_oracle_state():
+    """The apply kernel alone, fed the oracle's state rounded to fp32."""
+    w = W.WORKLOADS["sana16_1024px_b16"]
+    x, dev = _inputs(w)
+    st64 = L.state_from_inputs(x["k"], x["v"], w.dtype)
+    st = torch().from_numpy(st64.astype(np.float32)).cuda()
+    out = R.apply(dev["q"], st, eps=w.eps)
+    torch().cuda.synchronize()
+    got = decode(to_host(out, w.dtype), w.dtype)
+    # reference from the same fp32-rounded state
+    ref = np.empty_like(got)
+    st32 = st64.astype(np.float32).astype(np.float64)
+    for b in range(w.B):
+        ref[b] = L.apply_rows(decode(x["q"][b], w.dtype), st32[b], w.eps)
+    assert_close(got, ref, w.dtype, "apply from oracle state")
+
+
+def test_state_is_additive_over_token_ranges():
+    """States of two token halves, summed, equal the state of the whole."""
+    w = W.custom("additive", 2, 5000, 6, seed=77)
+    x, dev = _inputs(w)
+    whole = R.kv_state(dev["k"], dev["v"])
+    a = R.kv_state(dev["k"][:, :2000].contiguous(), dev["v"][:, :2000].contiguous())
+    b = R.kv_state(dev["k"][:, 2000:].contiguous(), dev["v"][:, 2000:].contiguous())
+    torch().cuda.synchronize()
+    _, rel, _ = metrics((a + b).cpu().numpy().astype(np.float64),
+                        whole.cpu().numpy().astype(np.float64))
+    assert rel < 1e-6, rel
+
+
+# ------------------------------------------------------------- invariants
+
+
+def test_dead_query_rows_are_exactly_zero():
+    """Workload sana16_1024px_b16 makes 2% of Q rows all-negative: phi(q) = 0,
+    so those output rows must be exactly 0 (num = 0, den + eps = eps)."""
+    w = W.WORKLOADS["sana16_1024px_b16"]
+    x, dev = _inputs(w)
+    rows = W.masked_rows(w)
+    for vname, var in VARIANTS.items():
+        out = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), "bf16")
+        flat = out.reshape(w.B * w.N, -1)
+        assert np.all((flat[rows] & 0x7FFF) == 0), vname   # +0 or -0
+        live = np.setdiff1d(np.arange(w.B * w.N), rows)[:500]
+        assert np.all(np.any((flat[live] & 0x7FFF) != 0, axis=1)), vname
+
+
+def test_dead_key_tokens_do_not_matter_bitwise():
+    """Workload sana06_1024px makes 5% of K rows all-negative: phi(k) = 0, so
+    replacing their V rows leaves the output bitwise unchanged."""
+    w = W.WORKLOADS["sana06_1024px"]
+    x, dev = _inputs(w)
+    rows = W.masked_rows(w)
+    v2 = x["v"].reshape(w.B * w.N, -1).copy()
+    rng = np.random.default_rng(9)
+    v2[rows] = W.f32_to_bf16_bits(rng.standard_normal((len(rows), w.D)).astype(np.float32) * 7)
+    dv2 = to_device(v2.reshape(w.shape), "bf16")
+    for vname, var in VARIANTS.items():
+        a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), "bf16")
+        b = to_host(R.forward(dev["q"], dev["k"], dv2, eps=w.eps, variant=var), "bf16")
+        assert np.array_equal(a, b), vname
+
+
+@pytest.mark.parametrize("name", ["sana06_1024px", "latent_4096px"])
+def test_repeat_calls_are_bitwise_identical(name):
+    w = W.WORKLOADS[name]
+    x, dev = _inputs(w)
+    for vname, var in VARIANTS.items():
+        a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), w.dtype)
+        for _ in range(3):
+            b = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), w.dtype)
+            assert np.array_equal(a, b), vname
+
+
+def test_scaling_k_by_two_changes_at_most_one_ulp():
+    """phi(2k) = 2 phi(k) and doubling is exact in bf16 and fp32, so the state
+    doubles exactly; the output moves only through eps, i.e. by at most one
+    bf16 rounding step."""
+    w = W.WORKLOADS["sana06_1024px"]
+    x, dev = _inputs(w)
+    a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps), "bf16").astype(np.int32)
+    b = to_host(R.forward(dev["q"], dev["k"] * 2, dev["v"], eps=w.eps), "bf16").astype(np.int32)
+    # compare as sign-magnitude integers: adjacent bf16 values differ by 1
+    def ordered(u):
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    assert np.max(np.abs(ordered(a) - ordered(b))) <= 1
+
+
+def test_convex_combination_bound():
+    w = W.WORKLOADS["sana06_1024px"]
+    x, dev = _inputs(w)
+    got = _run(w, dev)
+    v = decode(x["v"], "bf16")
+    lo = np.minimum(v.min(axis=1, keepdims=True), 0)
+    hi = np.maximum(v.max(axis=1, keepdims=True), 0)
+    ulp = 2.0 ** -7 * np.maximum(np.abs(got), 2.0 ** -126)  # one bf16 ulp
+    assert np.all(got >= lo - ulp) and np.all(got <= hi + ulp)
+
+
+def test_output_canaries_untouched():
+    """Bytes just before and after `out` keep their values."""
+    t = torch()
+    w = W.custom("canary", 2, 1000, 3, seed=5)
+    x, dev = _inputs(w)
+    n = w.B * w.N * w.H * w.d
+    pad = 4096
+    for vname, var in VARIANTS.items():
+        buf = t.full((n + 2 * pad,), 12345, dtype=t.int16, device="cuda")
+        out = buf[pad:pad + n].view(t.bfloat16).view(w.shape)
+        R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, out=out, variant=var)
+        t.cuda.synchronize()
+        host = buf.cpu().numpy()
+        assert np.all(host[:pad] == 12345) and np.all(host[pad + n:] == 12345), vname
+
+
+def test_heads_given_as_flat_width():
+    """(B, N, D) tensors with heads= are the same memory as (B, N, H, d)."""
+    w = W.WORKLOADS["sana06_1024px"]
+    x, dev = _inputs(w)
+    a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps), "bf16")
+    flat = {k: t.view(w.B, w.N, w.D) for k, t in dev.items()}
+    b = to_host(R.forward(flat["q"], flat["k"], flat["v"], eps=w.eps, heads=w.H), "bf16")
+    assert np.array_equal(a.reshape(-1), b.reshape(-1))
+
+
+def test_errors_enqueue_nothing():
+    t = torch()
+    w = W.custom("err", 1, 64, 2, seed=1)
+    x, dev = _inputs(w)
+    out = t.full_like(dev["q"], 3.0)
+    L_ = R.lib()
+    ws = t.empty(R.workspace_size(1, 64, 2), dtype=t.uint8, device="cuda")
+    q, k, v = (dev[c].data_ptr() for c in "qkv")
+    st = t.cuda.current_stream().cuda_stream
+    assert L_.sana_linattn_fwd(q, k, v, out.data_ptr(), 1, 64, 2, 32, -1.0, 1, ws.data_ptr(),
+                               ws.numel(), st) == 1
+    assert L_.sana_linattn_fwd(q, k, v, out.data_ptr(), 1, 64, 2, 32, 1e-6, 1, ws.data_ptr(),
+                               16, st) == 3
+    assert L_.sana_linattn_fwd(q + 2, k, v, out.data_ptr(), 1, 64, 2, 32, 1e-6, 1,
+                               ws.data_ptr(), ws.numel(), st) == 4
+    t.cuda.synchronize()
+    assert bool((out == 3.0).all())
+
+
+# --------------------------------------------- 1M tokens, sampled outputs
+
+
+@pytest.mark.timeout(900)
+def test_video_1m_tokens_sampled():
+    """B=1, N=1,048,576, H=36, t(4) heavy-tailed Q and K: the full state is
+    checked against the oracle's, and outputs on sampled token rows (plus the
+    first and last rows and chunk edges) element by element."""
+    w = W.WORKLOADS["video_1m_tokens"]
+    x, dev = {}, {}
+    for t in "qkv":
+        print(f"\n[case] {w.name}: generating {t}", flush=True)
+        x[t] = W.generate_tensor(w, t)
+        dev[t] = to_device(x[t], "bf16")
+    print("[case] running the HIP path", flush=True)
+    out = R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps)
+    st = R.kv_state(dev["k"], dev["v"])
+    torch().cuda.synchronize()
+    rng = np.random.default_rng(2024)
+    rows = np.unique(np.concatenate([rng.choice(w.N, 4096, replace=False),
+                                     [0, 1, 15, 16, 17, w.N - 17, w.N - 1],
+                                     np.arange(0, w.N, 18432)[:64]]))
+    got = decode(to_host(out[0, rows], "bf16"), "bf16")
+    print("[case] oracle state over 1M tokens", flush=True)
+    ref_state = L.state_from_inputs(x["k"], x["v"], "bf16")
+    _, srel, _ = metrics(st.cpu().numpy().astype(np.float64), ref_state)
+    print(f"state rel-L2 {srel:.3e}", flush=True)
+    assert srel < 1e-4
+    ref = L.apply_rows(decode(x["q"][0, rows], "bf16"), ref_state[0], w.eps)
+    assert_close(got, ref, "bf16", "video_1m_tokens sampled rows")
