@@ -80,7 +80,7 @@ typedef enum {
 
 typedef enum {
   SANA_VARIANT_AUTO = 0,   /* library picks by shape */
-  SANA_VARIANT_SPLIT = 1,  /* split-N state reduction, fixed-order combine, apply */
+  SANA_VARIANT_SPLIT = 1,  /* split-N state reduction with a fixed-order fold, then apply */
   SANA_VARIANT_FUSED = 2   /* one launch per (b, head pair): reduce into LDS, then apply */
 } sana_variant_t;
 
@@ -102,7 +102,8 @@ sana_status_t sana_linattn_workspace_size(int64_t B, int64_t N, int64_t H, int64
  * SANA_VARIANT_AUTO. workspace must hold at least
  * sana_linattn_workspace_size(...) bytes (it may be NULL only when that size
  * is 0), be 256-byte aligned, and must not be used by another call in flight.
- * Its contents on entry do not matter and are undefined on return.
+ * Its contents on entry do not matter (it needs no clearing, ever) and are
+ * undefined on return.
  */
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out,
                                int64_t B, int64_t N, int64_t H, int64_t d, float eps,
@@ -123,10 +124,10 @@ sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void*
  * sana_linattn_fwd_variant that also times its kernels: it records events[0]
  * on `stream` before the first kernel and events[i] right after kernel i, so
  * hipEventElapsedTime(events[i-1], events[i]) is the duration of kernel i.
- * The kernels, in order: SPLIT - state reduction over token chunks, fixed-
- * order combine of the chunk partials, apply; FUSED - the single fused
- * kernel. *n_kernels (if not NULL) receives that count (3 or 1) even when
- * the call fails. The events are created by the caller (hipEventCreate);
+ * The kernels, in order: SPLIT - the state reduction over token chunks
+ * (whose last block per head pair folds the chunk partials into the state in
+ * fixed order), then the apply; FUSED - the single fused kernel. *n_kernels
+ * (if not NULL) receives that count (2 or 1) even when the call fails. The events are created by the caller (hipEventCreate);
  * n_events must be at least *n_kernels + 1, else SANA_ERR_INVALID_ARG.
  * Computes exactly what sana_linattn_fwd_variant computes.
  */

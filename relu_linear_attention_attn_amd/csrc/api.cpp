@@ -9,22 +9,33 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "linattn_internal.h"
 
 namespace sana {
 namespace {
 
-constexpr int64_t kTargetReduceBlocks = 1024;  // 4 blocks (16 waves) per CU on 256 CUs
-constexpr int64_t kTargetApplyBlocks = 2048;
 constexpr int64_t kMinReduceChunk = 256;       // tokens: 8 tiles per wave at 2 sub-streams
 constexpr int64_t kMinApplyChunk = 256;
+constexpr int64_t kWorkspaceBlocks = 4096;     // reduction blocks the workspace allows for
 constexpr int64_t kMaxReduceChunks = 64;
-constexpr int64_t kMaxApplyChunks = 1 << 20;
+constexpr int64_t kMaxRounds = 4;              // block rounds considered when fitting the grid
 constexpr int64_t kFusedMaxN = 1024;           // AUTO picks the fused kernel up to this N
+constexpr int64_t kReduceWavesPerCu = 8;
 constexpr size_t kAlign = 256;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tokens per chunk for `chunks` chunks of N, in whole tiles. An even tile
+// count is made odd: chunk starts then do not share the high power-of-two
+// alignment that would send every chunk's stream to the same HBM channels.
+int64_t chunk_tokens(int64_t N, int64_t chunks) {
+  int64_t tiles = cdiv(cdiv(N, chunks), kTile);
+  if (tiles > 1 && tiles % 2 == 0) ++tiles;
+  return tiles * kTile;
+}
 int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -70,22 +81,92 @@ Plan make_plan(int64_t B, int64_t N, int64_t H) {
   p.H = H;
   p.pairs = cdiv(H, kHeadsPerBlock);
   p.units = B * p.pairs;
-  // Split-N reduction: enough chunks to fill the chip, each at least
-  // kMinReduceChunk tokens. Once N >= kMinReduceChunk * red_chunks_max the
-  // count no longer depends on N, nor does the workspace.
-  p.red_chunks_max = clamp64(cdiv(kTargetReduceBlocks, p.units), 1, kMaxReduceChunks);
-  const int64_t want = clamp64(cdiv(N, kMinReduceChunk), 1, p.red_chunks_max);
-  p.red_chunk = cdiv(cdiv(N, want), kTile) * kTile;
+  // The workspace holds up to red_chunks_max chunk partials per head. The
+  // bound stops depending on N once N >= kMinReduceChunk * red_chunks_max.
+  p.red_chunks_max = clamp64(std::min(cdiv(kWorkspaceBlocks, p.units), cdiv(N, kMinReduceChunk)),
+                             1, kMaxReduceChunks);
+  p.red_chunk = chunk_tokens(N, p.red_chunks_max);
   p.red_chunks = cdiv(N, p.red_chunk);
-  const int64_t awant = clamp64(std::min(cdiv(kTargetApplyBlocks, p.units), cdiv(N, kMinApplyChunk)),
-                                1, kMaxApplyChunks);
-  p.app_chunk = cdiv(cdiv(N, awant), kTile) * kTile;
-  p.app_chunks = cdiv(N, p.app_chunk);
+  p.app_chunk = cdiv(N, kTile) * kTile;
+  p.app_chunks = 1;
   const size_t bh = static_cast<size_t>(B * H);
   p.partial_bytes = align_up(static_cast<size_t>(p.red_chunks_max) * bh * kStateFloats * 4);
   p.state_bytes = align_up(bh * kStateFloats * 4);
-  p.workspace_bytes = p.partial_bytes + p.state_bytes;
+  p.ctl_bytes = align_up(static_cast<size_t>(p.units) * sizeof(unsigned long long));
+  p.workspace_bytes = p.partial_bytes + p.state_bytes + p.ctl_bytes;
   return p;
+}
+
+namespace {
+
+struct DeviceCaps {
+  int cus = 0;
+  int occ[2][2] = {{1, 1}, {1, 1}};  // [kernel: reduce, apply][dtype]
+};
+
+const DeviceCaps& device_caps() {
+  constexpr int kMaxDevices = 64;
+  static DeviceCaps caps[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::call_once(once[dev], [dev] {
+    DeviceCaps c;
+    if (hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c.cus <= 0)
+      c.cus = 256;
+    for (int dt = 0; dt < 2; ++dt) {
+      c.occ[0][dt] = occupancy_blocks_per_cu(KernelKind::kReduce, dt);
+      c.occ[1][dt] = occupancy_blocks_per_cu(KernelKind::kApply, dt);
+    }
+    caps[dev] = c;
+  });
+  return caps[dev];
+}
+
+// Chunks per unit such that the grid (units * chunks blocks) fills whole
+// rounds of `cap` co-resident blocks as closely as possible.
+int64_t pick_chunks(int64_t units, int64_t cap, int64_t max_chunks) {
+  int64_t best = 1;
+  double best_fill = -1.0;
+  for (int64_t k = 1; k <= kMaxRounds; ++k) {
+    const int64_t c = clamp64(k * cap / units, 1, max_chunks);
+    const int64_t blocks = units * c;
+    const int64_t rounds = cdiv(blocks, cap);
+    const double fill = static_cast<double>(blocks) / static_cast<double>(rounds * cap);
+    if (fill > best_fill + 0.01) {
+      best_fill = fill;
+      best = c;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+void fit_plan_to_device(Plan& p, int dtype) {
+  const DeviceCaps& c = device_caps();
+  const int dt = dtype == SANA_DTYPE_BF16 ? 1 : 0;
+  const int64_t rcap = static_cast<int64_t>(c.cus) * c.occ[0][dt];
+  const int64_t acap = static_cast<int64_t>(c.cus) * c.occ[1][dt];
+  // The reduction's cost grows with its chunk count (every chunk adds a
+  // partial to write and fold), so it takes the fewest chunks that still
+  // keep about kReduceWavesPerCu waves streaming on every CU, within one
+  // round of co-resident blocks.
+  const int64_t waves = static_cast<int64_t>(c.cus) * kReduceWavesPerCu;
+  const int64_t want = cdiv(waves, p.units * reduce_block_waves(dtype));
+  int64_t rc = clamp64(std::min(want, std::max<int64_t>(1, rcap / p.units)), 1, p.red_chunks_max);
+#ifdef SANA_TUNING
+  if (const char* e = getenv("SANA_RED_CHUNKS")) rc = clamp64(atoll(e), 1, p.red_chunks_max);
+#endif
+  p.red_chunk = chunk_tokens(p.N, rc);
+  p.red_chunks = cdiv(p.N, p.red_chunk);
+  int64_t ac = pick_chunks(p.units, acap, std::max<int64_t>(1, cdiv(p.N, kMinApplyChunk)));
+#ifdef SANA_TUNING
+  if (const char* e = getenv("SANA_APP_CHUNKS")) ac = std::max<int64_t>(1, atoll(e));
+#endif
+  p.app_chunk = chunk_tokens(p.N, ac);
+  p.app_chunks = cdiv(p.N, p.app_chunk);
 }
 
 namespace {
@@ -105,12 +186,26 @@ bool use_fused(const Plan& p, int variant) {
   return p.N <= kFusedMaxN;
 }
 
-sana_status_t run_state(const Plan& p, int dtype, const void* k, const void* v, float* state,
-                        void* ws, hipStream_t stream) {
-  float* partials = static_cast<float*>(ws);
-  hipError_t e = launch_reduce(p, dtype, k, v, partials, stream);
-  if (e != hipSuccess) return SANA_ERR_HIP;
-  return to_status(launch_combine(p, partials, state, stream));
+// A fresh tag per call for the per-pair control words (48 bits; never 0).
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> counter{0};
+  unsigned long long e;
+  do {
+    e = (counter.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
+  } while (e == 0);
+  return e;
+}
+
+struct WorkspaceParts {
+  float* partials;
+  float* state;
+  unsigned long long* ctl;
+};
+
+WorkspaceParts split_workspace(const Plan& p, void* ws) {
+  char* base = static_cast<char*>(ws);
+  return {reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + p.partial_bytes),
+          reinterpret_cast<unsigned long long*>(base + p.partial_bytes + p.state_bytes)};
 }
 
 }  // namespace
@@ -160,11 +255,15 @@ sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void*
   if (sana::overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
 
   (void)hipGetLastError();  // clear an unrelated earlier error
-  if (sana::use_fused(p, variant))
-    return sana::to_status(sana::launch_fused(p, dtype, q, k, v, out, eps, stream));
-  float* state = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_bytes);
-  if ((s = sana::run_state(p, dtype, k, v, state, workspace, stream)) != SANA_OK) return s;
-  return sana::to_status(sana::launch_apply(p, dtype, q, state, out, eps, stream));
+  Plan fp = p;
+  sana::fit_plan_to_device(fp, dtype);
+  if (sana::use_fused(fp, variant))
+    return sana::to_status(sana::launch_fused(fp, dtype, q, k, v, out, eps, stream));
+  const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
+  if (sana::launch_reduce(fp, dtype, k, v, w.partials, w.state, w.ctl, sana::next_epoch(),
+                          stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  return sana::to_status(sana::launch_apply(fp, dtype, q, w.state, out, eps, stream));
 }
 
 sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void* v, void* out,
@@ -179,7 +278,7 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
     return SANA_ERR_UNSUPPORTED;
   const sana::Plan p = sana::make_plan(B, N, H);
   const bool fused = sana::use_fused(p, variant);
-  const int nk = fused ? 1 : 3;
+  const int nk = fused ? 1 : 2;
   if (n_kernels) *n_kernels = nk;
   if (!events || n_events < nk + 1) return SANA_ERR_INVALID_ARG;
   for (int i = 0; i <= nk; ++i)
@@ -195,19 +294,20 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
   if (sana::overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
 
   (void)hipGetLastError();
+  Plan fp = p;
+  sana::fit_plan_to_device(fp, dtype);
   if (hipEventRecord(events[0], stream) != hipSuccess) return SANA_ERR_HIP;
   if (fused) {
-    if (sana::launch_fused(p, dtype, q, k, v, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
+    if (sana::launch_fused(fp, dtype, q, k, v, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
     return sana::to_status(hipEventRecord(events[1], stream));
   }
-  float* partials = static_cast<float*>(workspace);
-  float* state = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_bytes);
-  if (sana::launch_reduce(p, dtype, k, v, partials, stream) != hipSuccess) return SANA_ERR_HIP;
+  const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
+  if (sana::launch_reduce(fp, dtype, k, v, w.partials, w.state, w.ctl, sana::next_epoch(),
+                          stream) != hipSuccess)
+    return SANA_ERR_HIP;
   if (hipEventRecord(events[1], stream) != hipSuccess) return SANA_ERR_HIP;
-  if (sana::launch_combine(p, partials, state, stream) != hipSuccess) return SANA_ERR_HIP;
-  if (hipEventRecord(events[2], stream) != hipSuccess) return SANA_ERR_HIP;
-  if (sana::launch_apply(p, dtype, q, state, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
-  return sana::to_status(hipEventRecord(events[3], stream));
+  if (sana::launch_apply(fp, dtype, q, w.state, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
+  return sana::to_status(hipEventRecord(events[2], stream));
 }
 
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -230,10 +330,14 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, 
   if ((s = sana::check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
   const size_t sb = static_cast<size_t>(B * H) * sana::kStateFloats * 4;
   if (sana::overlaps(state, sb, k, tb) || sana::overlaps(state, sb, v, tb) ||
-      sana::overlaps(state, sb, workspace, p.partial_bytes))
+      sana::overlaps(state, sb, workspace, p.workspace_bytes))
     return SANA_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  return sana::run_state(p, dtype, k, v, state, workspace, stream);
+  Plan fp = p;
+  sana::fit_plan_to_device(fp, dtype);
+  const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
+  return sana::to_status(sana::launch_reduce(fp, dtype, k, v, w.partials, state, w.ctl,
+                                             sana::next_epoch(), stream));
 }
 
 sana_status_t sana_linattn_apply(const void* q, const float* state, void* out, int64_t B,
@@ -249,8 +353,9 @@ sana_status_t sana_linattn_apply(const void* q, const float* state, void* out, i
   const size_t sb = static_cast<size_t>(B * H) * sana::kStateFloats * 4;
   if (sana::overlaps(out, tb, q, tb) || sana::overlaps(out, tb, state, sb))
     return SANA_ERR_INVALID_ARG;
-  const Plan p = sana::make_plan(B, N, H);
+  Plan p = sana::make_plan(B, N, H);
   (void)hipGetLastError();
+  sana::fit_plan_to_device(p, dtype);
   return sana::to_status(sana::launch_apply(p, dtype, q, state, out, eps, stream));
 }
 

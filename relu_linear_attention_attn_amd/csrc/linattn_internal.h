@@ -16,30 +16,39 @@ constexpr int kStateFloats = kHeadDim * kStateCols;   // 1056 floats = 4224 byte
 constexpr int kTile = 16;                             // tokens per wave iteration
 constexpr int kHeadsPerBlock = 2;                     // a head pair shares 128-byte lines (bf16)
 
-// Work split of one call, derived from the shape only (so the workspace query
-// and the launch agree).
+// Work split of one call. The chunk counts depend on the device (CU count and
+// kernel occupancy) so that every round of blocks fills the chip; the
+// workspace is sized for the largest count any device can pick.
 struct Plan {
   int64_t B, N, H;
   int64_t pairs;          // ceil(H / 2) head pairs per batch item
   int64_t units;          // B * pairs: blocks per token chunk
   int64_t red_chunk;      // tokens per reduction chunk (multiple of kTile)
-  int64_t red_chunks;     // chunks actually used (<= red_chunks_max)
+  int64_t red_chunks;     // chunks used (<= red_chunks_max)
   int64_t red_chunks_max; // chunks the workspace is sized for
   int64_t app_chunk;      // tokens per apply chunk (multiple of kTile)
   int64_t app_chunks;
   size_t partial_bytes;   // workspace bytes for chunk partials
   size_t state_bytes;     // workspace bytes for the combined state
+  size_t ctl_bytes;       // workspace bytes for the per-pair control words
   size_t workspace_bytes; // total
 };
 
+// Device-independent part of the plan: sizes and the workspace layout.
 Plan make_plan(int64_t B, int64_t N, int64_t H);
+// Fills the chunk counts for the current device (makes HIP queries once per device).
+void fit_plan_to_device(Plan& p, int dtype);
+
+enum class KernelKind { kReduce, kApply };
+int occupancy_blocks_per_cu(KernelKind kind, int dtype);
+int reduce_block_waves(int dtype);  // waves per block of the reduction kernel
 
 // Launchers. They enqueue on `stream` and return the launch status.
-// dtype: 0 = fp32, 1 = bf16 (sana_dtype_t).
+// dtype: 0 = fp32, 1 = bf16 (sana_dtype_t). The reduction writes chunk
+// partials, and the last block of each head pair folds them into `state`.
 hipError_t launch_reduce(const Plan& p, int dtype, const void* k, const void* v,
-                         float* partials, hipStream_t stream);
-hipError_t launch_combine(const Plan& p, const float* partials, float* state,
-                          hipStream_t stream);
+                         float* partials, float* state, unsigned long long* ctl,
+                         unsigned long long epoch, hipStream_t stream);
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state,
                         void* out, float eps, hipStream_t stream);
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k,

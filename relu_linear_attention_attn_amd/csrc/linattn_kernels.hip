@@ -67,6 +67,18 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
+// Streaming (nontemporal) accesses for data touched exactly once per call: K
+// and V in the reduction, the output in the apply. They keep the single-use
+// lines from displacing others in L2 and the Infinity Cache, and let output
+// lines go to HBM while the apply runs instead of being evicted, dirty, during
+// the next call's reads. (Q is read with ordinary loads: measured faster.)
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_stream(void* p, u32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
+
 // ReLU on 8 packed bf16: a bf16 compares like its int16 bit pattern against
 // +0 (negative values and -0 have the sign bit set), so max(x, 0) as signed
 // 16-bit integers is the float ReLU.
@@ -76,72 +88,115 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
   return __builtin_bit_cast(u32x4, s);
 }
 
+// -------------------------------------------------- line tiles in LDS
+//
+// A wave owns a head pair (h, h+1): per token that is one 128-byte line of
+// the [B][N][H][d] bf16 tensor (two 64-byte head rows). Every global load and
+// store moves whole lines: lane l handles 16-byte piece l%8 of tokens l/8 and
+// 8 + l/8 of a 16-token tile, so one instruction covers 8 full lines (whole
+// lines are what keeps the HBM write path at full rate). The tile is staged
+// in the wave's own LDS slot as 16 rows of 128 bytes; piece j of token t sits
+// in slot j ^ ((t >> 1) & 7) of its row. That swizzle makes the column reads
+// of the MFMA layouts (16 tokens, one piece) and the line reads both free of
+// bank conflicts.
+constexpr int kLineBytes = 128;
+constexpr int kTileBytes = kTile * kLineBytes;  // 2 KB
+
+__device__ __forceinline__ int tile_off(int t, int j) {
+  return (t << 7) + ((j ^ ((t >> 1) & 7)) << 4);
+}
+
+template <bool Coherent>
+__device__ __forceinline__ void put(float* p, float x) {
+  if (Coherent) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *p = x;
+  }
+}
+
 // ------------------------------------------------------------ bf16 reduce
 
-constexpr int kRedRow = 64;                    // bytes of one token's head row
-constexpr int kRedHalfPad = 64;                // tokens 8..15 start one half-bank-row later
-constexpr int kRedTileBytes = kTile * kRedRow + kRedHalfPad;   // 1088
-constexpr int kRedSlotBytes = 2 * kRedTileBytes;               // K tile + V tile
-
-// LDS offset of token t of a staged tile. Lanes 0-31 gather token s while
-// lanes 32-63 gather token 8+s; the extra 64 bytes put the two rows on
-// different banks.
-__device__ __forceinline__ int red_lds_off(int t) { return t * kRedRow + (t >= 8 ? kRedHalfPad : 0); }
-
-// Accumulates phi(K)^T V and phi(K)^T 1 of one head over the tiles
-// sub, sub + S, ... of the token range [n_lo, n_hi). `base` is the element
-// offset of (b, n = 0, h, c = 0) and `row` the element stride between tokens.
+// Accumulates phi(K)^T V (into acc, MFMA layout) and phi(K)^T 1 (into ks:
+// lane l sums channel l%32 over the tokens it gathers) for the head pair over
+// the tiles sub, sub + S, ... of the token range [n_lo, n_hi). `base` is the
+// element offset of (b, n = 0, h, c = 0) for the pair's first head, `row` the
+// element stride between tokens. `two` says whether the pair's second head
+// exists (H odd leaves the last pair with one head: its lanes then read the
+// first head's half-line again, which stays inside the tensor, and the second
+// head's sums are discarded).
 template <int U>
-__device__ __forceinline__ void reduce_bf16_wave(const unsigned short* __restrict__ K,
+__device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V,
                                                  int64_t row, int64_t base, int64_t n_lo,
-                                                 int64_t n_hi, int sub, int S,
-                                                 unsigned char* slot, f32x16& acc, f32x16& accs) {
+                                                 int64_t n_hi, int sub, int S, bool two,
+                                                 unsigned char* slot, f32x16 (&acc)[2],
+                                                 float (&ks)[2]) {
   const int l = lane_id();
-  const int lt = l >> 2;           // token of the tile this lane loads
-  const int lq = l & 3;            // which 16-byte quarter of the 64-byte head row
-  const int wr = red_lds_off(lt) + lq * 16;
+  const int t0 = l >> 3;
+  const int j = l & 7;
+  const int jl = two ? j : (j & 3);
   const int rc = l & 31;           // channel this lane gathers
   const int rt = (l >> 5) * 8;     // first of the 8 tokens this lane gathers
   const int64_t tiles = (n_hi - n_lo + kTile - 1) / kTile;
   const int64_t mine = tiles > sub ? (tiles - sub + S - 1) / S : 0;
 
-  // Loads are never predicated: a lane whose token lies outside the range
-  // (ragged tail, or a tile past the end) reads row n_lo instead, which is
-  // always inside the tensor, and its k is zeroed when the tile is used
-  // (phi(0) = 0 removes the token from both KV and ksum). Keeping the load
-  // unconditional lets the compiler keep U tiles in flight.
-  u32x4 kb[U], vb[U];
-  auto issue = [&](int64_t i, u32x4& kd, u32x4& vd) {
-    const int64_t n = n_lo + (sub + i * S) * kTile + lt;
-    const int64_t off = base + (n < n_hi ? n : n_lo) * row + lq * 8;
-    kd = ld16(K + off);
-    vd = ld16(V + off);
+  // Loads are never predicated: a token outside the range (ragged tail, or a
+  // tile past the end) reads row n_lo instead, which is always inside the
+  // tensor, and its k is zeroed when staged (phi(0) = 0 drops the token from
+  // both KV and ksum). Unconditional loads keep U tiles in flight.
+  u32x4 kb[U][2], vb[U][2];
+  auto issue = [&](int64_t i, u32x4 (&kd)[2], u32x4 (&vd)[2]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile + t0;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int64_t n = n0 + 8 * h2;
+      const int64_t off = base + (n < n_hi ? n : n_lo) * row + 8 * jl;
+      kd[h2] = ld16_stream(K + off);
+      vd[h2] = ld16_stream(V + off);
+    }
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u, kb[u], vb[u]);
 
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, (u32x4)0x3F803F80u);
-  auto stage = [&](int64_t i, u32x4 kin, u32x4 vin) {
-    const int64_t n = n_lo + (sub + i * S) * kTile + lt;
-    const u32x4 kc = n < n_hi ? kin : (u32x4)0;
-    *reinterpret_cast<u32x4*>(slot + wr) = kc;
-    *reinterpret_cast<u32x4*>(slot + kRedTileBytes + wr) = vin;
+  auto stage = [&](int64_t i, const u32x4 (&kin)[2], const u32x4 (&vin)[2]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile + t0;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int o = tile_off(t0 + 8 * h2, j);
+      *reinterpret_cast<u32x4*>(slot + o) = n0 + 8 * h2 < n_hi ? kin[h2] : (u32x4)0;
+      *reinterpret_cast<u32x4*>(slot + kTileBytes + o) = vin[h2];
+    }
   };
   auto consume = [&]() {
     wave_lds_order();
-    s16x8 a, bv;
+    s16x8 a[2], bv[2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int o = red_lds_off(rt + s) + 2 * rc;
-      a[s] = *reinterpret_cast<const short*>(slot + o);
-      bv[s] = *reinterpret_cast<const short*>(slot + kRedTileBytes + o);
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int o = tile_off(rt + s, hh * 4 + (rc >> 3)) + 2 * (rc & 7);
+        a[hh][s] = *reinterpret_cast<const short*>(slot + o);
+        bv[hh][s] = *reinterpret_cast<const short*>(slot + kTileBytes + o);
+      }
     }
     wave_lds_order();
-    a = __builtin_elementwise_max(a, (s16x8)0);   // phi(k), packed
-    const bf16x8 ab = __builtin_bit_cast(bf16x8, a);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-    accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ones, accs, 0, 0, 0);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const s16x8 pk = __builtin_elementwise_max(a[hh], (s16x8)0);   // phi(k), packed
+      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                        __builtin_bit_cast(bf16x8, bv[hh]),
+                                                        acc[hh], 0, 0, 0);
+      // ksum: widen each bf16 exactly (it is the top half of a binary32) and add
+      const u32x4 w = __builtin_bit_cast(u32x4, pk);
+      float sum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sum += __builtin_bit_cast(float, w[e] << 16);
+        sum += __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+      }
+      ks[hh] += sum;
+    }
   };
   // Main loop: whole groups of U tiles and no branches inside, so the load
   // counter stays exact and U tiles stay in flight.
@@ -167,47 +222,105 @@ __device__ __forceinline__ void reduce_bf16_wave(const unsigned short* __restric
 
 // 32x32 accumulator layout: lane l, register r holds row
 // 8*(r/4) + 4*(l/32) + r%4 and column l%32. Rows are k channels c, columns
-// v channels j; accs holds ksum[c] in every column.
-__device__ __forceinline__ void store_state_from_mfma32(float* dst, const f32x16& acc,
-                                                        const f32x16& accs) {
+// v channels j. ksum[c] is ks of lane c plus ks of lane c + 32 (the two
+// token halves of the gather), added here in that order.
+template <bool Coherent>
+__device__ __forceinline__ void store_state_from_mfma32(float* dst, const f32x16& acc, float ks) {
   const int l = lane_id();
   const int j = l & 31;
   const int cb = 4 * (l >> 5);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int c = 8 * (r >> 2) + cb + (r & 3);
-    dst[c * kSC + j] = acc[r];
-    if (j == 0) dst[c * kSC + kD] = accs[r];
+    put<Coherent>(dst + c * kSC + j, acc[r]);
   }
+  const float hi = __shfl_down(ks, 32);
+  if (l < 32) put<Coherent>(dst + l * kSC + kD, ks + hi);
 }
 
-// Sums the S sub-stream accumulators of each head of the block in fixed order
-// (sub 0, then 1, 2, ...) into sub-stream 0. All threads of the block must call.
-template <int S, int R>
-__device__ __forceinline__ void combine_substreams(float (&regs)[R], float* xchg, int hh, int sub) {
+// Sums the accumulators of the S sub-stream waves of a block into wave 0 in
+// fixed order (0, then 1, 2, ...), one wave at a time through `xchg`
+// (R floats per lane). All threads of the block must call.
+template <int R>
+__device__ __forceinline__ void fold_substreams(float (&regs)[R], float* xchg, int sub, int S) {
   const int l = lane_id();
-  if (S > 1) {
-    if (sub > 0) {
-      float* dst = xchg + ((sub - 1) * 2 + hh) * R * kWave;
+  for (int s = 1; s < S; ++s) {
+    if (sub == s) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) dst[r * kWave + l] = regs[r];
+      for (int r = 0; r < R; ++r) xchg[r * kWave + l] = regs[r];
     }
     __syncthreads();
     if (sub == 0) {
-      for (int s = 1; s < S; ++s) {
-        const float* src = xchg + ((s - 1) * 2 + hh) * R * kWave;
 #pragma unroll
-        for (int r = 0; r < R; ++r) regs[r] += src[r * kWave + l];
-      }
+      for (int r = 0; r < R; ++r) regs[r] += xchg[r * kWave + l];
     }
+    __syncthreads();
   }
 }
 
-template <int S>
-struct RedShared {
-  unsigned char slot[2 * S][kRedSlotBytes];
-  float xchg[(S > 1 ? S - 1 : 1) * 2 * 32 * kWave];
-};
+// Chunk partials of a head pair are folded into the final state by the last
+// block to finish that pair, in ascending chunk order, so the result does not
+// depend on which block finishes last. The hand-off between blocks (which may
+// sit on different XCDs, each with its own L2) avoids device-wide fences,
+// whose L2 write-back per block would cost more than the whole reduction:
+//   * partials are written with device-coherent stores (relaxed atomic
+//     stores at agent scope, which write through the L2),
+//   * each wave waits until its stores have completed, then the block bumps
+//     the pair's control word with a device-scope atomic,
+//   * the block that brings the count to the number of chunks reads the
+//     partials back with device-coherent loads.
+// The control word holds (call epoch << 16 | finished blocks). A word left by
+// an earlier call, or garbage, carries another epoch and restarts the count,
+// so the workspace needs no clearing between calls.
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool arrive_last(unsigned long long* ctl, unsigned long long epoch,
+                                            int64_t nchunks) {
+  __shared__ int last;
+  // wait until this wave's coherent partial stores have completed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long cur = __hip_atomic_load(ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long nxt;
+    while (true) {
+      nxt = (cur >> 16) == epoch ? cur + 1 : ((epoch << 16) | 1ull);
+      if (__hip_atomic_compare_exchange_strong(ctl, &cur, nxt, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    last = static_cast<int64_t>(nxt & 0xFFFFull) == nchunks;
+  }
+  __syncthreads();
+  return last != 0;
+}
+
+// state[h][e] = sum_{p < P} partials[p][h][e] for the (up to two) heads of a
+// pair. All loads of a batch are issued before any is added, so the fold
+// costs about one memory round trip per 16 chunks; the sum itself runs in
+// ascending p.
+__device__ __forceinline__ void fold_partials(const float* __restrict__ partials,
+                                             float* __restrict__ state, int64_t bh0, int nheads,
+                                             int64_t BH, int64_t P) {
+  constexpr int kBatch = 16;
+  const int64_t stride = BH * kSF;
+  for (int e = threadIdx.x; e < nheads * kSF; e += blockDim.x) {
+    const float* src = partials + bh0 * kSF + e;
+    float acc = 0.0f;
+    for (int64_t p0 = 0; p0 < P; p0 += kBatch) {
+      float x[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        x[u] = p0 + u < P ? load_coherent(src + (p0 + u) * stride) : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (p0 + u < P) acc = (p0 + u == 0) ? x[u] : acc + x[u];
+    }
+    state[bh0 * kSF + e] = acc;
+  }
+}
 
 // ------------------------------------------------------------- bf16 apply
 
@@ -217,7 +330,7 @@ struct ApplyOperands {
 
 // Builds the A operands of the three 16x16x32 MFMA tiles from a [d][d+1]
 // fp32 state. A lane supplies row i = l%16 and contraction indices
-// k = 8*(l/16) + s, s = 0..7 (the same k the lane loads from q). Tile t row i
+// k = 8*(l/16) + s, s = 0..7 (the same k the lane reads from q). Tile t row i
 // stands for output channel 8*(i/4) + 4t + i%4, so after the MFMA a lane
 // holds output channels 8*(l/16) .. +7 of token l%16.
 __device__ __forceinline__ ApplyOperands make_apply_operands(const float* st) {
@@ -242,75 +355,148 @@ __device__ __forceinline__ ApplyOperands make_apply_operands(const float* st) {
   return o;
 }
 
+// One head's 16-token output: phi(q) from the operand-layout piece, six
+// MFMAs, one reciprocal per token, bf16 rounding. Returns the lane's 8
+// output channels (one 16-byte piece) of token l%16.
+__device__ __forceinline__ u32x4 apply_head(const ApplyOperands& op, u32x4 qpiece, float eps) {
+  const bf16x8 qv = __builtin_bit_cast(bf16x8, relu_bf16x8(qpiece));
+  f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qv, (f32x4)0, 0, 0, 0);
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, qv, a0, 0, 0, 0);
+  f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, qv, (f32x4)0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, qv, a1, 0, 0, 0);
+  f32x4 ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, qv, (f32x4)0, 0, 0, 0);
+  ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_lo, qv, ad, 0, 0, 0);
+  const float rinv = 1.0f / (ad[0] + eps);
+  bf16x8 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o[r] = (__bf16)(a0[r] * rinv);
+    o[4 + r] = (__bf16)(a1[r] * rinv);
+  }
+  return __builtin_bit_cast(u32x4, o);
+}
+
+// Applies the pair's two heads to the tiles sub, sub + S, ... of [n_lo, n_hi).
+// `two` as for reduce_pair_wave: with one head, the second half-line is read
+// from the first head (inside the tensor), computed and never stored.
 template <int U>
-__device__ __forceinline__ void apply_bf16_wave(const unsigned short* __restrict__ Q,
+__device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict__ Q,
                                                 unsigned short* __restrict__ Out,
-                                                const ApplyOperands& op, float eps, int64_t row,
-                                                int64_t base, int64_t n_lo, int64_t n_hi, int sub,
-                                                int S) {
+                                                const ApplyOperands (&op)[2], float eps,
+                                                int64_t row, int64_t base, int64_t n_lo,
+                                                int64_t n_hi, int sub, int S, bool two,
+                                                unsigned char* slot) {
   const int l = lane_id();
+  const int t0 = l >> 3;
+  const int j = l & 7;
+  const int jl = two ? j : (j & 3);
   const int g = l >> 4;
   const int col = l & 15;
   const int64_t tiles = (n_hi - n_lo + kTile - 1) / kTile;
   const int64_t mine = tiles > sub ? (tiles - sub + S - 1) / S : 0;
 
-  // Unpredicated loads (see reduce_bf16_wave): an out-of-range token reads
+  // Unpredicated loads (see reduce_pair_wave): an out-of-range token reads
   // row n_lo and its result is simply not stored.
-  u32x4 qb[U];
-  auto issue = [&](int64_t i, u32x4& qd) {
-    const int64_t n = n_lo + (sub + i * S) * kTile + col;
-    qd = ld16(Q + base + (n < n_hi ? n : n_lo) * row + 8 * g);
+  u32x4 qb[U][2];
+  auto issue = [&](int64_t i, u32x4 (&qd)[2]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile + t0;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int64_t n = n0 + 8 * h2;
+      qd[h2] = ld16(Q + base + (n < n_hi ? n : n_lo) * row + 8 * jl);
+    }
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u, qb[u]);
 
-  auto compute = [&](u32x4 qrelu) -> u32x4 {
-    const bf16x8 qv = __builtin_bit_cast(bf16x8, qrelu);
-    f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qv, (f32x4)0, 0, 0, 0);
-    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, qv, a0, 0, 0, 0);
-    f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, qv, (f32x4)0, 0, 0, 0);
-    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, qv, a1, 0, 0, 0);
-    f32x4 ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, qv, (f32x4)0, 0, 0, 0);
-    ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_lo, qv, ad, 0, 0, 0);
-    const float rinv = 1.0f / (ad[0] + eps);
-    bf16x8 o;
+  // stage the tile's lines, compute both heads in place in the tile, and read
+  // the output lines back; `full` says the whole tile is inside the range
+  auto compute = [&](const u32x4 (&qin)[2]) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      o[r] = (__bf16)(a0[r] * rinv);
-      o[4 + r] = (__bf16)(a1[r] * rinv);
-    }
-    return __builtin_bit_cast(u32x4, o);
+    for (int h2 = 0; h2 < 2; ++h2)
+      *reinterpret_cast<u32x4*>(slot + tile_off(t0 + 8 * h2, j)) = qin[h2];
+    wave_lds_order();
+    u32x4 qp[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      qp[hh] = *reinterpret_cast<const u32x4*>(slot + tile_off(col, hh * 4 + g));
+    wave_lds_order();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<u32x4*>(slot + tile_off(col, hh * 4 + g)) = apply_head(op[hh], qp[hh], eps);
+    wave_lds_order();
   };
-  auto out_ptr = [&](int64_t i) {
-    return Out + base + (n_lo + (sub + i * S) * kTile + col) * row + 8 * g;
+  auto out_line = [&](int h2) {
+    return *reinterpret_cast<const u32x4*>(slot + tile_off(t0 + 8 * h2, j));
+  };
+  auto out_ptr = [&](int64_t i, int h2) {
+    return Out + base + (n_lo + (sub + i * S) * kTile + t0 + 8 * h2) * row + 8 * j;
   };
   // Main loop over this wave's tiles that lie wholly inside the range: no
-  // branches, unconditional stores, U loads in flight.
-  const int64_t whole = (n_hi - n_lo) / kTile;
+  // branches, unconditional stores, U tiles in flight.
+  const int64_t whole = two ? (n_hi - n_lo) / kTile : 0;
   const int64_t mine_whole = whole > sub ? (whole - sub + S - 1) / S : 0;
   int64_t i0 = 0;
-  for (; i0 + U <= mine_whole; i0 += U) {
+  {
+    for (; i0 + U <= mine_whole; i0 += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const u32x4 qc = relu_bf16x8(qb[u]);
-      // refill qb[u] only after its last use, so it keeps its registers
-      __builtin_amdgcn_sched_barrier(0);
-      issue(i0 + u + U, qb[u]);
-      st16(out_ptr(i0 + u), compute(qc));
+      for (int u = 0; u < U; ++u) {
+        compute(qb[u]);
+        // refill qb[u] only after its last use, so it keeps its registers
+        __builtin_amdgcn_sched_barrier(0);
+        issue(i0 + u + U, qb[u]);
+        const u32x4 o0 = out_line(0), o1 = out_line(1);
+        wave_lds_order();
+        st16_stream(out_ptr(i0 + u, 0), o0);
+        st16_stream(out_ptr(i0 + u, 1), o1);
+      }
     }
   }
-  // Remainder: fewer than U whole tiles, and possibly the ragged last tile.
+  // Remainder: the last few tiles, the ragged last tile, and a one-head pair.
+  for (; i0 < mine; i0 += U) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (i0 + u < mine) {
-      const u32x4 o = compute(relu_bf16x8(qb[u]));
-      const int64_t n = n_lo + (sub + (i0 + u) * S) * kTile + col;
-      if (n < n_hi) st16(out_ptr(i0 + u), o);
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < mine) {
+        compute(qb[u]);
+        issue(i0 + u + U, qb[u]);
+        const u32x4 o0 = out_line(0), o1 = out_line(1);
+        wave_lds_order();
+        const int64_t n = n_lo + (sub + (i0 + u) * S) * kTile + t0;
+        if (two || j < 4) {
+          if (n < n_hi) st16_stream(out_ptr(i0 + u, 0), o0);
+          if (n + 8 < n_hi) st16_stream(out_ptr(i0 + u, 1), o1);
+        }
+      }
     }
   }
 }
 
 // ----------------------------------------------------------- fp32 reduce
+//
+// fp32 blocks hold 2 heads x S sub-streams (wave w: head w%2, sub-stream w/2).
+
+// Sums the S sub-stream accumulators of each head of the block in fixed order
+// (sub 0, then 1, 2, ...) into sub-stream 0. All threads of the block must call.
+template <int S, int R>
+__device__ __forceinline__ void combine_substreams(float (&regs)[R], float* xchg, int hh, int sub) {
+  const int l = lane_id();
+  if (S > 1) {
+    if (sub > 0) {
+      float* dst = xchg + ((sub - 1) * 2 + hh) * R * kWave;
+#pragma unroll
+      for (int r = 0; r < R; ++r) dst[r * kWave + l] = regs[r];
+    }
+    __syncthreads();
+    if (sub == 0) {
+      for (int s = 1; s < S; ++s) {
+        const float* src = xchg + ((s - 1) * 2 + hh) * R * kWave;
+#pragma unroll
+        for (int r = 0; r < R; ++r) regs[r] += src[r * kWave + l];
+      }
+    }
+  }
+}
+
 
 // Lane l owns state rows c = l/2, columns 16*(l%2) .. +15, and ksum[c].
 template <int U>
@@ -367,13 +553,14 @@ __device__ __forceinline__ void reduce_f32_wave(const float* __restrict__ K,
   }
 }
 
+template <bool Coherent>
 __device__ __forceinline__ void store_state_from_f32(float* dst, const float (&acc)[17]) {
   const int l = lane_id();
   const int c = l >> 1;
   const int jh = (l & 1) * 16;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) dst[c * kSC + jh + m] = acc[m];
-  if (jh == 0) dst[c * kSC + kD] = acc[16];
+  for (int m = 0; m < 16; ++m) put<Coherent>(dst + c * kSC + jh + m, acc[m]);
+  if (jh == 0) put<Coherent>(dst + c * kSC + kD, acc[16]);
 }
 
 // ------------------------------------------------------------ fp32 apply
@@ -459,39 +646,84 @@ __device__ __forceinline__ BlockCoords block_coords(int64_t pairs, int64_t units
   return c;
 }
 
-template <int S, int U>
-__global__ __launch_bounds__(128 * S) void reduce_bf16_kernel(
-    const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
-    float* __restrict__ partials, int64_t N, int64_t H, int64_t pairs, int64_t units,
-    int64_t chunk, int64_t BH) {
-  __shared__ RedShared<S> sh;
-  const BlockCoords bc = block_coords(pairs, units, H);
-  const int64_t n_lo = bc.p * chunk;
-  const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
-  f32x16 acc = (f32x16)0, accs = (f32x16)0;
-  if (bc.active)
-    reduce_bf16_wave<U>(K, V, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S,
-                        sh.slot[threadIdx.x >> 6], acc, accs);
+// bf16 blocks: S waves, all on one head pair; wave w is token sub-stream w.
+struct PairCoords {
+  int64_t b, h, p;
+  int sub;
+  bool two;  // the pair's second head exists
+};
+
+__device__ __forceinline__ PairCoords pair_coords(int64_t pairs, int64_t units, int64_t H) {
+  PairCoords c;
+  const int64_t bid = blockIdx.x;
+  const int64_t unit = bid % units;
+  c.p = bid / units;
+  c.b = unit / pairs;
+  c.h = 2 * (unit % pairs);
+  c.sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.two = c.h + 1 < H;
+  return c;
+}
+
+// LDS of a bf16 reduction block: one K + V tile slot per wave, reused at the
+// end to pass accumulators between waves (32 floats per lane at a time).
+template <int S>
+union RedLds {
+  unsigned char slot[S][2 * kTileBytes];
+  float xchg[32 * kWave];
+};
+
+// Sums the block's sub-stream accumulators into wave 0, in sub-stream order.
+template <int S>
+__device__ __forceinline__ void fold_pair_accumulators(f32x16 (&acc)[2], float (&ks)[2],
+                                                       RedLds<S>& lds, int sub) {
+  if (S == 1) return;
+  __syncthreads();  // every wave is done with its tile slot
   float regs[32];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    regs[r] = acc[r];
-    regs[16 + r] = accs[r];
+    regs[r] = acc[0][r];
+    regs[16 + r] = acc[1][r];
   }
-  combine_substreams<S, 32>(regs, sh.xchg, bc.hh, bc.sub);
+  fold_substreams<32>(regs, lds.xchg, sub, S);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    acc[r] = regs[r];
-    accs[r] = regs[16 + r];
+    acc[0][r] = regs[r];
+    acc[1][r] = regs[16 + r];
   }
-  if (bc.active && bc.sub == 0)
-    store_state_from_mfma32(partials + (bc.p * BH + bc.b * H + bc.h) * kSF, acc, accs);
+  fold_substreams<2>(ks, lds.xchg, sub, S);
+}
+
+template <int S, int U>
+__global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
+    const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
+    float* __restrict__ partials, float* __restrict__ state, unsigned long long* __restrict__ ctl,
+    unsigned long long epoch, int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk,
+    int64_t nchunks, int64_t BH) {
+  __shared__ RedLds<S> lds;
+  const PairCoords pc = pair_coords(pairs, units, H);
+  const int64_t n_lo = pc.p * chunk;
+  const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
+  const int64_t base = (pc.b * N * H + pc.h) * kD;
+  f32x16 acc[2] = {(f32x16)0, (f32x16)0};
+  float ks[2] = {0.0f, 0.0f};
+  reduce_pair_wave<U>(K, V, H * kD, base, n_lo, n_hi, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
+  fold_pair_accumulators<S>(acc, ks, lds, pc.sub);
+  const int64_t bh = pc.b * H + pc.h;
+  if (pc.sub == 0) {
+    store_state_from_mfma32<true>(partials + (pc.p * BH + bh) * kSF, acc[0], ks[0]);
+    if (pc.two) store_state_from_mfma32<true>(partials + (pc.p * BH + bh + 1) * kSF, acc[1], ks[1]);
+  }
+  if (arrive_last(ctl + blockIdx.x % units, epoch, nchunks))
+    fold_partials(partials, state, bh, pc.two ? 2 : 1, BH, nchunks);
 }
 
 template <int S, int U>
 __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
     const float* __restrict__ K, const float* __restrict__ V, float* __restrict__ partials,
-    int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk, int64_t BH) {
+    float* __restrict__ state, unsigned long long* __restrict__ ctl, unsigned long long epoch,
+    int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk, int64_t nchunks,
+    int64_t BH) {
   __shared__ float slot[2 * S][2 * kTile * kD];
   __shared__ float xchg[(S > 1 ? S - 1 : 1) * 2 * 17 * kWave];
   const BlockCoords bc = block_coords(pairs, units, H);
@@ -505,31 +737,29 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
                        slot[threadIdx.x >> 6], acc);
   combine_substreams<S, 17>(acc, xchg, bc.hh, bc.sub);
   if (bc.active && bc.sub == 0)
-    store_state_from_f32(partials + (bc.p * BH + bc.b * H + bc.h) * kSF, acc);
-}
-
-// state[e] = sum_{p < P} partials[p][e], p ascending.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partials,
-                                                      float* __restrict__ state, int64_t total,
-                                                      int64_t P) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  float s = partials[e];
-  for (int64_t p = 1; p < P; ++p) s += partials[p * total + e];
-  state[e] = s;
+    store_state_from_f32<true>(partials + (bc.p * BH + bc.b * H + bc.h) * kSF, acc);
+  const int64_t unit = blockIdx.x % units;
+  if (arrive_last(ctl + unit, epoch, nchunks)) {
+    const int64_t h0 = 2 * (unit % pairs);
+    fold_partials(partials, state, bc.b * H + h0, H - h0 < 2 ? 1 : 2, BH, nchunks);
+  }
 }
 
 template <int S, int U>
-__global__ __launch_bounds__(128 * S) void apply_bf16_kernel(
+__global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     const unsigned short* __restrict__ Q, const float* __restrict__ state,
     unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
     int64_t units, int64_t chunk) {
-  const BlockCoords bc = block_coords(pairs, units, H);
-  if (!bc.active) return;
-  const int64_t n_lo = bc.p * chunk;
+  __shared__ unsigned char slots[S][kTileBytes];
+  const PairCoords pc = pair_coords(pairs, units, H);
+  const int64_t n_lo = pc.p * chunk;
   const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
-  const ApplyOperands op = make_apply_operands(state + (bc.b * H + bc.h) * kSF);
-  apply_bf16_wave<U>(Q, Out, op, eps, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S);
+  const int64_t base = (pc.b * N * H + pc.h) * kD;
+  const float* st = state + (pc.b * H + pc.h) * kSF;
+  ApplyOperands op[2];
+  op[0] = make_apply_operands(st);
+  op[1] = pc.two ? make_apply_operands(st + kSF) : op[0];
+  apply_pair_wave<U>(Q, Out, op, eps, H * kD, base, n_lo, n_hi, pc.sub, S, pc.two, slots[pc.sub]);
 }
 
 template <int S>
@@ -547,38 +777,30 @@ __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
 }
 
 // One block per (b, head pair) over all N tokens: reduce into registers,
-// combine sub-streams through LDS, keep the state in LDS, apply.
+// fold the sub-streams through LDS, keep the state in LDS, apply.
 template <int S, int U>
-__global__ __launch_bounds__(128 * S) void fused_bf16_kernel(
+__global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
     const unsigned short* __restrict__ V, unsigned short* __restrict__ Out, float eps,
     int64_t N, int64_t H, int64_t pairs) {
-  __shared__ RedShared<S> sh;
+  __shared__ RedLds<S> lds;
   __shared__ float st[2][kSF];
-  const BlockCoords bc = block_coords(pairs, (int64_t)gridDim.x, H);
-  const int64_t base = (bc.b * N * H + bc.h) * kD;
-  f32x16 acc = (f32x16)0, accs = (f32x16)0;
-  if (bc.active)
-    reduce_bf16_wave<U>(K, V, H * kD, base, 0, N, bc.sub, S, sh.slot[threadIdx.x >> 6], acc, accs);
-  float regs[32];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    regs[r] = acc[r];
-    regs[16 + r] = accs[r];
-  }
-  combine_substreams<S, 32>(regs, sh.xchg, bc.hh, bc.sub);
-  if (bc.active && bc.sub == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc[r] = regs[r];
-      accs[r] = regs[16 + r];
-    }
-    store_state_from_mfma32(st[bc.hh], acc, accs);
+  const PairCoords pc = pair_coords(pairs, (int64_t)gridDim.x, H);
+  const int64_t base = (pc.b * N * H + pc.h) * kD;
+  f32x16 acc[2] = {(f32x16)0, (f32x16)0};
+  float ks[2] = {0.0f, 0.0f};
+  reduce_pair_wave<U>(K, V, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
+  fold_pair_accumulators<S>(acc, ks, lds, pc.sub);
+  if (pc.sub == 0) {
+    store_state_from_mfma32<false>(st[0], acc[0], ks[0]);
+    store_state_from_mfma32<false>(st[1], acc[1], ks[1]);
   }
   __syncthreads();
-  if (!bc.active) return;
-  const ApplyOperands op = make_apply_operands(st[bc.hh]);
-  apply_bf16_wave<U>(Q, Out, op, eps, H * kD, base, 0, N, bc.sub, S);
+  ApplyOperands op[2];
+  op[0] = make_apply_operands(st[0]);
+  op[1] = make_apply_operands(st[1]);
+  __syncthreads();  // tile slots are reused by the apply
+  apply_pair_wave<U>(Q, Out, op, eps, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub]);
 }
 
 template <int S, int U>
@@ -597,7 +819,7 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
   if (bc.active)
     reduce_f32_wave<U>(K, V, H * kD, base, 0, N, bc.sub, S, slot[threadIdx.x >> 6], acc);
   combine_substreams<S, 17>(acc, xchg, bc.hh, bc.sub);
-  if (bc.active && bc.sub == 0) store_state_from_f32(st[bc.hh], acc);
+  if (bc.active && bc.sub == 0) store_state_from_f32<false>(st[bc.hh], acc);
   __syncthreads();
   if (bc.active && bc.sub == 0) stage_state_padded(stp[bc.hh], st[bc.hh]);
   __syncthreads();
@@ -605,42 +827,71 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
   apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, base, 0, N, bc.sub, S);
 }
 
-constexpr int kRedS = 2, kRedU = 4;
-constexpr int kAppS = 2, kAppU = 4;
-constexpr int kFusS = 4, kFusU = 2;
+#ifndef SANA_RED_S
+#define SANA_RED_S 8
+#endif
+#ifndef SANA_RED_U
+#define SANA_RED_U 2
+#endif
+#ifndef SANA_APP_S
+#define SANA_APP_S 8
+#endif
+#ifndef SANA_APP_U
+#define SANA_APP_U 2
+#endif
+// token sub-streams per head (S) and tiles in flight per wave (U)
+constexpr int kRedS = SANA_RED_S, kRedU = SANA_RED_U;
+constexpr int kAppS = SANA_APP_S, kAppU = SANA_APP_U;
+constexpr int kFusS = 8, kFusU = 2;
 constexpr int kF32S = 2, kF32U = 2;
 
 }  // namespace
 
 hipError_t launch_reduce(const Plan& p, int dtype, const void* k, const void* v, float* partials,
+                         float* state, unsigned long long* ctl, unsigned long long epoch,
                          hipStream_t stream) {
   const dim3 grid((unsigned)(p.units * p.red_chunks));
   const int64_t BH = p.B * p.H;
   if (dtype == 1) {
-    hipLaunchKernelGGL((reduce_bf16_kernel<kRedS, kRedU>), grid, dim3(128 * kRedS), 0, stream,
+    hipLaunchKernelGGL((reduce_bf16_kernel<kRedS, kRedU>), grid, dim3(64 * kRedS), 0, stream,
                        static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
-                       partials, p.N, p.H, p.pairs, p.units, p.red_chunk, BH);
+                       partials, state, ctl, epoch, p.N, p.H, p.pairs, p.units, p.red_chunk,
+                       p.red_chunks, BH);
   } else {
     hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U>), grid, dim3(128 * kF32S), 0, stream,
-                       static_cast<const float*>(k), static_cast<const float*>(v), partials, p.N,
-                       p.H, p.pairs, p.units, p.red_chunk, BH);
+                       static_cast<const float*>(k), static_cast<const float*>(v), partials, state,
+                       ctl, epoch, p.N, p.H, p.pairs, p.units, p.red_chunk, p.red_chunks, BH);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Plan& p, const float* partials, float* state, hipStream_t stream) {
-  const int64_t total = p.B * p.H * kStateFloats;
-  const dim3 grid((unsigned)((total + 255) / 256));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, partials, state, total,
-                     p.red_chunks);
-  return hipGetLastError();
+int reduce_block_waves(int dtype) { return dtype == 1 ? kRedS : 2 * kF32S; }
+
+int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (kind) {
+    case KernelKind::kReduce:
+      e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &n, reduce_bf16_kernel<kRedS, kRedU>, 64 * kRedS, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &n, reduce_f32_kernel<kF32S, kF32U>, 128 * kF32S, 0);
+      break;
+    case KernelKind::kApply:
+      e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &n, apply_bf16_kernel<kAppS, kAppU>, 64 * kAppS, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &n, apply_f32_kernel<kF32S>, 128 * kF32S, 0);
+      break;
+  }
+  return e == hipSuccess && n > 0 ? n : 1;
 }
 
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state, void* out,
                         float eps, hipStream_t stream) {
   const dim3 grid((unsigned)(p.units * p.app_chunks));
   if (dtype == 1) {
-    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), grid, dim3(128 * kAppS), 0, stream,
+    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), grid, dim3(64 * kAppS), 0, stream,
                        static_cast<const unsigned short*>(q), state,
                        static_cast<unsigned short*>(out), eps, p.N, p.H, p.pairs, p.units,
                        p.app_chunk);
@@ -656,7 +907,7 @@ hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k, 
                         void* out, float eps, hipStream_t stream) {
   const dim3 grid((unsigned)p.units);
   if (dtype == 1) {
-    hipLaunchKernelGGL((fused_bf16_kernel<kFusS, kFusU>), grid, dim3(128 * kFusS), 0, stream,
+    hipLaunchKernelGGL((fused_bf16_kernel<kFusS, kFusU>), grid, dim3(64 * kFusS), 0, stream,
                        static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                        static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out),
                        eps, p.N, p.H, p.pairs);
