@@ -1,0 +1,170 @@
+"""The C ABI on the host: the library loads without a GPU, exports every
+function include/sana_linattn.h declares, and rejects every invalid call with
+the documented status before touching HIP.
+
+Every call below carries at least one argument that the host checks reject,
+so no kernel is ever launched (the pointers are placeholders, never
+dereferenced)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sana_linattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGNMENT, HIPERR = range(6)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    from relu_linear_attention_attn_amd import binding
+
+    if not os.path.exists(binding.LIB_PATH):
+        subprocess.run([sys.executable, os.path.join(ROOT, "relu_linear_attention_attn_amd",
+                                                      "csrc", "build.py")], check=True)
+    return binding.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sana_linattn_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+    from relu_linear_attention_attn_amd import binding
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_version_and_strerror(L):
+    assert L.sana_linattn_version() == 1
+    seen = set()
+    for code in range(6):
+        msg = L.sana_linattn_strerror(code).decode()
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert L.sana_linattn_strerror(99).decode() == "unknown status"
+
+
+def ws_size(L, B, N, H, d=32, dt=BF16):
+    n = ctypes.c_size_t(123)
+    st = L.sana_linattn_workspace_size(B, N, H, d, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_rules(L):
+    assert ws_size(L, 2, 16384, 70) [0] == OK
+    assert ws_size(L, 0, 16, 2) == (INVALID, 0)
+    assert ws_size(L, 1, 0, 2) == (INVALID, 0)
+    assert ws_size(L, 1, 16, -1) == (INVALID, 0)
+    assert ws_size(L, 1, 16, 2, d=64) == (UNSUPPORTED, 0)
+    assert ws_size(L, 1, 16, 2, dt=7) == (UNSUPPORTED, 0)
+    assert L.sana_linattn_workspace_size(1, 16, 2, 32, BF16, None) == INVALID
+    # B*N*H*d*2 beyond 2^62 bytes, and int64 overflow of the product
+    assert ws_size(L, 1 << 20, 1 << 20, 1 << 16)[0] == INVALID   # exactly 2^62 bytes
+    assert ws_size(L, 1 << 20, 1 << 20, 1 << 15)[0] == OK        # 2^61 bytes is addressable
+    assert ws_size(L, 1 << 62, 1 << 62, 1)[0] == INVALID
+    # the state does not grow with n: constant once N is large
+    sizes = {ws_size(L, 2, n, 70)[1] for n in (1 << 16, 1 << 18, 1 << 20, 1 << 24)}
+    assert len(sizes) == 1
+    # and every size is a multiple of 256 bytes and covers B*H states
+    st, n = ws_size(L, 3, 5000, 7)
+    assert st == OK and n % 256 == 0 and n >= 3 * 7 * 32 * 33 * 4
+    # dtype does not change the state size
+    assert ws_size(L, 2, 4096, 36, dt=F32) == ws_size(L, 2, 4096, 36, dt=BF16)
+
+
+def test_state_size(L):
+    n = ctypes.c_size_t(0)
+    assert L.sana_linattn_state_size(2, 70, 32, ctypes.byref(n)) == OK
+    assert n.value == 2 * 70 * 32 * 33 * 4
+    assert L.sana_linattn_state_size(0, 70, 32, ctypes.byref(n)) == INVALID
+    assert L.sana_linattn_state_size(1, 70, 16, ctypes.byref(n)) == UNSUPPORTED
+
+
+A = 1 << 20       # placeholder device addresses, 256-byte aligned and far apart
+P_Q, P_K, P_V, P_O, P_W = (A * i for i in range(1, 6))
+
+
+def fwd(L, q=P_Q, k=P_K, v=P_V, o=P_O, B=1, N=64, H=2, d=32, eps=1e-6, dt=BF16, var=0,
+        ws=P_W, wsb=1 << 30):
+    return L.sana_linattn_fwd_variant(q, k, v, o, B, N, H, d, eps, dt, var, ws, wsb, None)
+
+
+def test_fwd_rejects_invalid_arguments(L):
+    assert fwd(L, B=0) == INVALID
+    assert fwd(L, N=-5) == INVALID
+    assert fwd(L, H=0) == INVALID
+    assert fwd(L, d=16) == UNSUPPORTED
+    assert fwd(L, dt=2) == UNSUPPORTED
+    assert fwd(L, var=9) == UNSUPPORTED
+    for name in ("q", "k", "v", "o"):
+        assert fwd(L, **{name: None}) == INVALID, name
+    for eps in (-1e-6, math.nan, math.inf):
+        assert fwd(L, eps=eps) == INVALID, eps
+    for name in ("q", "k", "v", "o"):
+        assert fwd(L, **{name: A * 7 + 8}) == ALIGNMENT, name
+    # out overlapping an input (bf16: 1*64*2*32*2 = 8 KB tensors)
+    assert fwd(L, o=P_Q + 4096) == INVALID
+    assert fwd(L, o=P_V - 4096) == INVALID
+    # workspace missing, too small, misaligned, overlapping out
+    need = ws_size(L, 1, 64, 2)[1]
+    assert fwd(L, ws=None) == WORKSPACE
+    assert fwd(L, wsb=need - 1) == WORKSPACE
+    assert fwd(L, ws=P_W + 16, wsb=need) == ALIGNMENT
+    assert fwd(L, ws=P_O, wsb=need) == INVALID
+    # size overflow
+    assert fwd(L, B=1 << 40, N=1 << 40) == INVALID
+    # the plain entry point checks the same
+    assert L.sana_linattn_fwd(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, -1.0, BF16, P_W, 1 << 30,
+                              None) == INVALID
+
+
+def test_profiled_needs_enough_events(L):
+    nk = ctypes.c_int(-1)
+    events = (ctypes.c_void_p * 1)(None)
+    st = L.sana_linattn_fwd_profiled(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 1e-6, BF16, 1, P_W,
+                                     1 << 30, events, 1, ctypes.byref(nk), None)
+    assert st == INVALID and nk.value == 2          # split: reduction + apply
+    st = L.sana_linattn_fwd_profiled(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 1e-6, BF16, 2, P_W,
+                                     1 << 30, events, 1, ctypes.byref(nk), None)
+    assert st == INVALID and nk.value == 1          # fused: one kernel needs two events
+    st = L.sana_linattn_fwd_profiled(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 1e-6, BF16, 1, P_W,
+                                     1 << 30, None, 3, ctypes.byref(nk), None)
+    assert st == INVALID
+
+
+def test_kv_state_and_apply_reject_invalid_arguments(L):
+    kv = L.sana_linattn_kv_state
+    assert kv(P_K, P_V, None, 1, 64, 2, 32, BF16, P_W, 1 << 30, None) == INVALID
+    assert kv(P_K, P_V, P_O, 1, 64, 2, 64, BF16, P_W, 1 << 30, None) == UNSUPPORTED
+    assert kv(P_K, P_V, P_O + 4, 1, 64, 2, 32, BF16, P_W, 1 << 30, None) == ALIGNMENT
+    assert kv(P_K, P_V, P_O, 1, 64, 2, 32, BF16, P_W, 8, None) == WORKSPACE
+    assert kv(P_K, P_V, P_K + 64, 1, 64, 2, 32, BF16, P_W, 1 << 30, None) == INVALID
+    ap = L.sana_linattn_apply
+    assert ap(P_Q, None, P_O, 1, 64, 2, 32, 1e-6, BF16, None) == INVALID
+    assert ap(P_Q, P_K, P_O, 1, 64, 2, 32, -2.0, BF16, None) == INVALID
+    assert ap(P_Q, P_K, P_Q, 1, 64, 2, 32, 1e-6, BF16, None) == INVALID
+    assert ap(P_Q, P_K, P_O + 2, 1, 64, 2, 32, 1e-6, BF16, None) == ALIGNMENT
+    assert ap(P_Q, P_K, P_O, 1, 64, 2, 32, 1e-6, 5, None) == UNSUPPORTED
+
+
+def test_binding_raises_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    import relu_linear_attention_attn_amd as R
+
+    x = torch.zeros((1, 16, 2, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        R.forward(x, x, x)
+    with pytest.raises(TypeError if torch.cuda.is_available() else ValueError):
+        R.forward(x.half(), x.half(), x.half())
