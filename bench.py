@@ -39,6 +39,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run two plain device copies of this size (the "
+                         "reference for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, "
+                         "WRITE_SIZE) of a `--copy-mib` bench run into the traffic record")
     return ap.parse_args()
 
 
@@ -66,6 +72,52 @@ def measured_traffic(kernel: str, workload: str):
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(folder: str):
+    import csv
+    import glob
+
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _kernel_key(name: str) -> str:
+    for k, v in (("reduce_bf16_kernel", "reduce"), ("apply_bf16_kernel", "apply"),
+                 ("fused_bf16_kernel", "fused"), ("bitwise_not", "copy")):
+        if k in name:
+            return v
+    return ""
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, workload: str):
+    """KiB per dispatch of FETCH_SIZE and WRITE_SIZE per kernel, calibrated
+    against the plain device copy (which must read and write copy_mib MiB)."""
+    per = {}
+    for folder, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for r in _counter_rows(folder):
+            if r["Counter_Name"] != counter:
+                continue
+            key = _kernel_key(r["Kernel_Name"])
+            if key:
+                per.setdefault(key, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+    copy_kib = copy_mib * 1024.0
+    avg = {k: {c: sum(v[1:] or v) / len(v[1:] or v) for c, v in d.items()} for k, d in per.items()}
+    f_scale = copy_kib / avg["copy"]["FETCH_SIZE"]
+    w_scale = copy_kib / avg["copy"]["WRITE_SIZE"]
+    kernels = {}
+    for k, d in avg.items():
+        if k == "copy":
+            continue
+        fb = d["FETCH_SIZE"] * f_scale * 1024
+        wb = d["WRITE_SIZE"] * w_scale * 1024
+        kernels[k] = {"fetch_kib_raw": d["FETCH_SIZE"], "write_kib_raw": d["WRITE_SIZE"],
+                      "fetch_bytes": fb, "write_bytes": wb, "hbm_bytes_per_launch": fb + wb}
+    return {"workload": workload, "kernel_source_sha256": kernel_source_hash(),
+            "calibration": {"copy_mib": copy_mib, "fetch_scale": f_scale,
+                            "write_scale": w_scale},
+            "kernels": kernels}
 
 
 def cpu_baseline(w, inputs, budget_s: float):
@@ -122,6 +174,12 @@ def cpu_baseline(w, inputs, budget_s: float):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        from relu_linear_attention_attn_amd import workloads as W
+        rec = summarize_counters(*args.summarize_counters, args.copy_mib or 256,
+                                 args.workload or W.HEADLINE)
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(the state reduction would shard over heads or tokens, see the "
@@ -223,6 +281,13 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic},
     }
+    if args.copy_mib > 0:  # counter calibration, outside every timed region
+        # a plain streaming kernel that reads and writes exactly copy_mib MiB
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
     if rank == 0 and args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
