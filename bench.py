@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E spec peak
 METRIC = "linear-attn fwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
-KERNELS_SRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc", "linattn_kernels.hip")
+CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_latent_4096px.json")
 
 
@@ -54,8 +54,14 @@ def log(args, *a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNELS_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the library's sources (kernels, and the host code that
+    picks their grids), in name order."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):

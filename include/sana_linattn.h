@@ -44,8 +44,10 @@
  * failed kernel launch returns SANA_ERR_HIP.
  *
  * Domain. B, N, H >= 1; d == 32 (other head widths return
- * SANA_ERR_UNSUPPORTED); B*N*H*d must fit in int64 and every tensor must be
- * addressable (total bytes < 2^62). eps must be finite and >= 0; with
+ * SANA_ERR_UNSUPPORTED); B*N*H*d must fit in int64, every tensor must be
+ * addressable (total bytes < 2^62) and B*ceil(H/2), the number of head pairs,
+ * must be below 2^31 (one kernel grid covers them). eps must be finite and
+ * >= 0; with
  * eps = 0 a query row with phi(q_i) = 0 gives 0/0 = NaN, otherwise such a row
  * gives exactly 0. Tensor pointers must be 16-byte aligned
  * (SANA_ERR_ALIGNMENT otherwise). Inputs must be finite.
@@ -79,9 +81,12 @@ typedef enum {
 } sana_status_t;
 
 typedef enum {
-  SANA_VARIANT_AUTO = 0,   /* library picks by shape */
-  SANA_VARIANT_SPLIT = 1,  /* split-N state reduction with a fixed-order fold, then apply */
-  SANA_VARIANT_FUSED = 2   /* one launch per (b, head pair): reduce into LDS, then apply */
+  SANA_VARIANT_AUTO = 0,   /* FUSED up to N = 1024, SPLIT beyond */
+  SANA_VARIANT_SPLIT = 1,  /* two launches: split-N state reduction into per-block partials,
+                              then the apply, which sums a head pair's partials in fixed
+                              order (bf16); fp32 folds them at the end of the reduction */
+  SANA_VARIANT_FUSED = 2   /* one launch, one block per (b, head pair): reduce into LDS,
+                              then apply; for short sequences */
 } sana_variant_t;
 
 /*
@@ -113,7 +118,7 @@ sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void
 /*
  * Same as sana_linattn_fwd with an explicit kernel variant (sana_variant_t).
  * Every variant computes the same function; results of one variant are
- * bitwise repeatable for the same inputs and shape.
+ * bitwise repeatable for the same inputs and shape on the same device.
  */
 sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void* v, void* out,
                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
@@ -124,10 +129,11 @@ sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void*
  * sana_linattn_fwd_variant that also times its kernels: it records events[0]
  * on `stream` before the first kernel and events[i] right after kernel i, so
  * hipEventElapsedTime(events[i-1], events[i]) is the duration of kernel i.
- * The kernels, in order: SPLIT - the state reduction over token chunks
- * (whose last block per head pair folds the chunk partials into the state in
- * fixed order), then the apply; FUSED - the single fused kernel. *n_kernels
- * (if not NULL) receives that count (2 or 1) even when the call fails. The events are created by the caller (hipEventCreate);
+ * The kernels, in order: SPLIT - the state reduction over token ranges,
+ * then the apply (which, in bf16, also sums the reduction's partials); FUSED -
+ * its single kernel. *n_kernels (if not NULL) receives that count (2 or 1)
+ * whenever the shape, dtype and variant are valid, even when the call fails
+ * otherwise. The events are created by the caller (hipEventCreate);
  * n_events must be at least *n_kernels + 1, else SANA_ERR_INVALID_ARG.
  * Computes exactly what sana_linattn_fwd_variant computes.
  */

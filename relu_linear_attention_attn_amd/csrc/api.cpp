@@ -4,9 +4,11 @@
 
 #include "sana_linattn.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <algorithm>
 #include <atomic>
@@ -21,9 +23,11 @@ constexpr int64_t kMinReduceChunk = 256;       // tokens: 8 tiles per wave at 2 
 constexpr int64_t kMinApplyChunk = 256;
 constexpr int64_t kWorkspaceBlocks = 4096;     // reduction blocks the workspace allows for
 constexpr int64_t kMaxReduceChunks = 64;
-constexpr int64_t kMaxRounds = 4;              // block rounds considered when fitting the grid
 constexpr int64_t kFusedMaxN = 1024;           // AUTO picks the fused kernel up to this N
 constexpr int64_t kReduceWavesPerCu = 8;
+constexpr int64_t kMaxRangeBlocks = 2048;      // bf16 blocks per launch, any device
+constexpr int64_t kMinTilesPerWave = 4;        // bf16: fewer tiles per wave than this
+                                               // and blocks are not worth their epilogue
 constexpr size_t kAlign = 256;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -60,9 +64,12 @@ sana_status_t check_shape(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
       __builtin_mul_overflow(t, d, &t) || __builtin_mul_overflow(t, item, &t) ||
       t >= (int64_t(1) << 62))
     return SANA_ERR_INVALID_ARG;
-  // state and workspace sizes stay far below this once B*H fits
-  int64_t bh = 0;
-  if (__builtin_mul_overflow(B, H, &bh) || bh > (int64_t(1) << 40)) return SANA_ERR_INVALID_ARG;
+  // head pairs index one grid dimension (every grid has at most
+  // max(units, co-resident blocks) blocks); the state and workspace sizes
+  // stay far below the tensor limit then
+  int64_t units = 0;
+  if (__builtin_mul_overflow(B, cdiv(H, kHeadsPerBlock), &units) || units > INT32_MAX)
+    return SANA_ERR_INVALID_ARG;
   if (tensor_bytes) *tensor_bytes = static_cast<size_t>(t);
   return SANA_OK;
 }
@@ -81,8 +88,16 @@ Plan make_plan(int64_t B, int64_t N, int64_t H) {
   p.H = H;
   p.pairs = cdiv(H, kHeadsPerBlock);
   p.units = B * p.pairs;
-  // The workspace holds up to red_chunks_max chunk partials per head. The
-  // bound stops depending on N once N >= kMinReduceChunk * red_chunks_max.
+  p.tiles = cdiv(N, kTile);
+  const int64_t F = p.units * p.tiles;
+  // bf16 ranges: at most kMaxRangeBlocks blocks, so at least ceil(F / that)
+  // tiles per block and at most ceil(T / q_min) + 1 blocks touching a unit.
+  const int64_t q_min = cdiv(F, kMaxRangeBlocks);
+  p.slots = std::min(p.tiles, cdiv(p.tiles, q_min)) + 1;
+  p.red_q = q_min;
+  p.red_blocks = cdiv(F, q_min);
+  // fp32 chunks: at most red_chunks_max, a bound that stops depending on N
+  // once N >= kMinReduceChunk * red_chunks_max.
   p.red_chunks_max = clamp64(std::min(cdiv(kWorkspaceBlocks, p.units), cdiv(N, kMinReduceChunk)),
                              1, kMaxReduceChunks);
   p.red_chunk = chunk_tokens(N, p.red_chunks_max);
@@ -90,7 +105,10 @@ Plan make_plan(int64_t B, int64_t N, int64_t H) {
   p.app_chunk = cdiv(N, kTile) * kTile;
   p.app_chunks = 1;
   const size_t bh = static_cast<size_t>(B * H);
-  p.partial_bytes = align_up(static_cast<size_t>(p.red_chunks_max) * bh * kStateFloats * 4);
+  const size_t f32_partials = static_cast<size_t>(p.red_chunks_max) * bh * kStateFloats * 4;
+  const size_t bf16_partials =
+      static_cast<size_t>(p.units) * static_cast<size_t>(p.slots) * 2 * kStateFloats * 4;
+  p.partial_bytes = align_up(std::max(f32_partials, bf16_partials));
   p.state_bytes = align_up(bh * kStateFloats * 4);
   p.ctl_bytes = align_up(static_cast<size_t>(p.units) * sizeof(unsigned long long));
   p.workspace_bytes = p.partial_bytes + p.state_bytes + p.ctl_bytes;
@@ -124,24 +142,6 @@ const DeviceCaps& device_caps() {
   return caps[dev];
 }
 
-// Chunks per unit such that the grid (units * chunks blocks) fills whole
-// rounds of `cap` co-resident blocks as closely as possible.
-int64_t pick_chunks(int64_t units, int64_t cap, int64_t max_chunks) {
-  int64_t best = 1;
-  double best_fill = -1.0;
-  for (int64_t k = 1; k <= kMaxRounds; ++k) {
-    const int64_t c = clamp64(k * cap / units, 1, max_chunks);
-    const int64_t blocks = units * c;
-    const int64_t rounds = cdiv(blocks, cap);
-    const double fill = static_cast<double>(blocks) / static_cast<double>(rounds * cap);
-    if (fill > best_fill + 0.01) {
-      best_fill = fill;
-      best = c;
-    }
-  }
-  return best;
-}
-
 }  // namespace
 
 void fit_plan_to_device(Plan& p, int dtype) {
@@ -149,24 +149,42 @@ void fit_plan_to_device(Plan& p, int dtype) {
   const int dt = dtype == SANA_DTYPE_BF16 ? 1 : 0;
   const int64_t rcap = static_cast<int64_t>(c.cus) * c.occ[0][dt];
   const int64_t acap = static_cast<int64_t>(c.cus) * c.occ[1][dt];
-  // The reduction's cost grows with its chunk count (every chunk adds a
-  // partial to write and fold), so it takes the fewest chunks that still
-  // keep about kReduceWavesPerCu waves streaming on every CU, within one
-  // round of co-resident blocks.
-  const int64_t waves = static_cast<int64_t>(c.cus) * kReduceWavesPerCu;
-  const int64_t want = cdiv(waves, p.units * reduce_block_waves(dtype));
-  int64_t rc = clamp64(std::min(want, std::max<int64_t>(1, rcap / p.units)), 1, p.red_chunks_max);
+  if (dt == 1) {
+    // bf16 reduction: one round of co-resident blocks over equal shares of
+    // the (unit, tile) index; never more blocks than the workspace allows for
+    const int64_t F = p.units * p.tiles;
+    int64_t g = std::min<int64_t>(rcap, kMaxRangeBlocks);
+    g = std::min(g, std::max<int64_t>(1, F / (block_waves(KernelKind::kReduce, dt) *
+                                                 kMinTilesPerWave)));
 #ifdef SANA_TUNING
-  if (const char* e = getenv("SANA_RED_CHUNKS")) rc = clamp64(atoll(e), 1, p.red_chunks_max);
+    if (const char* e = getenv("SANA_RED_BLOCKS")) g = clamp64(atoll(e), 1, kMaxRangeBlocks);
 #endif
-  p.red_chunk = chunk_tokens(p.N, rc);
-  p.red_chunks = cdiv(p.N, p.red_chunk);
-  int64_t ac = pick_chunks(p.units, acap, std::max<int64_t>(1, cdiv(p.N, kMinApplyChunk)));
+    p.red_q = cdiv(F, g);
+    p.red_blocks = cdiv(F, p.red_q);
+  } else {
+    // fp32 reduction: (unit, chunk) grid with the fewest chunks that keep
+    // about kReduceWavesPerCu waves streaming per CU within one round
+    const int64_t waves = static_cast<int64_t>(c.cus) * kReduceWavesPerCu;
+    const int64_t want = cdiv(waves, p.units * block_waves(KernelKind::kReduce, dtype));
+    const int64_t rc = clamp64(std::min(want, std::max<int64_t>(1, rcap / p.units)), 1,
+                               p.red_chunks_max);
+    p.red_chunk = chunk_tokens(p.N, rc);
+    p.red_chunks = cdiv(p.N, p.red_chunk);
+  }
+  // apply: (unit, chunk) grid of at most one round of co-resident blocks
+  // (measured: extra rounds cost more than idle slots in the one round)
+  int64_t ac = clamp64(acap / p.units, 1, std::max<int64_t>(1, cdiv(p.N, kMinApplyChunk)));
 #ifdef SANA_TUNING
   if (const char* e = getenv("SANA_APP_CHUNKS")) ac = std::max<int64_t>(1, atoll(e));
 #endif
   p.app_chunk = chunk_tokens(p.N, ac);
   p.app_chunks = cdiv(p.N, p.app_chunk);
+#ifdef SANA_TUNING
+  if (getenv("SANA_PRINT_PLAN"))
+    fprintf(stderr, "plan cus %d occ red %d app %d | red blocks %lld q %lld | app chunks %lld chunk %lld\n",
+            c.cus, c.occ[0][dt], c.occ[1][dt], (long long)p.red_blocks, (long long)p.red_q,
+            (long long)p.app_chunks, (long long)p.app_chunk);
+#endif
 }
 
 namespace {
@@ -180,11 +198,20 @@ sana_status_t check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
 
 sana_status_t to_status(hipError_t e) { return e == hipSuccess ? SANA_OK : SANA_ERR_HIP; }
 
-bool use_fused(const Plan& p, int variant) {
-  if (variant == SANA_VARIANT_FUSED) return true;
-  if (variant == SANA_VARIANT_SPLIT) return false;
-  return p.N <= kFusedMaxN;
+bool valid_variant(int variant) {
+  return variant == SANA_VARIANT_AUTO || variant == SANA_VARIANT_SPLIT ||
+         variant == SANA_VARIANT_FUSED;
 }
+
+// The kernel arrangement a call runs: AUTO takes the fused kernel for short
+// sequences (one block per head pair fills the device poorly once N grows,
+// but saves the second launch while N is small) and the split pair beyond.
+int resolve_variant(const Plan& p, int variant) {
+  if (variant != SANA_VARIANT_AUTO) return variant;
+  return p.N <= kFusedMaxN ? SANA_VARIANT_FUSED : SANA_VARIANT_SPLIT;
+}
+
+int kernels_of(int variant) { return variant == SANA_VARIANT_SPLIT ? 2 : 1; }
 
 // A fresh tag per call for the per-pair control words (48 bits; never 0).
 unsigned long long next_epoch() {
@@ -199,13 +226,14 @@ unsigned long long next_epoch() {
 struct WorkspaceParts {
   float* partials;
   float* state;
-  unsigned long long* ctl;
+  unsigned long long* ctl;  // one control word per unit
 };
 
 WorkspaceParts split_workspace(const Plan& p, void* ws) {
   char* base = static_cast<char*>(ws);
-  return {reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + p.partial_bytes),
-          reinterpret_cast<unsigned long long*>(base + p.partial_bytes + p.state_bytes)};
+  unsigned long long* ctl =
+      reinterpret_cast<unsigned long long*>(base + p.partial_bytes + p.state_bytes);
+  return {reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + p.partial_bytes), ctl};
 }
 
 }  // namespace
@@ -234,36 +262,73 @@ sana_status_t sana_linattn_state_size(int64_t B, int64_t H, int64_t d, size_t* b
   return SANA_OK;
 }
 
+}  // extern "C"
+
+namespace sana {
+namespace {
+
+// The forward pass behind every fwd entry point. events (may be NULL) are
+// recorded before the first kernel and after each kernel.
+sana_status_t forward(const void* q, const void* k, const void* v, void* out, int64_t B,
+                      int64_t N, int64_t H, int64_t d, float eps, int dtype, int variant,
+                      void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
+                      int* n_kernels, hipStream_t stream) {
+  size_t tb = 0;
+  sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
+  if (s != SANA_OK) return s;
+  if (!valid_variant(variant)) return SANA_ERR_UNSUPPORTED;
+  const Plan p = make_plan(B, N, H);
+  const int run = resolve_variant(p, variant);
+  const int nk = kernels_of(run);
+  if (n_kernels) *n_kernels = nk;
+  if (events) {
+    if (n_events < nk + 1) return SANA_ERR_INVALID_ARG;
+    for (int i = 0; i <= nk; ++i)
+      if (!events[i]) return SANA_ERR_INVALID_ARG;
+  }
+  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
+  if ((s = check_eps(eps)) != SANA_OK) return s;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return SANA_ERR_ALIGNMENT;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+    return SANA_ERR_INVALID_ARG;
+  if ((s = check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
+  if (overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
+
+  // every check passed: from here on HIP is called
+  (void)hipGetLastError();  // clear an unrelated earlier error
+  Plan fp = p;
+  fit_plan_to_device(fp, dtype);
+  auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+  if (!mark(0)) return SANA_ERR_HIP;
+  const WorkspaceParts w = split_workspace(fp, workspace);
+  if (run == SANA_VARIANT_FUSED) {
+    if (launch_fused(fp, dtype, q, k, v, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
+    return mark(1) ? SANA_OK : SANA_ERR_HIP;
+  }
+  // split: bf16 hands the reduction's partials straight to the apply (no
+  // fold at the end of the reduction); fp32 folds, then applies the state
+  const bool bf16 = dtype == SANA_DTYPE_BF16;
+  if (launch_reduce(fp, dtype, !bf16, k, v, w.partials, w.state, w.ctl, next_epoch(), stream) !=
+      hipSuccess)
+    return SANA_ERR_HIP;
+  if (!mark(1)) return SANA_ERR_HIP;
+  const hipError_t e = bf16 ? launch_apply_partials(fp, q, w.partials, out, eps, stream)
+                            : launch_apply(fp, dtype, q, w.state, out, eps, stream);
+  if (e != hipSuccess) return SANA_ERR_HIP;
+  return mark(2) ? SANA_OK : SANA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace sana
+
+extern "C" {
+
 sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void* v, void* out,
                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
                                        int dtype, int variant, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream) {
-  size_t tb = 0;
-  sana_status_t s = sana::check_shape(B, N, H, d, dtype, &tb);
-  if (s != SANA_OK) return s;
-  if (variant != SANA_VARIANT_AUTO && variant != SANA_VARIANT_SPLIT && variant != SANA_VARIANT_FUSED)
-    return SANA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
-  if ((s = sana::check_eps(eps)) != SANA_OK) return s;
-  if (sana::misaligned(q) || sana::misaligned(k) || sana::misaligned(v) || sana::misaligned(out))
-    return SANA_ERR_ALIGNMENT;
-  if (sana::overlaps(out, tb, q, tb) || sana::overlaps(out, tb, k, tb) ||
-      sana::overlaps(out, tb, v, tb))
-    return SANA_ERR_INVALID_ARG;
-  const Plan p = sana::make_plan(B, N, H);
-  if ((s = sana::check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
-  if (sana::overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
-
-  (void)hipGetLastError();  // clear an unrelated earlier error
-  Plan fp = p;
-  sana::fit_plan_to_device(fp, dtype);
-  if (sana::use_fused(fp, variant))
-    return sana::to_status(sana::launch_fused(fp, dtype, q, k, v, out, eps, stream));
-  const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
-  if (sana::launch_reduce(fp, dtype, k, v, w.partials, w.state, w.ctl, sana::next_epoch(),
-                          stream) != hipSuccess)
-    return SANA_ERR_HIP;
-  return sana::to_status(sana::launch_apply(fp, dtype, q, w.state, out, eps, stream));
+  return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, variant, workspace, workspace_bytes,
+                       nullptr, 0, nullptr, stream);
 }
 
 sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void* v, void* out,
@@ -271,43 +336,17 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
                                         int dtype, int variant, void* workspace,
                                         size_t workspace_bytes, hipEvent_t* events,
                                         int n_events, int* n_kernels, hipStream_t stream) {
-  size_t tb = 0;
-  sana_status_t s = sana::check_shape(B, N, H, d, dtype, &tb);
-  if (s != SANA_OK) return s;
-  if (variant != SANA_VARIANT_AUTO && variant != SANA_VARIANT_SPLIT && variant != SANA_VARIANT_FUSED)
-    return SANA_ERR_UNSUPPORTED;
-  const sana::Plan p = sana::make_plan(B, N, H);
-  const bool fused = sana::use_fused(p, variant);
-  const int nk = fused ? 1 : 2;
-  if (n_kernels) *n_kernels = nk;
-  if (!events || n_events < nk + 1) return SANA_ERR_INVALID_ARG;
-  for (int i = 0; i <= nk; ++i)
-    if (!events[i]) return SANA_ERR_INVALID_ARG;
-  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
-  if ((s = sana::check_eps(eps)) != SANA_OK) return s;
-  if (sana::misaligned(q) || sana::misaligned(k) || sana::misaligned(v) || sana::misaligned(out))
-    return SANA_ERR_ALIGNMENT;
-  if (sana::overlaps(out, tb, q, tb) || sana::overlaps(out, tb, k, tb) ||
-      sana::overlaps(out, tb, v, tb))
+  if (!events) {
+    if (n_kernels) {
+      // still report the kernel count when the arguments allow it
+      size_t tb = 0;
+      if (sana::check_shape(B, N, H, d, dtype, &tb) == SANA_OK && sana::valid_variant(variant))
+        *n_kernels = sana::kernels_of(sana::resolve_variant(sana::make_plan(B, N, H), variant));
+    }
     return SANA_ERR_INVALID_ARG;
-  if ((s = sana::check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
-  if (sana::overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
-
-  (void)hipGetLastError();
-  Plan fp = p;
-  sana::fit_plan_to_device(fp, dtype);
-  if (hipEventRecord(events[0], stream) != hipSuccess) return SANA_ERR_HIP;
-  if (fused) {
-    if (sana::launch_fused(fp, dtype, q, k, v, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
-    return sana::to_status(hipEventRecord(events[1], stream));
   }
-  const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
-  if (sana::launch_reduce(fp, dtype, k, v, w.partials, w.state, w.ctl, sana::next_epoch(),
-                          stream) != hipSuccess)
-    return SANA_ERR_HIP;
-  if (hipEventRecord(events[1], stream) != hipSuccess) return SANA_ERR_HIP;
-  if (sana::launch_apply(fp, dtype, q, w.state, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
-  return sana::to_status(hipEventRecord(events[2], stream));
+  return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, variant, workspace, workspace_bytes,
+                       events, n_events, n_kernels, stream);
 }
 
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -336,7 +375,7 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, 
   Plan fp = p;
   sana::fit_plan_to_device(fp, dtype);
   const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
-  return sana::to_status(sana::launch_reduce(fp, dtype, k, v, w.partials, state, w.ctl,
+  return sana::to_status(sana::launch_reduce(fp, dtype, true, k, v, w.partials, state, w.ctl,
                                              sana::next_epoch(), stream));
 }
 

@@ -16,21 +16,28 @@ constexpr int kStateFloats = kHeadDim * kStateCols;   // 1056 floats = 4224 byte
 constexpr int kTile = 16;                             // tokens per wave iteration
 constexpr int kHeadsPerBlock = 2;                     // a head pair shares 128-byte lines (bf16)
 
-// Work split of one call. The chunk counts depend on the device (CU count and
-// kernel occupancy) so that every round of blocks fills the chip; the
-// workspace is sized for the largest count any device can pick.
+// Work split of one call. The bf16 reduction runs blocks over balanced
+// ranges of the flattened (head-pair unit, tile) index; the fp32 reduction
+// and both applies run (unit, token chunk) grids. The block and chunk counts
+// depend on the device (CU count and kernel occupancy); the workspace is
+// sized for the largest counts any device can pick.
 struct Plan {
   int64_t B, N, H;
   int64_t pairs;          // ceil(H / 2) head pairs per batch item
-  int64_t units;          // B * pairs: blocks per token chunk
+  int64_t units;          // B * pairs
+  int64_t tiles;          // 16-token tiles per unit, ceil(N / 16)
+  // bf16 reduction: blocks and tiles per block (ranges of the flattened index)
+  int64_t red_blocks, red_q;
+  int64_t slots;          // partial slots per unit the workspace holds
+  // token chunks (fp32 reduction; apply of both dtypes)
   int64_t red_chunk;      // tokens per reduction chunk (multiple of kTile)
   int64_t red_chunks;     // chunks used (<= red_chunks_max)
   int64_t red_chunks_max; // chunks the workspace is sized for
   int64_t app_chunk;      // tokens per apply chunk (multiple of kTile)
   int64_t app_chunks;
-  size_t partial_bytes;   // workspace bytes for chunk partials
+  size_t partial_bytes;   // workspace bytes for partials
   size_t state_bytes;     // workspace bytes for the combined state
-  size_t ctl_bytes;       // workspace bytes for the per-pair control words
+  size_t ctl_bytes;       // workspace bytes for the per-unit control words
   size_t workspace_bytes; // total
 };
 
@@ -41,16 +48,22 @@ void fit_plan_to_device(Plan& p, int dtype);
 
 enum class KernelKind { kReduce, kApply };
 int occupancy_blocks_per_cu(KernelKind kind, int dtype);
-int reduce_block_waves(int dtype);  // waves per block of the reduction kernel
+int block_waves(KernelKind kind, int dtype);  // waves per block
 
 // Launchers. They enqueue on `stream` and return the launch status.
-// dtype: 0 = fp32, 1 = bf16 (sana_dtype_t). The reduction writes chunk
-// partials, and the last block of each head pair folds them into `state`.
-hipError_t launch_reduce(const Plan& p, int dtype, const void* k, const void* v,
+// dtype: 0 = fp32, 1 = bf16 (sana_dtype_t). The reduction writes per-block
+// partials; with fold (always for fp32) the last block of each head pair
+// also folds them into `state`, without (bf16) the partials are the result
+// and launch_apply_partials sums them where it needs them.
+hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, const void* v,
                          float* partials, float* state, unsigned long long* ctl,
                          unsigned long long epoch, hipStream_t stream);
+// Apply from a folded [B][H][d][d+1] state.
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state,
                         void* out, float eps, hipStream_t stream);
+// bf16 apply from the partials of launch_reduce(fold = false) with the same plan.
+hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
+                                 float eps, hipStream_t stream);
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k,
                         const void* v, void* out, float eps, hipStream_t stream);
 

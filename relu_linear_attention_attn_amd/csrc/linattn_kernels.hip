@@ -238,26 +238,6 @@ __device__ __forceinline__ void store_state_from_mfma32(float* dst, const f32x16
   if (l < 32) put<Coherent>(dst + l * kSC + kD, ks + hi);
 }
 
-// Sums the accumulators of the S sub-stream waves of a block into wave 0 in
-// fixed order (0, then 1, 2, ...), one wave at a time through `xchg`
-// (R floats per lane). All threads of the block must call.
-template <int R>
-__device__ __forceinline__ void fold_substreams(float (&regs)[R], float* xchg, int sub, int S) {
-  const int l = lane_id();
-  for (int s = 1; s < S; ++s) {
-    if (sub == s) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) xchg[r * kWave + l] = regs[r];
-    }
-    __syncthreads();
-    if (sub == 0) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) regs[r] += xchg[r * kWave + l];
-    }
-    __syncthreads();
-  }
-}
-
 // Chunk partials of a head pair are folded into the final state by the last
 // block to finish that pair, in ascending chunk order, so the result does not
 // depend on which block finishes last. The hand-off between blocks (which may
@@ -297,28 +277,46 @@ __device__ __forceinline__ bool arrive_last(unsigned long long* ctl, unsigned lo
   return last != 0;
 }
 
-// state[h][e] = sum_{p < P} partials[p][h][e] for the (up to two) heads of a
-// pair. All loads of a batch are issued before any is added, so the fold
-// costs about one memory round trip per 16 chunks; the sum itself runs in
-// ascending p.
-__device__ __forceinline__ void fold_partials(const float* __restrict__ partials,
-                                             float* __restrict__ state, int64_t bh0, int nheads,
-                                             int64_t BH, int64_t P) {
+// dst[e] = sum_{p < P} src[p * stride + e] for e < n, in ascending p. All
+// loads of a batch are issued before any is added, so the fold costs about
+// one memory round trip per 16 partials.
+__device__ __forceinline__ void fold_partials(const float* __restrict__ src, int64_t stride,
+                                             float* __restrict__ dst, int n, int64_t P) {
   constexpr int kBatch = 16;
-  const int64_t stride = BH * kSF;
-  for (int e = threadIdx.x; e < nheads * kSF; e += blockDim.x) {
-    const float* src = partials + bh0 * kSF + e;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
     float acc = 0.0f;
     for (int64_t p0 = 0; p0 < P; p0 += kBatch) {
       float x[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        x[u] = p0 + u < P ? load_coherent(src + (p0 + u) * stride) : 0.0f;
+        x[u] = p0 + u < P ? load_coherent(src + (p0 + u) * stride + e) : 0.0f;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (p0 + u < P) acc = (p0 + u == 0) ? x[u] : acc + x[u];
     }
-    state[bh0 * kSF + e] = acc;
+    dst[e] = acc;
+  }
+}
+
+// Pairwise tree over the S waves of a block (R floats per lane): in the round
+// with stride s, wave w with w % 2s == s adds into wave w - s. After
+// ceil(log2 S) rounds wave 0 holds the sum, in an order fixed by S alone.
+// xchg holds ceil(S/2) * R * 64 floats. All threads of the block must call.
+template <int R>
+__device__ __forceinline__ void tree_fold(float (&regs)[R], float* xchg, int sub, int S) {
+  const int l = lane_id();
+  for (int s = 1; s < S; s *= 2) {
+    float* d = xchg + (sub / (2 * s)) * R * kWave;
+    if (sub % (2 * s) == s) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) d[r * kWave + l] = regs[r];
+    }
+    __syncthreads();
+    if (sub % (2 * s) == 0 && sub + s < S) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) regs[r] += d[r * kWave + l];
+    }
+    __syncthreads();
   }
 }
 
@@ -379,10 +377,13 @@ __device__ __forceinline__ u32x4 apply_head(const ApplyOperands& op, u32x4 qpiec
 // Applies the pair's two heads to the tiles sub, sub + S, ... of [n_lo, n_hi).
 // `two` as for reduce_pair_wave: with one head, the second half-line is read
 // from the first head (inside the tensor), computed and never stored.
-template <int U>
+// make_ops(op) fills the two heads' operands; it runs after the first U tiles'
+// loads are issued, so whatever it waits for (the state's loads, a block
+// barrier: every wave of the block calls it) overlaps those loads.
+template <int U, class MakeOps>
 __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict__ Q,
                                                 unsigned short* __restrict__ Out,
-                                                const ApplyOperands (&op)[2], float eps,
+                                                MakeOps&& make_ops, float eps,
                                                 int64_t row, int64_t base, int64_t n_lo,
                                                 int64_t n_hi, int sub, int S, bool two,
                                                 unsigned char* slot) {
@@ -408,6 +409,8 @@ __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u, qb[u]);
+  ApplyOperands op[2];
+  make_ops(op);
 
   // stage the tile's lines, compute both heads in place in the tile, and read
   // the output lines back; `full` says the whole tile is inside the range
@@ -666,56 +669,108 @@ __device__ __forceinline__ PairCoords pair_coords(int64_t pairs, int64_t units, 
 }
 
 // LDS of a bf16 reduction block: one K + V tile slot per wave, reused at the
-// end to pass accumulators between waves (32 floats per lane at a time).
+// end of each head pair's range to fold the waves' sums (34 floats per lane).
+constexpr int kFoldFloats = 34;  // 32 accumulator registers + ksum of both heads
 template <int S>
 union RedLds {
   unsigned char slot[S][2 * kTileBytes];
-  float xchg[32 * kWave];
+  float xchg[((S + 1) / 2) * kFoldFloats * kWave];
 };
 
-// Sums the block's sub-stream accumulators into wave 0, in sub-stream order.
+// Sums the block's sub-stream sums into wave 0 (fixed tree order).
 template <int S>
 __device__ __forceinline__ void fold_pair_accumulators(f32x16 (&acc)[2], float (&ks)[2],
                                                        RedLds<S>& lds, int sub) {
   if (S == 1) return;
   __syncthreads();  // every wave is done with its tile slot
-  float regs[32];
+  float regs[kFoldFloats];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     regs[r] = acc[0][r];
     regs[16 + r] = acc[1][r];
   }
-  fold_substreams<32>(regs, lds.xchg, sub, S);
+  regs[32] = ks[0];
+  regs[33] = ks[1];
+  tree_fold<kFoldFloats>(regs, lds.xchg, sub, S);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     acc[0][r] = regs[r];
     acc[1][r] = regs[16 + r];
   }
-  fold_substreams<2>(ks, lds.xchg, sub, S);
+  ks[0] = regs[32];
+  ks[1] = regs[33];
 }
 
-template <int S, int U>
+// Balanced ranges. The work of a bf16 kernel is the flattened index
+// f = unit * T + t over head-pair units (b, pair) and their T 16-token tiles.
+// Block g takes f in [g * Qb, (g + 1) * Qb): one round of co-resident blocks,
+// equal shares, crossing unit boundaries where they fall. Within a unit's
+// segment the block's S waves take its tiles as interleaved sub-streams.
+struct Segment {
+  int64_t unit, b, h, n_lo, n_hi;
+  bool two;
+};
+
+__device__ __forceinline__ Segment segment_of(int64_t unit, int64_t f_lo, int64_t f_hi, int64_t T,
+                                              int64_t N, int64_t H, int64_t pairs) {
+  Segment sg;
+  sg.unit = unit;
+  sg.b = unit / pairs;
+  sg.h = 2 * (unit % pairs);
+  sg.two = sg.h + 1 < H;
+  const int64_t t_lo = (f_lo > unit * T ? f_lo : unit * T) - unit * T;
+  const int64_t t_hi = (f_hi < (unit + 1) * T ? f_hi : (unit + 1) * T) - unit * T;
+  sg.n_lo = t_lo * kTile;
+  sg.n_hi = t_hi * kTile < N ? t_hi * kTile : N;
+  return sg;
+}
+
+// The blocks of the reduction that touch unit `unit` when block g covers
+// tiles [g * Qb, (g + 1) * Qb) of the flattened (unit, tile) index: blocks
+// first .. first + count - 1. Block g writes the unit's partial g - first.
+struct SlotRange {
+  int64_t first, count;
+};
+__device__ __forceinline__ SlotRange slot_range(int64_t unit, int64_t T, int64_t Qb) {
+  const int64_t first = unit * T / Qb;
+  return {first, ((unit + 1) * T - 1) / Qb - first + 1};
+}
+
+// State reduction over one block's range. For each unit it touches, the
+// block folds its waves' sums and writes them as partial number
+// (g - first block of the unit) of that unit. With Fold, the last of the
+// unit's contributing blocks also folds the unit's partials, in order, into
+// the state; without, the partials are the result (the apply sums them).
+// Partials: [units][slots][2 heads][d][d+1].
+template <int S, int U, bool Fold>
 __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
     float* __restrict__ partials, float* __restrict__ state, unsigned long long* __restrict__ ctl,
-    unsigned long long epoch, int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk,
-    int64_t nchunks, int64_t BH) {
+    unsigned long long epoch, int64_t N, int64_t H, int64_t pairs, int64_t T, int64_t Qb,
+    int64_t F, int64_t slots) {
   __shared__ RedLds<S> lds;
-  const PairCoords pc = pair_coords(pairs, units, H);
-  const int64_t n_lo = pc.p * chunk;
-  const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
-  const int64_t base = (pc.b * N * H + pc.h) * kD;
-  f32x16 acc[2] = {(f32x16)0, (f32x16)0};
-  float ks[2] = {0.0f, 0.0f};
-  reduce_pair_wave<U>(K, V, H * kD, base, n_lo, n_hi, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
-  fold_pair_accumulators<S>(acc, ks, lds, pc.sub);
-  const int64_t bh = pc.b * H + pc.h;
-  if (pc.sub == 0) {
-    store_state_from_mfma32<true>(partials + (pc.p * BH + bh) * kSF, acc[0], ks[0]);
-    if (pc.two) store_state_from_mfma32<true>(partials + (pc.p * BH + bh + 1) * kSF, acc[1], ks[1]);
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t g = blockIdx.x;
+  const int64_t f_lo = g * Qb;
+  const int64_t f_hi = f_lo + Qb < F ? f_lo + Qb : F;
+  for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
+    const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
+    const int64_t base = (sg.b * N * H + sg.h) * kD;
+    f32x16 acc[2] = {(f32x16)0, (f32x16)0};
+    float ks[2] = {0.0f, 0.0f};
+    reduce_pair_wave<U>(K, V, H * kD, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub], acc, ks);
+    fold_pair_accumulators<S>(acc, ks, lds, sub);
+    const SlotRange sr = slot_range(unit, T, Qb);
+    float* part = partials + ((unit * slots) + (g - sr.first)) * 2 * kSF;
+    if (sub == 0) {
+      store_state_from_mfma32<Fold>(part, acc[0], ks[0]);
+      if (sg.two) store_state_from_mfma32<Fold>(part + kSF, acc[1], ks[1]);
+    }
+    if (Fold && arrive_last(ctl + unit, epoch, sr.count))
+      fold_partials(partials + unit * slots * 2 * kSF, 2 * kSF, state + (sg.b * H + sg.h) * kSF,
+                    (sg.two ? 2 : 1) * kSF, sr.count);
+    __syncthreads();  // the LDS is reused by the next segment
   }
-  if (arrive_last(ctl + blockIdx.x % units, epoch, nchunks))
-    fold_partials(partials, state, bh, pc.two ? 2 : 1, BH, nchunks);
 }
 
 template <int S, int U>
@@ -740,26 +795,70 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
     store_state_from_f32<true>(partials + (bc.p * BH + bc.b * H + bc.h) * kSF, acc);
   const int64_t unit = blockIdx.x % units;
   if (arrive_last(ctl + unit, epoch, nchunks)) {
-    const int64_t h0 = 2 * (unit % pairs);
-    fold_partials(partials, state, bc.b * H + h0, H - h0 < 2 ? 1 : 2, BH, nchunks);
+    const int64_t bh0 = bc.b * H + 2 * (unit % pairs);
+    fold_partials(partials + bh0 * kSF, BH * kSF, state + bh0 * kSF,
+                  (H - 2 * (unit % pairs) < 2 ? 1 : 2) * kSF, nchunks);
   }
 }
 
+// Apply, one block per (unit, token chunk): block g takes chunk g % C (Qa
+// tiles) of unit g / C. The state of a unit is the sum of `count`
+// consecutive [2][d][d+1] slots at src + b * sb + p * sp (+ j * 2 * kSF),
+// count from slot_range(unit, T, Qr) when Qr > 0 (the partials of the
+// reduction, summed here in ascending slot order, as fold_partials does), else
+// 1 (a folded state). The block sums them once into LDS; each wave then builds
+// its MFMA operands from there.
 template <int S, int U>
 __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
-    const unsigned short* __restrict__ Q, const float* __restrict__ state,
-    unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
-    int64_t units, int64_t chunk) {
+    const unsigned short* __restrict__ Q, const float* __restrict__ src, int64_t sb, int64_t sp,
+    int64_t Qr, unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
+    int64_t T, int64_t C, int64_t Qa) {
+  static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
   __shared__ unsigned char slots[S][kTileBytes];
-  const PairCoords pc = pair_coords(pairs, units, H);
-  const int64_t n_lo = pc.p * chunk;
-  const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
-  const int64_t base = (pc.b * N * H + pc.h) * kD;
-  const float* st = state + (pc.b * H + pc.h) * kSF;
-  ApplyOperands op[2];
-  op[0] = make_apply_operands(st);
-  op[1] = pc.two ? make_apply_operands(st + kSF) : op[0];
-  apply_pair_wave<U>(Q, Out, op, eps, H * kD, base, n_lo, n_hi, pc.sub, S, pc.two, slots[pc.sub]);
+  __shared__ f32x4 stage[2 * kSF / 4];
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t unit = blockIdx.x / C;
+  const int64_t f_lo = unit * T + (blockIdx.x - unit * C) * Qa;
+  const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
+  {
+    const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
+    const int64_t count = Qr > 0 ? slot_range(unit, T, Qr).count : 1;
+    const f32x4* st = reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp);
+    const int n4 = (sg.two ? 2 : 1) * kSF / 4;
+    auto make_ops = [&](ApplyOperands (&op)[2]) {
+      // Each thread sums elements e and e + blockDim.x of the pair's state.
+      // Loads are unconditional (indices clamped to valid slots and elements)
+      // and a batch's loads are all issued before any is added.
+      constexpr int kBatch = 8;
+      const int e0 = threadIdx.x < n4 ? threadIdx.x : n4 - 1;
+      const int e1 = threadIdx.x + blockDim.x < n4 ? threadIdx.x + blockDim.x : n4 - 1;
+      f32x4 a0 = st[e0], a1 = st[e1];
+      for (int64_t j0 = 1; j0 < count; j0 += kBatch) {
+        f32x4 x0[kBatch], x1[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int64_t j = j0 + u < count ? j0 + u : count - 1;
+          x0[u] = st[j * (2 * kSF / 4) + e0];
+          x1[u] = st[j * (2 * kSF / 4) + e1];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (j0 + u < count) {
+            a0 += x0[u];
+            a1 += x1[u];
+          }
+        }
+      }
+      if (threadIdx.x < n4) stage[threadIdx.x] = a0;
+      if (threadIdx.x + blockDim.x < n4) stage[threadIdx.x + blockDim.x] = a1;
+      __syncthreads();
+      const float* stf = reinterpret_cast<const float*>(stage);
+      op[0] = make_apply_operands(stf);
+      op[1] = sg.two ? make_apply_operands(stf + kSF) : op[0];
+    };
+    apply_pair_wave<U>(Q, Out, make_ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
+                       sg.n_hi, sub, S, sg.two, slots[sub]);
+  }
 }
 
 template <int S>
@@ -790,17 +889,19 @@ __global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
   f32x16 acc[2] = {(f32x16)0, (f32x16)0};
   float ks[2] = {0.0f, 0.0f};
   reduce_pair_wave<U>(K, V, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
-  fold_pair_accumulators<S>(acc, ks, lds, pc.sub);
-  if (pc.sub == 0) {
-    store_state_from_mfma32<false>(st[0], acc[0], ks[0]);
-    store_state_from_mfma32<false>(st[1], acc[1], ks[1]);
-  }
-  __syncthreads();
-  ApplyOperands op[2];
-  op[0] = make_apply_operands(st[0]);
-  op[1] = make_apply_operands(st[1]);
-  __syncthreads();  // tile slots are reused by the apply
-  apply_pair_wave<U>(Q, Out, op, eps, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub]);
+  fold_pair_accumulators<S>(acc, ks, lds, pc.sub);  // ends with a barrier: the
+                                                    // tile slots are free again
+  auto make_ops = [&](ApplyOperands (&op)[2]) {
+    if (pc.sub == 0) {
+      store_state_from_mfma32<false>(st[0], acc[0], ks[0]);
+      store_state_from_mfma32<false>(st[1], acc[1], ks[1]);
+    }
+    __syncthreads();
+    op[0] = make_apply_operands(st[0]);
+    op[1] = make_apply_operands(st[1]);
+  };
+  apply_pair_wave<U>(Q, Out, make_ops, eps, H * kD, base, 0, N, pc.sub, S, pc.two,
+                     lds.slot[pc.sub]);
 }
 
 template <int S, int U>
@@ -847,25 +948,31 @@ constexpr int kF32S = 2, kF32U = 2;
 
 }  // namespace
 
-hipError_t launch_reduce(const Plan& p, int dtype, const void* k, const void* v, float* partials,
-                         float* state, unsigned long long* ctl, unsigned long long epoch,
-                         hipStream_t stream) {
-  const dim3 grid((unsigned)(p.units * p.red_chunks));
+hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, const void* v,
+                         float* partials, float* state, unsigned long long* ctl,
+                         unsigned long long epoch, hipStream_t stream) {
   const int64_t BH = p.B * p.H;
   if (dtype == 1) {
-    hipLaunchKernelGGL((reduce_bf16_kernel<kRedS, kRedU>), grid, dim3(64 * kRedS), 0, stream,
+    auto* kernel = fold ? reduce_bf16_kernel<kRedS, kRedU, true>
+                        : reduce_bf16_kernel<kRedS, kRedU, false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)p.red_blocks), dim3(64 * kRedS), 0, stream,
                        static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
-                       partials, state, ctl, epoch, p.N, p.H, p.pairs, p.units, p.red_chunk,
-                       p.red_chunks, BH);
+                       partials, state, ctl, epoch, p.N, p.H, p.pairs, p.tiles, p.red_q,
+                       p.units * p.tiles, p.slots);
   } else {
-    hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U>), grid, dim3(128 * kF32S), 0, stream,
-                       static_cast<const float*>(k), static_cast<const float*>(v), partials, state,
-                       ctl, epoch, p.N, p.H, p.pairs, p.units, p.red_chunk, p.red_chunks, BH);
+    if (!fold) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U>), dim3((unsigned)(p.units * p.red_chunks)),
+                       dim3(128 * kF32S), 0, stream, static_cast<const float*>(k),
+                       static_cast<const float*>(v), partials, state, ctl, epoch, p.N, p.H,
+                       p.pairs, p.units, p.red_chunk, p.red_chunks, BH);
   }
   return hipGetLastError();
 }
 
-int reduce_block_waves(int dtype) { return dtype == 1 ? kRedS : 2 * kF32S; }
+int block_waves(KernelKind kind, int dtype) {
+  if (dtype != 1) return 2 * kF32S;
+  return kind == KernelKind::kReduce ? kRedS : kAppS;
+}
 
 int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
   int n = 0;
@@ -873,7 +980,7 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
   switch (kind) {
     case KernelKind::kReduce:
       e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                           &n, reduce_bf16_kernel<kRedS, kRedU>, 64 * kRedS, 0)
+                           &n, reduce_bf16_kernel<kRedS, kRedU, false>, 64 * kRedS, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(
                            &n, reduce_f32_kernel<kF32S, kF32U>, 128 * kF32S, 0);
       break;
@@ -889,17 +996,26 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
 
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state, void* out,
                         float eps, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.units * p.app_chunks));
   if (dtype == 1) {
-    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), grid, dim3(64 * kAppS), 0, stream,
-                       static_cast<const unsigned short*>(q), state,
-                       static_cast<unsigned short*>(out), eps, p.N, p.H, p.pairs, p.units,
-                       p.app_chunk);
+    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), dim3((unsigned)(p.units * p.app_chunks)),
+                       dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), state,
+                       p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
+                       eps, p.N, p.H, p.pairs, p.tiles, p.app_chunks, p.app_chunk / kTile);
   } else {
-    hipLaunchKernelGGL((apply_f32_kernel<kF32S>), grid, dim3(128 * kF32S), 0, stream,
-                       static_cast<const float*>(q), state, static_cast<float*>(out), eps, p.N,
-                       p.H, p.pairs, p.units, p.app_chunk);
+    hipLaunchKernelGGL((apply_f32_kernel<kF32S>), dim3((unsigned)(p.units * p.app_chunks)),
+                       dim3(128 * kF32S), 0, stream, static_cast<const float*>(q), state,
+                       static_cast<float*>(out), eps, p.N, p.H, p.pairs, p.units, p.app_chunk);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
+                                 float eps, hipStream_t stream) {
+  const int64_t sp = p.slots * 2 * kSF;
+  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), dim3((unsigned)(p.units * p.app_chunks)),
+                     dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), partials,
+                     p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
+                     p.pairs, p.tiles, p.app_chunks, p.app_chunk / kTile);
   return hipGetLastError();
 }
 

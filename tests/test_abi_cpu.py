@@ -71,9 +71,13 @@ def test_workspace_size_rules(L):
     assert ws_size(L, 1, 16, 2, dt=7) == (UNSUPPORTED, 0)
     assert L.sana_linattn_workspace_size(1, 16, 2, 32, BF16, None) == INVALID
     # B*N*H*d*2 beyond 2^62 bytes, and int64 overflow of the product
-    assert ws_size(L, 1 << 20, 1 << 20, 1 << 16)[0] == INVALID   # exactly 2^62 bytes
-    assert ws_size(L, 1 << 20, 1 << 20, 1 << 15)[0] == OK        # 2^61 bytes is addressable
+    assert ws_size(L, 1, 1 << 40, 1 << 16)[0] == INVALID   # exactly 2^62 bytes
+    assert ws_size(L, 1, 1 << 40, 1 << 15)[0] == OK        # 2^61 bytes is addressable
     assert ws_size(L, 1 << 62, 1 << 62, 1)[0] == INVALID
+    # head pairs B*ceil(H/2) index one grid dimension: below 2^31
+    assert ws_size(L, 1 << 16, 1, (1 << 16) - 2)[0] == OK    # 2^31 - 2^16 pairs
+    assert ws_size(L, 1 << 16, 1, (1 << 16) + 1)[0] == INVALID
+    assert ws_size(L, 1 << 31, 1, 2)[0] == INVALID          # exactly 2^31 pairs
     # the state does not grow with n: constant once N is large
     sizes = {ws_size(L, 2, n, 70)[1] for n in (1 << 16, 1 << 18, 1 << 20, 1 << 24)}
     assert len(sizes) == 1

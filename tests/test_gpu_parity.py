@@ -18,6 +18,11 @@ pytestmark = pytest.mark.gpu
 VARIANTS = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}
 
 
+def variants(dtype):
+    """Variants that support dtype (all of them, for both dtypes)."""
+    return dict(VARIANTS)
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     t = torch()
@@ -52,7 +57,7 @@ def test_workload_matches_oracle_all_variants(name):
     print(f"\n[case] workload {name} shape {w.shape} {w.dtype}", flush=True)
     x, dev = _inputs(w)
     ref = _oracle(w, x)
-    for vname, var in VARIANTS.items():
+    for vname, var in variants(w.dtype).items():
         got = _run(w, dev, var)
         assert_close(got, ref, w.dtype, f"{name}/{vname}")
 
@@ -82,7 +87,7 @@ def test_ragged_shapes(B, N, H, dtype):
     print(f"\n[case] ragged B={B} N={N} H={H} {dtype}", flush=True)
     x, dev = _inputs(w)
     ref = _oracle(w, x)
-    for vname, var in VARIANTS.items():
+    for vname, var in variants(dtype).items():
         assert_close(_run(w, dev, var), ref, dtype, f"B={B} N={N} H={H} {dtype} {vname}")
 
 
@@ -171,7 +176,7 @@ def test_dead_key_tokens_do_not_matter_bitwise():
 def test_repeat_calls_are_bitwise_identical(name):
     w = W.WORKLOADS[name]
     x, dev = _inputs(w)
-    for vname, var in VARIANTS.items():
+    for vname, var in variants(w.dtype).items():
         a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), w.dtype)
         for _ in range(3):
             b = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), w.dtype)
@@ -227,6 +232,42 @@ def test_heads_given_as_flat_width():
     flat = {k: t.view(w.B, w.N, w.D) for k, t in dev.items()}
     b = to_host(R.forward(flat["q"], flat["k"], flat["v"], eps=w.eps, heads=w.H), "bf16")
     assert np.array_equal(a.reshape(-1), b.reshape(-1))
+
+
+def test_split_equals_kv_state_then_apply_bitwise():
+    """The bf16 split forward sums the reduction's partials inside the apply;
+    kv_state folds the same partials, in the same order, at the end of the
+    reduction. Both routes must give the same bits."""
+    for w in (W.WORKLOADS["latent_4096px"], W.custom("odd", 3, 5001, 7, seed=31)):
+        x, dev = _inputs(w)
+        a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=R.VARIANT_SPLIT),
+                    "bf16")
+        st = R.kv_state(dev["k"], dev["v"])
+        b = to_host(R.apply(dev["q"], st, eps=w.eps), "bf16")
+        assert np.array_equal(a, b), w.name
+
+
+def test_one_workspace_across_calls_and_shapes():
+    """One workspace serves forward and kv_state calls of different shapes in
+    turn: stale partials and control words from earlier calls never leak
+    into a later result (each call is equal to one on a fresh workspace)."""
+    t = torch()
+    wa = W.custom("sa", 2, 3000, 6, seed=21)
+    wb = W.custom("sb", 1, 5000, 5, seed=22)
+    xa, da = _inputs(wa)
+    xb, db = _inputs(wb)
+    size = max(R.workspace_size(2, 3000, 6), R.workspace_size(1, 5000, 5))
+    ws = t.full((size,), 0x7f, dtype=t.uint8, device="cuda")
+    ra = to_host(R.forward(da["q"], da["k"], da["v"], variant=R.VARIANT_SPLIT), "bf16")
+    rb = to_host(R.forward(db["q"], db["k"], db["v"], variant=R.VARIANT_SPLIT), "bf16")
+    sa = R.kv_state(da["k"], da["v"]).cpu().numpy()
+    for i in range(4):
+        oa = R.forward(da["q"], da["k"], da["v"], workspace=ws, variant=R.VARIANT_SPLIT)
+        gs = R.kv_state(da["k"], da["v"], workspace=ws)
+        ob = R.forward(db["q"], db["k"], db["v"], workspace=ws, variant=R.VARIANT_SPLIT)
+        assert np.array_equal(to_host(oa, "bf16"), ra), f"A call {i}"
+        assert np.array_equal(to_host(ob, "bf16"), rb), f"B call {i}"
+        assert np.array_equal(gs.cpu().numpy(), sa), f"state call {i}"
 
 
 def test_errors_enqueue_nothing():
