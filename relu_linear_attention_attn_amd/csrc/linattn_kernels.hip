@@ -220,27 +220,10 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
   }
 }
 
-// 32x32 accumulator layout: lane l, register r holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32. Rows are k channels c, columns
-// v channels j. ksum[c] is ks of lane c plus ks of lane c + 32 (the two
-// token halves of the gather), added here in that order.
-template <bool Coherent>
-__device__ __forceinline__ void store_state_from_mfma32(float* dst, const f32x16& acc, float ks) {
-  const int l = lane_id();
-  const int j = l & 31;
-  const int cb = 4 * (l >> 5);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int c = 8 * (r >> 2) + cb + (r & 3);
-    put<Coherent>(dst + c * kSC + j, acc[r]);
-  }
-  const float hi = __shfl_down(ks, 32);
-  if (l < 32) put<Coherent>(dst + l * kSC + kD, ks + hi);
-}
-
-// Chunk partials of a head pair are folded into the final state by the last
-// block to finish that pair, in ascending chunk order, so the result does not
-// depend on which block finishes last. The hand-off between blocks (which may
+// Where a launch must leave one folded state (the fp32 reduction, and the
+// bf16 one behind sana_linattn_kv_state), the partials of a head pair are
+// folded into it by the last block to finish that pair, in ascending chunk
+// order, so the result does not depend on which block finishes last. The hand-off between blocks (which may
 // sit on different XCDs, each with its own L2) avoids device-wide fences,
 // whose L2 write-back per block would cost more than the whole reduction:
 //   * partials are written with device-coherent stores (relaxed atomic
@@ -295,28 +278,6 @@ __device__ __forceinline__ void fold_partials(const float* __restrict__ src, int
         if (p0 + u < P) acc = (p0 + u == 0) ? x[u] : acc + x[u];
     }
     dst[e] = acc;
-  }
-}
-
-// Pairwise tree over the S waves of a block (R floats per lane): in the round
-// with stride s, wave w with w % 2s == s adds into wave w - s. After
-// ceil(log2 S) rounds wave 0 holds the sum, in an order fixed by S alone.
-// xchg holds ceil(S/2) * R * 64 floats. All threads of the block must call.
-template <int R>
-__device__ __forceinline__ void tree_fold(float (&regs)[R], float* xchg, int sub, int S) {
-  const int l = lane_id();
-  for (int s = 1; s < S; s *= 2) {
-    float* d = xchg + (sub / (2 * s)) * R * kWave;
-    if (sub % (2 * s) == s) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) d[r * kWave + l] = regs[r];
-    }
-    __syncthreads();
-    if (sub % (2 * s) == 0 && sub + s < S) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) regs[r] += d[r * kWave + l];
-    }
-    __syncthreads();
   }
 }
 
@@ -674,31 +635,69 @@ constexpr int kFoldFloats = 34;  // 32 accumulator registers + ksum of both head
 template <int S>
 union RedLds {
   unsigned char slot[S][2 * kTileBytes];
-  float xchg[((S + 1) / 2) * kFoldFloats * kWave];
+  float xchg[S][kFoldFloats][kWave];
 };
 
-// Sums the block's sub-stream sums into wave 0 (fixed tree order).
-template <int S>
-__device__ __forceinline__ void fold_pair_accumulators(f32x16 (&acc)[2], float (&ks)[2],
-                                                       RedLds<S>& lds, int sub) {
-  if (S == 1) return;
-  __syncthreads();  // every wave is done with its tile slot
-  float regs[kFoldFloats];
+// Block epilogue of the bf16 reduction: every wave writes its sums for the
+// head pair (acc in the 32x32 MFMA layout, ks per lane) to LDS; after one
+// barrier the whole block adds them in wave order and writes the pair's
+// [2][d][d+1] state to dst (only the first head when !two).
+// 32x32 accumulator layout: lane l, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32; rows are k channels c, columns
+// v channels j. ksum[c] is ks of lane c plus ks of lane c + 32 (the two
+// token halves of the gather), added in that order.
+// The KV part (2 x 32 x 32 values) is spread evenly over the block, each
+// thread issuing all its LDS reads before its first add; the 64 ksum values
+// go to the first 64 threads as one more batch. (A loop over the [d][d+1]
+// rows instead puts a ksum element in almost every wave, whose divergent
+// second path doubled the epilogue.)
+template <int S, bool Coherent>
+__device__ __forceinline__ void block_sum_state(const f32x16 (&acc)[2], const float (&ks)[2],
+                                                RedLds<S>& lds, int sub, float* dst, bool two) {
+  static_assert(2 * kD * kD % (kWave * S) == 0, "KV values split evenly over the block");
+  constexpr int kPer = 2 * kD * kD / (kWave * S);  // KV values per thread
+  const int l = lane_id();
+  __syncthreads();  // every wave is done with its tile slot (xchg overlays them)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    regs[r] = acc[0][r];
-    regs[16 + r] = acc[1][r];
+    lds.xchg[sub][r][l] = acc[0][r];
+    lds.xchg[sub][16 + r][l] = acc[1][r];
   }
-  regs[32] = ks[0];
-  regs[33] = ks[1];
-  tree_fold<kFoldFloats>(regs, lds.xchg, sub, S);
+  lds.xchg[sub][32][l] = ks[0];
+  lds.xchg[sub][33][l] = ks[1];
+  __syncthreads();
+  const int heads = two ? 2 : 1;
+  float x[kPer][S];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc[0][r] = regs[r];
-    acc[1][r] = regs[16 + r];
+  for (int i = 0; i < kPer; ++i) {
+    const int m = threadIdx.x + i * kWave * S;  // (head, c, j) = (m >> 10, (m >> 5) & 31, m & 31)
+    const int c = (m >> 5) & 31, j = m & 31;
+    const int r = 16 * (m >> 10) + 4 * (c >> 3) + (c & 3);
+    const int ln = j + 32 * ((c >> 2) & 1);
+#pragma unroll
+    for (int w = 0; w < S; ++w) x[i][w] = lds.xchg[w][r][ln];
   }
-  ks[0] = regs[32];
-  ks[1] = regs[33];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int m = threadIdx.x + i * kWave * S;
+    float sum = x[i][0];
+#pragma unroll
+    for (int w = 1; w < S; ++w) sum += x[i][w];
+    if ((m >> 10) < heads) put<Coherent>(dst + (m >> 10) * kSF + ((m >> 5) & 31) * kSC + (m & 31), sum);
+  }
+  if (threadIdx.x < 2 * kD) {
+    const int hh = threadIdx.x >> 5, c = threadIdx.x & 31;
+    float y[S][2];
+#pragma unroll
+    for (int w = 0; w < S; ++w) {
+      y[w][0] = lds.xchg[w][32 + hh][c];
+      y[w][1] = lds.xchg[w][32 + hh][c + 32];
+    }
+    float sum = y[0][0] + y[0][1];
+#pragma unroll
+    for (int w = 1; w < S; ++w) sum += y[w][0] + y[w][1];
+    if (hh < heads) put<Coherent>(dst + hh * kSF + c * kSC + kD, sum);
+  }
 }
 
 // Balanced ranges. The work of a bf16 kernel is the flattened index
@@ -759,13 +758,9 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
     reduce_pair_wave<U>(K, V, H * kD, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub], acc, ks);
-    fold_pair_accumulators<S>(acc, ks, lds, sub);
     const SlotRange sr = slot_range(unit, T, Qb);
     float* part = partials + ((unit * slots) + (g - sr.first)) * 2 * kSF;
-    if (sub == 0) {
-      store_state_from_mfma32<Fold>(part, acc[0], ks[0]);
-      if (sg.two) store_state_from_mfma32<Fold>(part + kSF, acc[1], ks[1]);
-    }
+    block_sum_state<S, Fold>(acc, ks, lds, sub, part, sg.two);
     if (Fold && arrive_last(ctl + unit, epoch, sr.count))
       fold_partials(partials + unit * slots * 2 * kSF, 2 * kSF, state + (sg.b * H + sg.h) * kSF,
                     (sg.two ? 2 : 1) * kSF, sr.count);
@@ -801,8 +796,15 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
   }
 }
 
-// Apply, one block per (unit, token chunk): block g takes chunk g % C (Qa
-// tiles) of unit g / C. The state of a unit is the sum of `count`
+// Apply, one block per (unit, token chunk of Qa tiles), C chunks per unit.
+// The hardware deals blocks to the XCDs round robin (block g to XCD g % X on
+// MI355X, X = 8), and each XCD has its own L2: block g takes item g / X of
+// XCD g % X's list, which holds units g % X, g % X + X, ... with their C
+// chunks in a row. A unit's chunk blocks then share one L2, which fetches the
+// unit's partials once instead of once per block. Blocks past the last unit
+// exit (the grid is X * ceil(units / X) * C). X = 1 keeps the plain order;
+// the mapping is a bijection either way, only locality depends on X.
+// The state of a unit is the sum of `count`
 // consecutive [2][d][d+1] slots at src + b * sb + p * sp (+ j * 2 * kSF),
 // count from slot_range(unit, T, Qr) when Qr > 0 (the partials of the
 // reduction, summed here in ascending slot order, as fold_partials does), else
@@ -812,13 +814,15 @@ template <int S, int U>
 __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     const unsigned short* __restrict__ Q, const float* __restrict__ src, int64_t sb, int64_t sp,
     int64_t Qr, unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
-    int64_t T, int64_t C, int64_t Qa) {
+    int64_t units, int64_t T, int64_t C, int64_t Qa, int64_t X) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
   __shared__ unsigned char slots[S][kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t unit = blockIdx.x / C;
-  const int64_t f_lo = unit * T + (blockIdx.x - unit * C) * Qa;
+  const int64_t x = blockIdx.x % X, k = blockIdx.x / X;
+  const int64_t unit = x + X * (k / C);
+  if (unit >= units) return;  // the whole block
+  const int64_t f_lo = unit * T + (k % C) * Qa;
   const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
   {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
@@ -832,21 +836,21 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
       constexpr int kBatch = 8;
       const int e0 = threadIdx.x < n4 ? threadIdx.x : n4 - 1;
       const int e1 = threadIdx.x + blockDim.x < n4 ? threadIdx.x + blockDim.x : n4 - 1;
-      f32x4 a0 = st[e0], a1 = st[e1];
-      for (int64_t j0 = 1; j0 < count; j0 += kBatch) {
+      f32x4 a0 = (f32x4)0, a1 = (f32x4)0;
+      for (int64_t j0 = 0; j0 < count; j0 += kBatch) {
         f32x4 x0[kBatch], x1[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const int64_t j = j0 + u < count ? j0 + u : count - 1;
+          const int64_t j = min(j0 + u, count - 1);
           x0[u] = st[j * (2 * kSF / 4) + e0];
           x1[u] = st[j * (2 * kSF / 4) + e1];
         }
+        // slot 0 starts the sum (no 0 + x), later slots add in order
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          if (j0 + u < count) {
-            a0 += x0[u];
-            a1 += x1[u];
-          }
+          const bool first = j0 + u == 0, take = j0 + u < count;
+          a0 = first ? x0[u] : (take ? a0 + x0[u] : a0);
+          a1 = first ? x1[u] : (take ? a1 + x1[u] : a1);
         }
       }
       if (threadIdx.x < n4) stage[threadIdx.x] = a0;
@@ -889,14 +893,10 @@ __global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
   f32x16 acc[2] = {(f32x16)0, (f32x16)0};
   float ks[2] = {0.0f, 0.0f};
   reduce_pair_wave<U>(K, V, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
-  fold_pair_accumulators<S>(acc, ks, lds, pc.sub);  // ends with a barrier: the
-                                                    // tile slots are free again
   auto make_ops = [&](ApplyOperands (&op)[2]) {
-    if (pc.sub == 0) {
-      store_state_from_mfma32<false>(st[0], acc[0], ks[0]);
-      store_state_from_mfma32<false>(st[1], acc[1], ks[1]);
-    }
-    __syncthreads();
+    // both heads, also for a one-head pair (its second head is never stored)
+    block_sum_state<S, false>(acc, ks, lds, pc.sub, &st[0][0], true);
+    __syncthreads();  // the state is complete; xchg is free for the tile slots
     op[0] = make_apply_operands(st[0]);
     op[1] = make_apply_operands(st[1]);
   };
@@ -944,6 +944,10 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
 constexpr int kRedS = SANA_RED_S, kRedU = SANA_RED_U;
 constexpr int kAppS = SANA_APP_S, kAppU = SANA_APP_U;
 constexpr int kFusS = 8, kFusU = 2;
+// XCDs of MI355X (the round-robin width of block dispatch). Fewer units than
+// that: plain order (grouping would leave most blocks empty).
+constexpr int64_t kXcds = 8;
+int64_t apply_xcds(const Plan& p) { return p.units >= kXcds ? kXcds : 1; }
 constexpr int kF32S = 2, kF32U = 2;
 
 }  // namespace
@@ -997,10 +1001,13 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state, void* out,
                         float eps, hipStream_t stream) {
   if (dtype == 1) {
-    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), dim3((unsigned)(p.units * p.app_chunks)),
+    const int64_t X = apply_xcds(p);
+    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>),
+                       dim3((unsigned)(X * ((p.units + X - 1) / X) * p.app_chunks)),
                        dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), state,
                        p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
-                       eps, p.N, p.H, p.pairs, p.tiles, p.app_chunks, p.app_chunk / kTile);
+                       eps, p.N, p.H, p.pairs, p.units, p.tiles, p.app_chunks,
+                       p.app_chunk / kTile, X);
   } else {
     hipLaunchKernelGGL((apply_f32_kernel<kF32S>), dim3((unsigned)(p.units * p.app_chunks)),
                        dim3(128 * kF32S), 0, stream, static_cast<const float*>(q), state,
@@ -1012,10 +1019,12 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
 hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
                                  float eps, hipStream_t stream) {
   const int64_t sp = p.slots * 2 * kSF;
-  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>), dim3((unsigned)(p.units * p.app_chunks)),
+  const int64_t X = apply_xcds(p);
+  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>),
+                     dim3((unsigned)(X * ((p.units + X - 1) / X) * p.app_chunks)),
                      dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), partials,
                      p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
-                     p.pairs, p.tiles, p.app_chunks, p.app_chunk / kTile);
+                     p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
   return hipGetLastError();
 }
 
