@@ -126,6 +126,34 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, workload: 
             "kernels": kernels}
 
 
+def copy_ceiling(device, mib: int = 1024, reps: int = 10):
+    """An achievable-bandwidth reference beside the 8 TB/s peak: the faster of
+    two plain device copies of `mib` MiB (torch's copy_ and an element-wise
+    bitwise_not kernel), read + write bytes over the median event time."""
+    import statistics
+
+    import torch
+
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    best = {}
+    for name, fn in (("copy_", lambda: dst.copy_(src)),
+                     ("bitwise_not", lambda: torch.bitwise_not(src, out=dst))):
+        fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        best[name] = 2 * (mib << 20) / (statistics.median(times) * 1e-3) / 1e9
+    del src, dst
+    name = max(best, key=best.get)
+    return {"gbps": best[name], "kernel": name, "mib": mib, "all_gbps": best}
+
+
 def cpu_baseline(w, inputs, budget_s: float):
     """Time the CPU oracle on whole heads of the workload until the budget is
     spent; report token-heads/s converted to tokens/s (all H heads of a
@@ -252,6 +280,7 @@ def main():
     torch.cuda.synchronize()
     ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
 
+    step_ms = sorted(ev[0].elapsed_time(ev[nk]) for ev in events)
     names = ["fused"] if nk == 1 else ["reduce", "apply"]
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
@@ -283,11 +312,17 @@ def main():
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "kernel_ms": per_kernel,
         "ms_per_step_with_kernel_events": ms_events,
+        "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic},
     }
-    if args.copy_mib > 0:  # counter calibration, outside every timed region
+    if args.copy_mib == 0:
+        # achievable-bandwidth reference, outside every timed region (not in
+        # counter runs, whose calibration keys on the one bitwise_not below)
+        ceil = copy_ceiling(dev["q"].device)
+        result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
+    else:  # counter calibration, outside every timed region
         # a plain streaming kernel that reads and writes exactly copy_mib MiB
         src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
         dst = torch.empty_like(src)
