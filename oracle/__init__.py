@@ -12,3 +12,9 @@ from .linattn import (  # noqa: F401
     state_from_inputs,
     to_f64,
 )
+from .linattn_bwd import (  # noqa: F401,E402
+    backward_head,
+    linattn_bwd_fp64,
+    linattn_bwd_from_inputs,
+    state_grad_head,
+)

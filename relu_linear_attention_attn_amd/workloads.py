@@ -19,7 +19,8 @@ Layout of every tensor: ``[B][N][H][d]`` row-major, i.e. a token row of
 Recipe (all draws in float64, then rounded to float32, then - for bf16
 workloads - rounded to bfloat16 with round-to-nearest-even):
   * token rows ``r = b*N + n`` are cut into chunks of ``CHUNK_ROWS`` rows;
-    chunk ``c`` of tensor ``t`` (q=0, k=1, v=2) draws from
+    chunk ``c`` of tensor ``t`` (q=0, k=1, v=2; g=4, the upstream gradient
+    dL/dout that the backward pass takes, N(0, 1) unless stated) draws from
     ``PCG64(SeedSequence([seed, t, c]))``, so generation is chunk-parallel and
     the result does not depend on the number of worker threads;
   * ``normal(mu, sigma)``: ``mu + sigma * standard_normal``;
@@ -40,7 +41,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 CHUNK_ROWS = 8192
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "g": 4}
 MASK_STREAM = 3
 
 
@@ -71,6 +72,7 @@ class Workload:
     v: Dist
     mask_tensor: Optional[str] = None  # which tensor gets all-negative rows
     mask_frac: float = 0.0
+    g: Dist = Dist("normal", 0.0, 1.0)  # upstream gradient (backward pass only)
 
     @property
     def D(self) -> int:
@@ -163,7 +165,8 @@ def _workers() -> int:
 
 def generate_tensor(w: Workload, which: str, rows: Optional[Tuple[int, int]] = None,
                     workers: Optional[int] = None) -> np.ndarray:
-    """Draw tensor ``which`` ('q', 'k' or 'v') of workload ``w``.
+    """Draw tensor ``which`` ('q', 'k', 'v', or 'g' for the backward's
+    upstream gradient) of workload ``w``.
 
     Returns uint16 bf16 bits or float32 values, shaped ``[rows, H, d]`` over
     the flattened token rows ``r = b*N + n`` in ``rows = (r0, r1)`` (default:
@@ -220,9 +223,11 @@ def masked_rows(w: Workload) -> np.ndarray:
     return np.sort(rng.choice(w.B * w.N, size=w.n_masked, replace=False)).astype(np.int64)
 
 
-def generate(w: Workload, workers: Optional[int] = None) -> Dict[str, np.ndarray]:
-    """All three input tensors of ``w`` as ``{'q','k','v'}`` -> [B, N, H, d]."""
-    return {t: generate_tensor(w, t, workers=workers) for t in ("q", "k", "v")}
+def generate(w: Workload, workers: Optional[int] = None, grad: bool = False) -> Dict[str, np.ndarray]:
+    """The input tensors of ``w`` as ``{'q','k','v'}`` (plus ``'g'`` with
+    ``grad``) -> [B, N, H, d]."""
+    names = ("q", "k", "v", "g") if grad else ("q", "k", "v")
+    return {t: generate_tensor(w, t, workers=workers) for t in names}
 
 
 def custom(name: str, B: int, N: int, H: int, dtype: str = "bf16", seed: int = 11,

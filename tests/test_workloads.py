@@ -82,3 +82,18 @@ def test_distributions_have_the_stated_moments():
     # t(4): variance nu/(nu-2) = 2; P(|t| > 2.776) = 0.05 (two-sided 95% point)
     assert abs(np.mean(np.abs(k) > 2.776445) - 0.05) < 0.002
     assert abs(np.median(k)) < 0.01
+
+
+def test_upstream_gradient_stream():
+    """g (the backward's dL/dout) has its own seeded stream: chunk-parallel
+    generation matches serial, it differs from q, k and v, and it is
+    N(0, 1)."""
+    w = W.custom("gstream", 2, 9000, 3, dtype="f32", seed=21)
+    a = W.generate_tensor(w, "g", workers=1)
+    b = W.generate_tensor(w, "g", workers=4)
+    assert np.array_equal(a, b)
+    for t in ("q", "k", "v"):
+        assert not np.array_equal(a, W.generate_tensor(w, t, workers=1))
+    assert abs(float(a.mean())) < 0.01 and abs(float(a.std()) - 1.0) < 0.01
+    x = W.generate(w, grad=True)
+    assert set(x) == {"q", "k", "v", "g"} and np.array_equal(x["g"], a)
