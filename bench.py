@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
-"""Throughput of the ReLU linear self-attention forward pass on one MI355X.
+"""Throughput of ReLU linear self-attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op fwd|bwd]
 
-A step is one full forward pass (the state reduction over token chunks with
-its fixed-order fold of chunk partials, then the apply) over one batch of
-synthetic input already resident in HBM. Prints one JSON line: tokens/s (B*N per step), the whole
+A step is one full forward pass (the state reduction over token ranges into
+per-block partials, then the apply, which sums them) - or, with --op bwd, one
+full backward pass (the state reduction, the q pass that also reduces the
+state gradient, the k/v pass) - over one batch of synthetic input already
+resident in HBM. Prints one JSON line: tokens/s (B*N per step), the whole
 path's achieved HBM GB/s, a roofline record for the dominant kernel (its
-duration from HIP events recorded on the launch stream inside the timed
+duration from HIP events recorded on the launch stream in a second timed
 region) and the CPU float64 oracle timed on a bounded sample of the same
 workload.
 """
@@ -25,8 +27,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E spec peak
 METRIC = "linear-attn fwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
+METRIC_BWD = "linear-attn bwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
 CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_latent_4096px.json")
+TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "traffic_latent_4096px.json"),
+                 "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json")}
 
 
 def parse():
@@ -36,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd"],
+                    help="forward pass (the headline) or backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--quiet", action="store_true")
@@ -64,11 +70,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, op: str = "fwd"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when absent or taken on a different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[op]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -91,7 +97,8 @@ def _counter_rows(folder: str):
 
 def _kernel_key(name: str) -> str:
     for k, v in (("reduce_bf16_kernel", "reduce"), ("apply_bf16_kernel", "apply"),
-                 ("fused_bf16_kernel", "fused"), ("bitwise_not", "copy")):
+                 ("fused_bf16_kernel", "fused"), ("bwd_q_bf16_kernel", "bwd_q"),
+                 ("bwd_kv_bf16_kernel", "bwd_kv"), ("bitwise_not", "copy")):
         if k in name:
             return v
     return ""
@@ -154,6 +161,16 @@ def copy_ceiling(device, mib: int = 1024, reps: int = 10):
     return {"gbps": best[name], "kernel": name, "mib": mib, "all_gbps": best}
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([p.get("num_threads", 1) for p in threadpool_info()
+                    if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        return 1
+
+
 def cpu_baseline(w, inputs, budget_s: float):
     """Time the CPU oracle on whole heads of the workload until the budget is
     spent; report token-heads/s converted to tokens/s (all H heads of a
@@ -161,12 +178,7 @@ def cpu_baseline(w, inputs, budget_s: float):
     import numpy as np
     import oracle.linattn as L
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
+    threads = _blas_threads()
     # whole passes over the workload's (b, h) heads until the budget is spent
     done = 0
     passes = 0
@@ -206,12 +218,140 @@ def cpu_baseline(w, inputs, budget_s: float):
     }
 
 
+def cpu_baseline_bwd(w, inputs, budget_s: float):
+    """The backward oracle on whole heads of the workload until the budget is
+    spent; token-heads/s converted to tokens/s (all H heads of a token)."""
+    import oracle.linattn as L
+    import oracle.linattn_bwd as LB
+
+    threads = _blas_threads()
+    done, passes, decode_s = 0, 0, 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for b in range(w.B):
+            for h in range(w.H):
+                ta = time.perf_counter()
+                q, k, v, g = (L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkvg")
+                decode_s += time.perf_counter() - ta
+                LB.backward_head(q, k, v, g, w.eps)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        passes += 1
+    wall = time.perf_counter() - t0
+    return {
+        "value": done * w.N / wall / w.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} (b, h) head backward passes ({w.B * w.H} heads per full pass, "
+                  f"{passes} pass(es)) x all {w.N} tokens of {w.name}, float64 NumPy "
+                  f"({wall:.1f} s wall incl. {decode_s:.1f} s bf16 decode); tokens/s = "
+                  f"token-heads/s / H",
+        "seconds": wall,
+    }
+
+
+def run_bwd(args, w):
+    """The backward pass: one JSON line like the forward's (see main)."""
+    import numpy as np
+    import torch
+
+    import relu_linear_attention_attn_amd as R
+    from relu_linear_attention_attn_amd import workloads as W
+
+    if w.dtype != "bf16":
+        raise SystemExit("the backward pass is bf16 only")
+    log(args, f"workload {w.name} {w.shape} bf16 backward: generating inputs")
+    x = W.generate(w, grad=True)
+    dev = {t: torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).cuda() for t in "qkvg"}
+    grads = tuple(torch.empty_like(dev["q"]) for _ in range(3))
+    ws = torch.empty(R.bwd_workspace_size(w.B, w.N, w.H), dtype=torch.uint8, device="cuda")
+
+    def step(events=None):
+        R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps, grads=grads,
+                   workspace=ws, events=events)
+
+    names = ["reduce", "bwd_q", "bwd_kv"]
+    log(args, f"warmup {args.warmup} steps ({len(names)} kernels per step)")
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    log(args, f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(args, f"timing {args.steps} steps with per-kernel events")
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
+    per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+                  for j, n in enumerate(names)}
+    step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
+    elem = w.B * w.N * w.H * w.d * w.itemsize
+    alg_bytes = {"reduce": 2 * elem, "bwd_q": 3 * elem, "bwd_kv": 4 * elem}
+    total_bytes = sum(alg_bytes.values())
+    dominant = max(per_kernel, key=per_kernel.get)
+    achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-3) / 1e9
+    path_gbps = total_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC_BWD,
+        "value": w.B * w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "bwd", "B": w.B, "N": w.N, "H": w.H, "d": w.d,
+                   "D": w.D, "eps": w.eps},
+        "achieved_hbm_gbps": path_gbps,
+        "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": total_bytes,
+        "kernel_ms": per_kernel,
+        "ms_per_step_with_kernel_events": ms_events,
+        "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(dominant, w.name, "bwd")},
+    }
+    if args.copy_mib == 0:
+        ceil = copy_ceiling(dev["q"].device)
+        result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
+    else:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+    if args.cpu_seconds > 0:
+        log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_bwd(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         from relu_linear_attention_attn_amd import workloads as W
         rec = summarize_counters(*args.summarize_counters, args.copy_mib or 256,
                                  args.workload or W.HEADLINE)
+        rec["op"] = args.op
         print(json.dumps(rec, indent=1))
         return
     if args.gpus != 1:
@@ -229,6 +369,10 @@ def main():
     rank = int(os.environ.get("RANK", "0"))
     wname = args.workload or W.HEADLINE
     w = W.WORKLOADS[wname]
+    if args.op == "bwd":
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        R.lib()
+        return run_bwd(args, w)
     variant = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}[args.variant]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.lib()

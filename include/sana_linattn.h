@@ -170,6 +170,50 @@ sana_status_t sana_linattn_apply(const void* q, const float* state, void* out,
 sana_status_t sana_linattn_state_size(int64_t B, int64_t H, int64_t d, size_t* bytes);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
+/*
+ * Backward pass (bf16 only). Given g = dL/dout for the forward pass with the
+ * same q, k, v and eps, writes dq = dL/dq, dk = dL/dk, dv = dL/dv, per (b, h):
+ *
+ *     dnum_i = g_i / den_i,   dden_i = -(g_i . out_i) / den_i
+ *     dq_i   = (KV dnum_i + ksum dden_i) * [q_i > 0]
+ *     dKV    = sum_i phi(q_i)^T dnum_i,    dksum = sum_i phi(q_i) dden_i
+ *     dk_n   = (dKV v_n + dksum) * [k_n > 0],   dv_n = phi(k_n) dKV
+ *
+ * (with den_i = phi(q_i) . ksum + eps). These are the chain rule through the
+ * forward definition; the Sana paper review, section 2.2 "Triton을 통한
+ * 학습/추론 가속화", fuses this attention for training, which needs them, but
+ * no page writes them out. The derivative of phi at exactly 0 is taken as 0.
+ * The forward state is recomputed from k and v (one extra read of both).
+ *
+ * q, k, v, dout (read) and dq, dk, dv (written): dense [B][N][H][d] bf16,
+ * 16-byte aligned; fp32 accumulation, round-to-nearest-even on the stores.
+ * An output may not overlap another output, an input or the workspace
+ * (SANA_ERR_INVALID_ARG); inputs may alias each other. workspace: at least
+ * sana_linattn_bwd_workspace_size(...) bytes, 256-byte aligned, contents
+ * irrelevant on entry and undefined on return. SANA_DTYPE_F32 returns
+ * SANA_ERR_UNSUPPORTED. With eps = 0, rows whose phi(q_i) is 0 give NaN
+ * gradients, as the forward gives NaN outputs there. All checks run before
+ * any HIP call; three kernels are enqueued on `stream`.
+ */
+sana_status_t sana_linattn_bwd_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
+                                              int dtype, size_t* bytes);
+sana_status_t sana_linattn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                               void* dq, void* dk, void* dv, int64_t B, int64_t N, int64_t H,
+                               int64_t d, float eps, int dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sana_linattn_bwd that records events[0] before its first kernel and
+ * events[i] after kernel i (i = 1..3: the state reduction, the q pass that
+ * also reduces dKV and dksum, the k/v pass); n_events must be >= 4 and the
+ * events created by the caller. Computes exactly what sana_linattn_bwd does.
+ */
+sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void* v,
+                                        const void* dout, void* dq, void* dk, void* dv,
+                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                        int dtype, void* workspace, size_t workspace_bytes,
+                                        hipEvent_t* events, int n_events, hipStream_t stream);
+
 const char* sana_linattn_strerror(int status);
 
 /* SANA_LINATTN_VERSION of the built library. */

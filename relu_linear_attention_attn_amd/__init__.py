@@ -1,4 +1,4 @@
-"""ReLU linear self-attention forward (Sana Linear DiT) for AMD MI355X.
+"""ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward and backward.
 
 The compute runs in hand-written HIP kernels behind a C ABI
 (``libsana_linattn.so``, declared in ``include/sana_linattn.h``); this package
@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     VARIANT_SPLIT,
     SanaError,
     apply,
+    backward,
+    bwd_workspace_size,
     forward,
     forward_profiled,
     kv_state,

@@ -38,6 +38,9 @@ EXPORTS = (
     "sana_linattn_kv_state",
     "sana_linattn_apply",
     "sana_linattn_state_size",
+    "sana_linattn_bwd_workspace_size",
+    "sana_linattn_bwd",
+    "sana_linattn_bwd_profiled",
     "sana_linattn_strerror",
     "sana_linattn_version",
 )
@@ -84,10 +87,17 @@ def lib() -> ctypes.CDLL:
                                             _vp, _sz, _vp]
         L.sana_linattn_apply.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
                                          ctypes.c_int, _vp]
+        L.sana_linattn_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
+                                                      ctypes.POINTER(_sz)]
+        L.sana_linattn_bwd.argtypes = [_vp] * 7 + [_i64] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                _vp, _sz, _vp]
+        L.sana_linattn_bwd_profiled.argtypes = [_vp] * 7 + [_i64] * 4 + [
+            ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
                      "sana_linattn_fwd", "sana_linattn_fwd_variant", "sana_linattn_fwd_profiled",
-                     "sana_linattn_kv_state",
-                     "sana_linattn_apply"):
+                     "sana_linattn_kv_state", "sana_linattn_apply",
+                     "sana_linattn_bwd_workspace_size", "sana_linattn_bwd",
+                     "sana_linattn_bwd_profiled"):
             getattr(L, name).restype = ctypes.c_int
         L.sana_linattn_strerror.argtypes = [ctypes.c_int]
         L.sana_linattn_strerror.restype = ctypes.c_char_p
@@ -270,3 +280,48 @@ def apply(q, state, eps: float = 1e-6, heads: Optional[int] = None, out=None):
                                     float(eps), dt, _stream(q)),
            "sana_linattn_apply")
     return out
+
+
+def bwd_workspace_size(B: int, N: int, H: int, d: int = HEAD_DIM, dtype: int = DTYPE_BF16) -> int:
+    n = _sz(0)
+    _check(lib().sana_linattn_bwd_workspace_size(B, N, H, d, dtype, ctypes.byref(n)),
+           "sana_linattn_bwd_workspace_size")
+    return n.value
+
+
+def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grads=None,
+             workspace=None, events=None):
+    """(dq, dk, dv) of the forward pass for the upstream gradient dout (bf16).
+
+    q, k, v, dout: contiguous bf16 GPU tensors of one shape. grads: optional
+    preallocated (dq, dk, dv). events: optional list of 4 torch.cuda.Event
+    (enable_timing=True) recorded before the first and after each of the
+    three kernels. Enqueued on torch's current stream; no synchronisation."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(t, name, q)
+    dt = _dtype_code(q)
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    else:
+        for name, t in zip(("dq", "dk", "dv"), grads):
+            _check_tensor(t, name, q)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_size(B, N, H, d, dt), 1), dtype=torch.uint8,
+                                device=q.device)
+    wb = workspace.numel() * workspace.element_size()
+    ptrs = [t.data_ptr() for t in (q, k, v, dout, *grads)]
+    if events is None:
+        _check(lib().sana_linattn_bwd(*ptrs, B, N, H, d, float(eps), dt, workspace.data_ptr(),
+                                      wb, _stream(q)), "sana_linattn_bwd")
+    else:
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event on first record
+                e.record()
+        arr = (_vp * len(events))(*[e.cuda_event for e in events])
+        _check(lib().sana_linattn_bwd_profiled(*ptrs, B, N, H, d, float(eps), dt,
+                                               workspace.data_ptr(), wb, arr, len(events),
+                                               _stream(q)), "sana_linattn_bwd_profiled")
+    return grads

@@ -120,6 +120,7 @@ namespace {
 struct DeviceCaps {
   int cus = 0;
   int occ[2][2] = {{1, 1}, {1, 1}};  // [kernel: reduce, apply][dtype]
+  int occ_bwd_kv = 1;                // backward k/v pass (bf16)
 };
 
 const DeviceCaps& device_caps() {
@@ -137,6 +138,7 @@ const DeviceCaps& device_caps() {
       c.occ[0][dt] = occupancy_blocks_per_cu(KernelKind::kReduce, dt);
       c.occ[1][dt] = occupancy_blocks_per_cu(KernelKind::kApply, dt);
     }
+    c.occ_bwd_kv = occupancy_blocks_per_cu(KernelKind::kBwdKV, 1);
     caps[dev] = c;
   });
   return caps[dev];
@@ -179,6 +181,14 @@ void fit_plan_to_device(Plan& p, int dtype) {
 #endif
   p.app_chunk = chunk_tokens(p.N, ac);
   p.app_chunks = cdiv(p.N, p.app_chunk);
+  // backward k/v pass: the apply's rule with its own occupancy
+  const int64_t bcap = static_cast<int64_t>(c.cus) * c.occ_bwd_kv;
+  int64_t bc = clamp64(bcap / p.units, 1, std::max<int64_t>(1, cdiv(p.N, kMinApplyChunk)));
+#ifdef SANA_TUNING
+  if (const char* e = getenv("SANA_BKV_CHUNKS")) bc = std::max<int64_t>(1, atoll(e));
+#endif
+  p.bkv_chunk = chunk_tokens(p.N, bc);
+  p.bkv_chunks = cdiv(p.N, p.bkv_chunk);
 #ifdef SANA_TUNING
   if (getenv("SANA_PRINT_PLAN"))
     fprintf(stderr, "plan cus %d occ red %d app %d | red blocks %lld q %lld | app chunks %lld chunk %lld\n",
@@ -197,6 +207,11 @@ sana_status_t check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
 }
 
 sana_status_t to_status(hipError_t e) { return e == hipSuccess ? SANA_OK : SANA_ERR_HIP; }
+
+constexpr int kBwdKernels = 3;
+
+// Backward workspace: the forward reduction's partials, then bwd_q's.
+size_t bwd_workspace_bytes(const Plan& p) { return 2 * p.partial_bytes; }
 
 bool valid_variant(int variant) {
   return variant == SANA_VARIANT_AUTO || variant == SANA_VARIANT_SPLIT ||
@@ -318,6 +333,63 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   return mark(2) ? SANA_OK : SANA_ERR_HIP;
 }
 
+// The backward pass (bf16): the forward state reduction (partials only),
+// bwd_q (dq and the [dS | dz] partials), bwd_kv (dk, dv). events (may be
+// NULL) are recorded before the first kernel and after each of the three.
+sana_status_t backward(const void* q, const void* k, const void* v, const void* g, void* dq,
+                       void* dk, void* dv, int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                       int dtype, void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                       int n_events, hipStream_t stream) {
+  size_t tb = 0;
+  sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
+  if (s != SANA_OK) return s;
+  if (dtype != SANA_DTYPE_BF16) return SANA_ERR_UNSUPPORTED;
+  if (events) {
+    if (n_events < kBwdKernels + 1) return SANA_ERR_INVALID_ARG;
+    for (int i = 0; i <= kBwdKernels; ++i)
+      if (!events[i]) return SANA_ERR_INVALID_ARG;
+  }
+  const void* in[] = {q, k, v, g};
+  void* outs[] = {dq, dk, dv};
+  for (const void* p : in)
+    if (!p) return SANA_ERR_INVALID_ARG;
+  for (const void* p : outs)
+    if (!p) return SANA_ERR_INVALID_ARG;
+  if ((s = check_eps(eps)) != SANA_OK) return s;
+  for (const void* p : in)
+    if (misaligned(p)) return SANA_ERR_ALIGNMENT;
+  for (const void* p : outs)
+    if (misaligned(p)) return SANA_ERR_ALIGNMENT;
+  const Plan p = make_plan(B, N, H);
+  const size_t wb = bwd_workspace_bytes(p);
+  if (!workspace || workspace_bytes < wb) return SANA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
+  // an output may overlap nothing else (inputs may alias each other)
+  for (int i = 0; i < 3; ++i) {
+    for (const void* x : in)
+      if (overlaps(outs[i], tb, x, tb)) return SANA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], tb, outs[j], tb)) return SANA_ERR_INVALID_ARG;
+    if (overlaps(outs[i], tb, workspace, wb)) return SANA_ERR_INVALID_ARG;
+  }
+
+  (void)hipGetLastError();
+  Plan fp = p;
+  fit_plan_to_device(fp, dtype);
+  auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+  float* fwd_parts = static_cast<float*>(workspace);
+  float* grad_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.partial_bytes);
+  if (!mark(0)) return SANA_ERR_HIP;
+  if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  if (!mark(1)) return SANA_ERR_HIP;
+  if (launch_bwd_q(fp, q, g, dq, fwd_parts, grad_parts, eps, stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  if (!mark(2)) return SANA_ERR_HIP;
+  if (launch_bwd_kv(fp, k, v, dk, dv, grad_parts, stream) != hipSuccess) return SANA_ERR_HIP;
+  return mark(3) ? SANA_OK : SANA_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace sana
 
@@ -396,6 +468,35 @@ sana_status_t sana_linattn_apply(const void* q, const float* state, void* out, i
   (void)hipGetLastError();
   sana::fit_plan_to_device(p, dtype);
   return sana::to_status(sana::launch_apply(p, dtype, q, state, out, eps, stream));
+}
+
+sana_status_t sana_linattn_bwd_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
+                                              int dtype, size_t* bytes) {
+  if (!bytes) return SANA_ERR_INVALID_ARG;
+  *bytes = 0;
+  const sana_status_t s = sana::check_shape(B, N, H, d, dtype, nullptr);
+  if (s != SANA_OK) return s;
+  if (dtype != SANA_DTYPE_BF16) return SANA_ERR_UNSUPPORTED;
+  *bytes = sana::bwd_workspace_bytes(sana::make_plan(B, N, H));
+  return SANA_OK;
+}
+
+sana_status_t sana_linattn_bwd(const void* q, const void* k, const void* v, const void* dout,
+                               void* dq, void* dk, void* dv, int64_t B, int64_t N, int64_t H,
+                               int64_t d, float eps, int dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
+                        workspace_bytes, nullptr, 0, stream);
+}
+
+sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void* v,
+                                        const void* dout, void* dq, void* dk, void* dv,
+                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                        int dtype, void* workspace, size_t workspace_bytes,
+                                        hipEvent_t* events, int n_events, hipStream_t stream) {
+  if (!events) return SANA_ERR_INVALID_ARG;
+  return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
+                        workspace_bytes, events, n_events, stream);
 }
 
 const char* sana_linattn_strerror(int status) {

@@ -35,6 +35,8 @@ struct Plan {
   int64_t red_chunks_max; // chunks the workspace is sized for
   int64_t app_chunk;      // tokens per apply chunk (multiple of kTile)
   int64_t app_chunks;
+  int64_t bkv_chunk;      // backward k/v pass (bf16): tokens per chunk, chunks per unit
+  int64_t bkv_chunks;
   size_t partial_bytes;   // workspace bytes for partials
   size_t state_bytes;     // workspace bytes for the combined state
   size_t ctl_bytes;       // workspace bytes for the per-unit control words
@@ -46,7 +48,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H);
 // Fills the chunk counts for the current device (makes HIP queries once per device).
 void fit_plan_to_device(Plan& p, int dtype);
 
-enum class KernelKind { kReduce, kApply };
+enum class KernelKind { kReduce, kApply, kBwdQ, kBwdKV };
 int occupancy_blocks_per_cu(KernelKind kind, int dtype);
 int block_waves(KernelKind kind, int dtype);  // waves per block
 
@@ -64,6 +66,13 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
 // bf16 apply from the partials of launch_reduce(fold = false) with the same plan.
 hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
                                  float eps, hipStream_t stream);
+// Backward (bf16). bwd_q runs on the reduction's grid: it sums the partials of
+// launch_reduce(fold = false) for the state, writes dq and writes [dS | dz]
+// partials on the same slots; bwd_kv sums those and writes dk and dv.
+hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
+                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream);
+hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
+                         const float* grad_parts, hipStream_t stream);
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k,
                         const void* v, void* out, float eps, hipStream_t stream);
 

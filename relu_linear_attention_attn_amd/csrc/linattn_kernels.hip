@@ -653,18 +653,19 @@ union RedLds {
 // second path doubled the epilogue.)
 template <int S, bool Coherent>
 __device__ __forceinline__ void block_sum_state(const f32x16 (&acc)[2], const float (&ks)[2],
-                                                RedLds<S>& lds, int sub, float* dst, bool two) {
+                                                float (&xchg)[S][kFoldFloats][kWave], int sub,
+                                                float* dst, bool two) {
   static_assert(2 * kD * kD % (kWave * S) == 0, "KV values split evenly over the block");
   constexpr int kPer = 2 * kD * kD / (kWave * S);  // KV values per thread
   const int l = lane_id();
   __syncthreads();  // every wave is done with its tile slot (xchg overlays them)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    lds.xchg[sub][r][l] = acc[0][r];
-    lds.xchg[sub][16 + r][l] = acc[1][r];
+    xchg[sub][r][l] = acc[0][r];
+    xchg[sub][16 + r][l] = acc[1][r];
   }
-  lds.xchg[sub][32][l] = ks[0];
-  lds.xchg[sub][33][l] = ks[1];
+  xchg[sub][32][l] = ks[0];
+  xchg[sub][33][l] = ks[1];
   __syncthreads();
   const int heads = two ? 2 : 1;
   float x[kPer][S];
@@ -675,7 +676,7 @@ __device__ __forceinline__ void block_sum_state(const f32x16 (&acc)[2], const fl
     const int r = 16 * (m >> 10) + 4 * (c >> 3) + (c & 3);
     const int ln = j + 32 * ((c >> 2) & 1);
 #pragma unroll
-    for (int w = 0; w < S; ++w) x[i][w] = lds.xchg[w][r][ln];
+    for (int w = 0; w < S; ++w) x[i][w] = xchg[w][r][ln];
   }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -690,8 +691,8 @@ __device__ __forceinline__ void block_sum_state(const f32x16 (&acc)[2], const fl
     float y[S][2];
 #pragma unroll
     for (int w = 0; w < S; ++w) {
-      y[w][0] = lds.xchg[w][32 + hh][c];
-      y[w][1] = lds.xchg[w][32 + hh][c + 32];
+      y[w][0] = xchg[w][32 + hh][c];
+      y[w][1] = xchg[w][32 + hh][c + 32];
     }
     float sum = y[0][0] + y[0][1];
 #pragma unroll
@@ -760,7 +761,7 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     reduce_pair_wave<U>(K, V, H * kD, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub], acc, ks);
     const SlotRange sr = slot_range(unit, T, Qb);
     float* part = partials + ((unit * slots) + (g - sr.first)) * 2 * kSF;
-    block_sum_state<S, Fold>(acc, ks, lds, sub, part, sg.two);
+    block_sum_state<S, Fold>(acc, ks, lds.xchg, sub, part, sg.two);
     if (Fold && arrive_last(ctl + unit, epoch, sr.count))
       fold_partials(partials + unit * slots * 2 * kSF, 2 * kSF, state + (sg.b * H + sg.h) * kSF,
                     (sg.two ? 2 : 1) * kSF, sr.count);
@@ -794,6 +795,39 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
     fold_partials(partials + bh0 * kSF, BH * kSF, state + bh0 * kSF,
                   (H - 2 * (unit % pairs) < 2 ? 1 : 2) * kSF, nchunks);
   }
+}
+
+// The state of one head pair as the sum of `count` consecutive
+// [2][d][d+1] fp32 slots at st (slot stride 2 * kSF floats), written to
+// stage (n4 = (heads) * kSF / 4 float4s). Slot 0 starts each sum, later slots
+// add in ascending order - the order fold_partials uses. Each thread sums
+// elements e and e + blockDim.x (blockDim.x >= n4 / 2); loads are
+// unconditional (indices clamped to valid slots and elements) and a batch's
+// loads are all issued before any is added. The caller synchronises before
+// reading stage.
+__device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, int64_t count,
+                                                 int n4, f32x4* stage) {
+  constexpr int kBatch = 8;
+  const int e0 = threadIdx.x < n4 ? threadIdx.x : n4 - 1;
+  const int e1 = threadIdx.x + blockDim.x < n4 ? threadIdx.x + blockDim.x : n4 - 1;
+  f32x4 a0 = (f32x4)0, a1 = (f32x4)0;
+  for (int64_t j0 = 0; j0 < count; j0 += kBatch) {
+    f32x4 x0[kBatch], x1[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t j = min(j0 + u, count - 1);
+      x0[u] = st[j * (2 * kSF / 4) + e0];
+      x1[u] = st[j * (2 * kSF / 4) + e1];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool first = j0 + u == 0, take = j0 + u < count;
+      a0 = first ? x0[u] : (take ? a0 + x0[u] : a0);
+      a1 = first ? x1[u] : (take ? a1 + x1[u] : a1);
+    }
+  }
+  if (threadIdx.x < n4) stage[threadIdx.x] = a0;
+  if (threadIdx.x + blockDim.x < n4) stage[threadIdx.x + blockDim.x] = a1;
 }
 
 // Apply, one block per (unit, token chunk of Qa tiles), C chunks per unit.
@@ -830,31 +864,7 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     const f32x4* st = reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp);
     const int n4 = (sg.two ? 2 : 1) * kSF / 4;
     auto make_ops = [&](ApplyOperands (&op)[2]) {
-      // Each thread sums elements e and e + blockDim.x of the pair's state.
-      // Loads are unconditional (indices clamped to valid slots and elements)
-      // and a batch's loads are all issued before any is added.
-      constexpr int kBatch = 8;
-      const int e0 = threadIdx.x < n4 ? threadIdx.x : n4 - 1;
-      const int e1 = threadIdx.x + blockDim.x < n4 ? threadIdx.x + blockDim.x : n4 - 1;
-      f32x4 a0 = (f32x4)0, a1 = (f32x4)0;
-      for (int64_t j0 = 0; j0 < count; j0 += kBatch) {
-        f32x4 x0[kBatch], x1[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int64_t j = min(j0 + u, count - 1);
-          x0[u] = st[j * (2 * kSF / 4) + e0];
-          x1[u] = st[j * (2 * kSF / 4) + e1];
-        }
-        // slot 0 starts the sum (no 0 + x), later slots add in order
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const bool first = j0 + u == 0, take = j0 + u < count;
-          a0 = first ? x0[u] : (take ? a0 + x0[u] : a0);
-          a1 = first ? x1[u] : (take ? a1 + x1[u] : a1);
-        }
-      }
-      if (threadIdx.x < n4) stage[threadIdx.x] = a0;
-      if (threadIdx.x + blockDim.x < n4) stage[threadIdx.x + blockDim.x] = a1;
+      sum_slots_to_lds(st, count, n4, stage);
       __syncthreads();
       const float* stf = reinterpret_cast<const float*>(stage);
       op[0] = make_apply_operands(stf);
@@ -895,7 +905,7 @@ __global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
   reduce_pair_wave<U>(K, V, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
   auto make_ops = [&](ApplyOperands (&op)[2]) {
     // both heads, also for a one-head pair (its second head is never stored)
-    block_sum_state<S, false>(acc, ks, lds, pc.sub, &st[0][0], true);
+    block_sum_state<S, false>(acc, ks, lds.xchg, pc.sub, &st[0][0], true);
     __syncthreads();  // the state is complete; xchg is free for the tile slots
     op[0] = make_apply_operands(st[0]);
     op[1] = make_apply_operands(st[1]);
@@ -928,6 +938,488 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
   apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, base, 0, N, bc.sub, S);
 }
 
+// ------------------------------------------------------------ bf16 backward
+//
+// Gradients of the forward pass, per head (S_aug = [S | z], g = dL/dout):
+//   dnum_i = g_i / den_i,  dden_i = -(g_i . num_i) / den_i^2
+//   dq_i   = ([S | z] [dnum_i | dden_i]^T) * [q_i > 0]
+//   [dS | dz] = sum_i phi(q_i)^T [dnum_i | dden_i]
+//   dk_n   = ([dS | dz] [v_n | 1]^T) * [k_n > 0],   dv_n = phi(k_n) dS
+// bwd_q reads q and g, writes dq and per-block [dS | dz] partials (its token
+// reduction has the forward reduction's grid and epilogue); bwd_kv reads k,
+// v and those partials and writes dk and dv (the apply's grid). Both build
+// their state from the sum of partials, like the apply.
+
+// A operands of 16x16x32 MFMAs computing y = M x for a [d][d+1] fp32 matrix
+// M (first d columns) and one length-d vector x per token, x in the B
+// operand (k = 8*(l/16) + s, token l%16). Row i of tile t stands for
+// channel 8*(i/4) + 4t + i%4 (make_apply_operands's permutation), so after
+// the two tiles a lane holds y for channels 8*(l/16) .. +7 of token l%16.
+// M's last column for those 8 channels rides along for the VALU.
+struct RowOperands {
+  bf16x8 m0_hi, m0_lo, m1_hi, m1_lo;
+  float last[8];
+};
+
+__device__ __forceinline__ RowOperands make_row_operands(const float* st) {
+  const int l = lane_id();
+  const int g = l >> 4;
+  const int i = l & 15;
+  RowOperands o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int k = 8 * g + s;
+    const float x0 = st[(8 * (i >> 2) + (i & 3)) * kSC + k];
+    const float x1 = st[(8 * (i >> 2) + 4 + (i & 3)) * kSC + k];
+    const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+    o.m0_hi[s] = h0;
+    o.m0_lo[s] = (__bf16)(x0 - (float)h0);
+    o.m1_hi[s] = h1;
+    o.m1_lo[s] = (__bf16)(x1 - (float)h1);
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o.last[m] = st[(8 * g + m) * kSC + kD];
+  return o;
+}
+
+// y = M x for the lane's 8 channels. x is exact in bf16 (x_hi, no x_lo) or
+// fp32 split as x_hi + x_lo; the products keep M's hi and lo parts.
+template <bool SplitX>
+__device__ __forceinline__ void row_product(const RowOperands& o, bf16x8 x_hi, bf16x8 x_lo,
+                                            float (&y)[8]) {
+  f32x4 e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.m0_hi, x_hi, (f32x4)0, 0, 0, 0);
+  e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.m0_lo, x_hi, e0, 0, 0, 0);
+  f32x4 e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.m1_hi, x_hi, (f32x4)0, 0, 0, 0);
+  e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.m1_lo, x_hi, e1, 0, 0, 0);
+  if (SplitX) {
+    e0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.m0_hi, x_lo, e0, 0, 0, 0);
+    e1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.m1_hi, x_lo, e1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    y[r] = e0[r];
+    y[4 + r] = e1[r];
+  }
+}
+
+// y = phi(x) M for the lane's 8 output channels (the forward apply's
+// numerator, no normaliser): 4 MFMAs with M^T's hi and lo parts.
+__device__ __forceinline__ void col_product(const ApplyOperands& op, bf16x8 px, float (&y)[8]) {
+  f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, px, (f32x4)0, 0, 0, 0);
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, px, a0, 0, 0, 0);
+  f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, px, (f32x4)0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, px, a1, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    y[r] = a0[r];
+    y[4 + r] = a1[r];
+  }
+}
+
+// 8 packed bf16 -> fp32 (exact: a bf16 is the top half of a binary32).
+__device__ __forceinline__ void widen_bf16x8(u32x4 w, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+    x[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+  }
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x to ~2^-17 relative).
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const __bf16 h = (__bf16)x[m];
+    hi[m] = h;
+    lo[m] = (__bf16)(x[m] - (float)h);
+  }
+}
+
+// Sum over the 4 lanes that hold one token's 32 channels (l, l^16, l^32, l^48).
+__device__ __forceinline__ float token_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// A dnum tile of one head: 16 token rows of 32 bf16 channels; rows 8..15
+// sit 64 bytes further on, so the two token halves of the 32x32x16 operand
+// gather fall in different LDS banks.
+constexpr int kDnRowBytes = 2 * kD;
+constexpr int kDnTileBytes = kTile * kDnRowBytes + 64;
+__device__ __forceinline__ int dn_off(int t, int c) {
+  return t * kDnRowBytes + (t >= 8 ? 64 : 0) + 2 * c;
+}
+
+// LDS of one wave in bwd_q: the q and g tiles (whole lines, swizzled as in
+// the forward), the dnum tiles (hi and lo) and the dden row of one head.
+struct BwdQWaveLds {
+  unsigned char q[kTileBytes];
+  unsigned char g[kTileBytes];
+  unsigned char dn_hi[kDnTileBytes];
+  unsigned char dn_lo[kDnTileBytes];
+  float dd[kTile];
+};
+
+// bwd_q for the pair's two heads over the tiles sub, sub + S, ... of
+// [n_lo, n_hi): writes dq, and adds phi(q)^T dnum (acc, 32x32 MFMA layout)
+// and phi(q)^T dden (ks, per lane: channel l%32 over the lane's 8 tokens)
+// for the pair. make_ops(ro) fills the state's operands once the first
+// loads are out. One product per token carries the step: with u = S g,
+// g . num = phi(q) . u (num = phi(q) S), and since dnum = g / den,
+// S dnum = u / den, so dphi(q) = u / den + z dden. den = phi(q) . z + eps is
+// summed on the VALU from z. Padded tokens (n >= n_hi) read row n_lo, are
+// zeroed in the q tile and get dnum = dden = 0, so they add nothing even
+// where eps = 0.
+template <int U, class MakeOps>
+__device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restrict__ Q,
+                                                 const unsigned short* __restrict__ G,
+                                                 unsigned short* __restrict__ dQ,
+                                                 MakeOps&& make_ops, float eps, int64_t row,
+                                                 int64_t base, int64_t n_lo, int64_t n_hi,
+                                                 int sub, int S, bool two, BwdQWaveLds& w,
+                                                 f32x16 (&acc)[2], float (&ks)[2]) {
+  const int l = lane_id();
+  const int t0 = l >> 3;
+  const int j = l & 7;
+  const int jl = two ? j : (j & 3);
+  const int g = l >> 4;
+  const int col = l & 15;
+  const int rc = l & 31;
+  const int rt = (l >> 5) * 8;
+  const int64_t tiles = (n_hi - n_lo + kTile - 1) / kTile;
+  const int64_t mine = tiles > sub ? (tiles - sub + S - 1) / S : 0;
+
+  u32x4 qb[U][2], gb[U][2];
+  auto issue = [&](int64_t i, u32x4 (&qd)[2], u32x4 (&gd)[2]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile + t0;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int64_t n = n0 + 8 * h2;
+      const int64_t off = base + (n < n_hi ? n : n_lo) * row + 8 * jl;
+      qd[h2] = ld16(Q + off);
+      gd[h2] = ld16_stream(G + off);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) issue(u, qb[u], gb[u]);
+  RowOperands ro[2];
+  make_ops(ro);
+
+  auto compute = [&](int64_t i, const u32x4 (&qin)[2], const u32x4 (&gin)[2]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int o = tile_off(t0 + 8 * h2, j);
+      *reinterpret_cast<u32x4*>(w.q + o) = n0 + t0 + 8 * h2 < n_hi ? qin[h2] : (u32x4)0;
+      *reinterpret_cast<u32x4*>(w.g + o) = gin[h2];
+    }
+    wave_lds_order();
+    const bool valid = n0 + col < n_hi;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int po = tile_off(col, hh * 4 + g);
+      const u32x4 qraw = *reinterpret_cast<const u32x4*>(w.q + po);
+      const u32x4 graw = *reinterpret_cast<const u32x4*>(w.g + po);
+      float pq[8], gf[8], u[8];
+      widen_bf16x8(relu_bf16x8(qraw), pq);
+      widen_bf16x8(graw, gf);
+      row_product<false>(ro[hh], __builtin_bit_cast(bf16x8, graw), (bf16x8)0, u);  // u = S g
+      float dp = 0.0f, p = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        dp += pq[m] * ro[hh].last[m];  // phi(q) . z over the lane's channels
+        p += pq[m] * u[m];             // g . num = phi(q) . (S g)
+      }
+      const float rinv = 1.0f / (token_sum(dp) + eps);
+      p = token_sum(p);
+      const float dden = valid ? -p * rinv * rinv : 0.0f;
+      float dn[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) dn[m] = valid ? gf[m] * rinv : 0.0f;
+      bf16x8 dh, dl;
+      split_bf16x8(dn, dh, dl);
+      // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the ReLU gate
+      const s16x8 qs = __builtin_bit_cast(s16x8, qraw);
+      bf16x8 dq;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        dq[m] = qs[m] > 0 ? (__bf16)(u[m] * rinv + ro[hh].last[m] * dden) : (__bf16)0.0f;
+      // the token reduction: dnum and dden to LDS, gathered transposed
+      *reinterpret_cast<bf16x8*>(w.dn_hi + dn_off(col, 8 * g)) = dh;
+      *reinterpret_cast<bf16x8*>(w.dn_lo + dn_off(col, 8 * g)) = dl;
+      if (g == 0) w.dd[col] = dden;
+      wave_lds_order();
+      s16x8 a, bh, bl;
+      float ddv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int o = tile_off(rt + s, hh * 4 + (rc >> 3)) + 2 * (rc & 7);
+        a[s] = *reinterpret_cast<const short*>(w.q + o);
+        bh[s] = *reinterpret_cast<const short*>(w.dn_hi + dn_off(rt + s, rc));
+        bl[s] = *reinterpret_cast<const short*>(w.dn_lo + dn_off(rt + s, rc));
+        ddv[s] = w.dd[rt + s];
+      }
+      wave_lds_order();
+      const s16x8 pa = __builtin_elementwise_max(a, (s16x8)0);
+      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                        __builtin_bit_cast(bf16x8, bh),
+                                                        acc[hh], 0, 0, 0);
+      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pa),
+                                                        __builtin_bit_cast(bf16x8, bl),
+                                                        acc[hh], 0, 0, 0);
+      float pf[8];
+      widen_bf16x8(__builtin_bit_cast(u32x4, pa), pf);
+      float zs = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) zs += pf[s] * ddv[s];
+      ks[hh] += zs;
+      // dq replaces the g piece this lane read (no other lane reads it)
+      *reinterpret_cast<bf16x8*>(w.g + po) = dq;
+      // one head at a time: interleaving the two heads' temporaries spills
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wave_lds_order();
+  };
+  auto out_line = [&](int h2) {
+    return *reinterpret_cast<const u32x4*>(w.g + tile_off(t0 + 8 * h2, j));
+  };
+  auto out_ptr = [&](int64_t i, int h2) {
+    return dQ + base + (n_lo + (sub + i * S) * kTile + t0 + 8 * h2) * row + 8 * j;
+  };
+  const int64_t whole = two ? (n_hi - n_lo) / kTile : 0;
+  const int64_t mine_whole = whole > sub ? (whole - sub + S - 1) / S : 0;
+  int64_t i0 = 0;
+  for (; i0 + U <= mine_whole; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      compute(i0 + u, qb[u], gb[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(i0 + u + U, qb[u], gb[u]);
+      const u32x4 o0 = out_line(0), o1 = out_line(1);
+      wave_lds_order();
+      st16_stream(out_ptr(i0 + u, 0), o0);
+      st16_stream(out_ptr(i0 + u, 1), o1);
+    }
+  }
+  for (; i0 < mine; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < mine) {
+        compute(i0 + u, qb[u], gb[u]);
+        issue(i0 + u + U, qb[u], gb[u]);
+        const u32x4 o0 = out_line(0), o1 = out_line(1);
+        wave_lds_order();
+        const int64_t n = n_lo + (sub + (i0 + u) * S) * kTile + t0;
+        if (two || j < 4) {
+          if (n < n_hi) st16_stream(out_ptr(i0 + u, 0), o0);
+          if (n + 8 < n_hi) st16_stream(out_ptr(i0 + u, 1), o1);
+        }
+      }
+    }
+  }
+}
+
+// bwd_kv for the pair's two heads over the tiles sub, sub + S, ... of
+// [n_lo, n_hi): dk = ([dS | dz] [v | 1]^T) * [k > 0] and dv = phi(k) dS.
+// slot holds the wave's k tile and v tile. Padded tokens are computed from
+// row n_lo and never stored.
+template <int U, class MakeOps>
+__device__ __forceinline__ void grad_kv_pair_wave(const unsigned short* __restrict__ K,
+                                                  const unsigned short* __restrict__ V,
+                                                  unsigned short* __restrict__ dK,
+                                                  unsigned short* __restrict__ dV,
+                                                  MakeOps&& make_ops, int64_t row, int64_t base,
+                                                  int64_t n_lo, int64_t n_hi, int sub, int S,
+                                                  bool two, unsigned char* slot) {
+  const int l = lane_id();
+  const int t0 = l >> 3;
+  const int j = l & 7;
+  const int jl = two ? j : (j & 3);
+  const int g = l >> 4;
+  const int col = l & 15;
+  const int64_t tiles = (n_hi - n_lo + kTile - 1) / kTile;
+  const int64_t mine = tiles > sub ? (tiles - sub + S - 1) / S : 0;
+
+  u32x4 kb[U][2], vb[U][2];
+  auto issue = [&](int64_t i, u32x4 (&kd)[2], u32x4 (&vd)[2]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile + t0;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int64_t n = n0 + 8 * h2;
+      const int64_t off = base + (n < n_hi ? n : n_lo) * row + 8 * jl;
+      kd[h2] = ld16_stream(K + off);
+      vd[h2] = ld16_stream(V + off);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) issue(u, kb[u], vb[u]);
+  ApplyOperands ao[2];
+  RowOperands ro[2];
+  make_ops(ao, ro);
+
+  auto compute = [&](const u32x4 (&kin)[2], const u32x4 (&vin)[2]) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int o = tile_off(t0 + 8 * h2, j);
+      *reinterpret_cast<u32x4*>(slot + o) = kin[h2];
+      *reinterpret_cast<u32x4*>(slot + kTileBytes + o) = vin[h2];
+    }
+    wave_lds_order();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int po = tile_off(col, hh * 4 + g);
+      const u32x4 kraw = *reinterpret_cast<const u32x4*>(slot + po);
+      const u32x4 vraw = *reinterpret_cast<const u32x4*>(slot + kTileBytes + po);
+      float y[8], x[8];
+      row_product<false>(ro[hh], __builtin_bit_cast(bf16x8, vraw), (bf16x8)0, y);
+      col_product(ao[hh], __builtin_bit_cast(bf16x8, relu_bf16x8(kraw)), x);
+      const s16x8 kq = __builtin_bit_cast(s16x8, kraw);
+      bf16x8 dk, dv;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        dk[m] = kq[m] > 0 ? (__bf16)(y[m] + ro[hh].last[m]) : (__bf16)0.0f;
+        dv[m] = (__bf16)x[m];
+      }
+      *reinterpret_cast<bf16x8*>(slot + po) = dk;
+      *reinterpret_cast<bf16x8*>(slot + kTileBytes + po) = dv;
+    }
+    wave_lds_order();
+  };
+  auto line = [&](int tile, int h2) {
+    return *reinterpret_cast<const u32x4*>(slot + tile * kTileBytes + tile_off(t0 + 8 * h2, j));
+  };
+  auto out_off = [&](int64_t i, int h2) {
+    return base + (n_lo + (sub + i * S) * kTile + t0 + 8 * h2) * row + 8 * j;
+  };
+  const int64_t whole = two ? (n_hi - n_lo) / kTile : 0;
+  const int64_t mine_whole = whole > sub ? (whole - sub + S - 1) / S : 0;
+  int64_t i0 = 0;
+  for (; i0 + U <= mine_whole; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      compute(kb[u], vb[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(i0 + u + U, kb[u], vb[u]);
+      const u32x4 k0 = line(0, 0), k1 = line(0, 1), v0 = line(1, 0), v1 = line(1, 1);
+      wave_lds_order();
+      st16_stream(dK + out_off(i0 + u, 0), k0);
+      st16_stream(dK + out_off(i0 + u, 1), k1);
+      st16_stream(dV + out_off(i0 + u, 0), v0);
+      st16_stream(dV + out_off(i0 + u, 1), v1);
+    }
+  }
+  for (; i0 < mine; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < mine) {
+        compute(kb[u], vb[u]);
+        issue(i0 + u + U, kb[u], vb[u]);
+        const u32x4 k0 = line(0, 0), k1 = line(0, 1), v0 = line(1, 0), v1 = line(1, 1);
+        wave_lds_order();
+        const int64_t n = n_lo + (sub + (i0 + u) * S) * kTile + t0;
+        if (two || j < 4) {
+          if (n < n_hi) {
+            st16_stream(dK + out_off(i0 + u, 0), k0);
+            st16_stream(dV + out_off(i0 + u, 0), v0);
+          }
+          if (n + 8 < n_hi) {
+            st16_stream(dK + out_off(i0 + u, 1), k1);
+            st16_stream(dV + out_off(i0 + u, 1), v1);
+          }
+        }
+      }
+    }
+  }
+}
+
+// The state operands of one segment: the sum of `count` slots of the pair
+// (see sum_slots_to_lds), then both heads' operands from LDS.
+struct StateOps {
+  const f32x4* st;
+  int64_t count;
+  bool two;
+  f32x4* stage;
+  __device__ __forceinline__ const float* sum() const {
+    sum_slots_to_lds(st, count, (two ? 2 : 1) * kSF / 4, stage);
+    __syncthreads();
+    return reinterpret_cast<const float*>(stage);
+  }
+  __device__ __forceinline__ void operator()(RowOperands (&ro)[2]) const {
+    const float* stf = sum();
+    ro[0] = make_row_operands(stf);
+    ro[1] = two ? make_row_operands(stf + kSF) : ro[0];
+  }
+  __device__ __forceinline__ void operator()(ApplyOperands (&ao)[2], RowOperands (&ro)[2]) const {
+    const float* stf = sum();
+    ao[0] = make_apply_operands(stf);
+    ro[0] = make_row_operands(stf);
+    ao[1] = two ? make_apply_operands(stf + kSF) : ao[0];
+    ro[1] = two ? make_row_operands(stf + kSF) : ro[0];
+  }
+};
+
+// bwd_q over one block's range of the flattened (unit, tile) index (the
+// forward reduction's grid): the forward state of a unit is the sum of the
+// reduction's partials fwd_parts (same grid, so the same slots), and the
+// block writes its [dS | dz] partial of each unit it touches to grad_parts
+// (partial g - first, like the reduction).
+template <int S, int U>
+__global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ G,
+    unsigned short* __restrict__ dQ, const float* __restrict__ fwd_parts,
+    float* __restrict__ grad_parts, float eps, int64_t N, int64_t H, int64_t pairs, int64_t T,
+    int64_t Qb, int64_t F, int64_t slots) {
+  static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
+  union Lds {
+    BwdQWaveLds wave[S];
+    float xchg[S][kFoldFloats][kWave];
+  };
+  __shared__ Lds lds;
+  __shared__ f32x4 stage[2 * kSF / 4];
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t g = blockIdx.x;
+  const int64_t f_lo = g * Qb;
+  const int64_t f_hi = f_lo + Qb < F ? f_lo + Qb : F;
+  for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
+    const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
+    const SlotRange sr = slot_range(unit, T, Qb);
+    const StateOps ops{reinterpret_cast<const f32x4*>(fwd_parts + unit * slots * 2 * kSF),
+                       sr.count, sg.two, stage};
+    f32x16 acc[2] = {(f32x16)0, (f32x16)0};
+    float ks[2] = {0.0f, 0.0f};
+    grad_q_pair_wave<U>(Q, G, dQ, ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
+                        sg.n_hi, sub, S, sg.two, lds.wave[sub], acc, ks);
+    block_sum_state<S, false>(acc, ks, lds.xchg, sub,
+                              grad_parts + (unit * slots + (g - sr.first)) * 2 * kSF, sg.two);
+    __syncthreads();  // the LDS (tiles, exchange, stage) is reused by the next segment
+  }
+}
+
+// bwd_kv, one block per (unit, chunk), grouped by XCD exactly like the apply;
+// a unit's [dS | dz] is the sum of bwd_q's partials (slots of grid Qr).
+template <int S, int U>
+__global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
+    const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
+    unsigned short* __restrict__ dK, unsigned short* __restrict__ dV,
+    const float* __restrict__ grad_parts, int64_t N, int64_t H, int64_t pairs, int64_t units,
+    int64_t T, int64_t C, int64_t Qa, int64_t X, int64_t Qr, int64_t slots) {
+  static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
+  __shared__ unsigned char tiles[S][2 * kTileBytes];
+  __shared__ f32x4 stage[2 * kSF / 4];
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t x = blockIdx.x % X, k = blockIdx.x / X;
+  const int64_t unit = x + X * (k / C);
+  if (unit >= units) return;  // the whole block
+  const int64_t f_lo = unit * T + (k % C) * Qa;
+  const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
+  const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
+  const StateOps ops{reinterpret_cast<const f32x4*>(grad_parts + unit * slots * 2 * kSF),
+                     slot_range(unit, T, Qr).count, sg.two, stage};
+  grad_kv_pair_wave<U>(K, V, dK, dV, ops, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi,
+                       sub, S, sg.two, tiles[sub]);
+}
+
 #ifndef SANA_RED_S
 #define SANA_RED_S 8
 #endif
@@ -940,10 +1432,18 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
 #ifndef SANA_APP_U
 #define SANA_APP_U 2
 #endif
+#ifndef SANA_BWQ_U
+#define SANA_BWQ_U 2
+#endif
+#ifndef SANA_BWKV_U
+#define SANA_BWKV_U 2
+#endif
 // token sub-streams per head (S) and tiles in flight per wave (U)
 constexpr int kRedS = SANA_RED_S, kRedU = SANA_RED_U;
 constexpr int kAppS = SANA_APP_S, kAppU = SANA_APP_U;
 constexpr int kFusS = 8, kFusU = 2;
+constexpr int kBwqS = 8, kBwqU = SANA_BWQ_U;
+constexpr int kBwkvS = 8, kBwkvU = SANA_BWKV_U;
 // XCDs of MI355X (the round-robin width of block dispatch). Fewer units than
 // that: plain order (grouping would leave most blocks empty).
 constexpr int64_t kXcds = 8;
@@ -974,6 +1474,11 @@ hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, con
 }
 
 int block_waves(KernelKind kind, int dtype) {
+  switch (kind) {
+    case KernelKind::kBwdQ: return kBwqS;
+    case KernelKind::kBwdKV: return kBwkvS;
+    default: break;
+  }
   if (dtype != 1) return 2 * kF32S;
   return kind == KernelKind::kReduce ? kRedS : kAppS;
 }
@@ -993,6 +1498,14 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
                            &n, apply_bf16_kernel<kAppS, kAppU>, 64 * kAppS, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(
                            &n, apply_f32_kernel<kF32S>, 128 * kF32S, 0);
+      break;
+    case KernelKind::kBwdQ:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_q_bf16_kernel<kBwqS, kBwqU>,
+                                                       64 * kBwqS, 0);
+      break;
+    case KernelKind::kBwdKV:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_kv_bf16_kernel<kBwkvS, kBwkvU>,
+                                                       64 * kBwkvS, 0);
       break;
   }
   return e == hipSuccess && n > 0 ? n : 1;
@@ -1025,6 +1538,28 @@ hipError_t launch_apply_partials(const Plan& p, const void* q, const float* part
                      dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), partials,
                      p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
                      p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
+                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_q_bf16_kernel<kBwqS, kBwqU>), dim3((unsigned)p.red_blocks),
+                     dim3(64 * kBwqS), 0, stream, static_cast<const unsigned short*>(q),
+                     static_cast<const unsigned short*>(g), static_cast<unsigned short*>(dq),
+                     fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles, p.red_q,
+                     p.units * p.tiles, p.slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
+                         const float* grad_parts, hipStream_t stream) {
+  const int64_t X = apply_xcds(p);
+  hipLaunchKernelGGL((bwd_kv_bf16_kernel<kBwkvS, kBwkvU>),
+                     dim3((unsigned)(X * ((p.units + X - 1) / X) * p.bkv_chunks)),
+                     dim3(64 * kBwkvS), 0, stream, static_cast<const unsigned short*>(k),
+                     static_cast<const unsigned short*>(v), static_cast<unsigned short*>(dk),
+                     static_cast<unsigned short*>(dv), grad_parts, p.N, p.H, p.pairs, p.units,
+                     p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, p.red_q, p.slots);
   return hipGetLastError();
 }
 

@@ -172,3 +172,58 @@ def test_binding_raises_without_gpu_tensors():
         R.forward(x, x, x)
     with pytest.raises(TypeError if torch.cuda.is_available() else ValueError):
         R.forward(x.half(), x.half(), x.half())
+
+
+def bws(L, B, N, H, d=32, dt=BF16):
+    n = ctypes.c_size_t(123)
+    st = L.sana_linattn_bwd_workspace_size(B, N, H, d, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_bwd_workspace_size_rules(L):
+    st, n = bws(L, 2, 16384, 70)
+    assert st == OK and n % 256 == 0 and n >= 2 * 2 * 70 * 32 * 33 * 4
+    assert bws(L, 2, 4096, 36, dt=F32) == (UNSUPPORTED, 0)   # the backward is bf16 only
+    assert bws(L, 0, 16, 2) == (INVALID, 0)
+    assert bws(L, 1, 16, 2, d=64) == (UNSUPPORTED, 0)
+    assert L.sana_linattn_bwd_workspace_size(1, 16, 2, 32, BF16, None) == INVALID
+    # constant once N is large, like the forward's
+    assert len({bws(L, 2, n, 70)[1] for n in (1 << 16, 1 << 20, 1 << 24)}) == 1
+
+
+P_G, P_DQ, P_DK, P_DV = (A * i for i in range(6, 10))
+
+
+def bwd(L, q=P_Q, k=P_K, v=P_V, g=P_G, dq=P_DQ, dk=P_DK, dv=P_DV, B=1, N=64, H=2, d=32,
+        eps=1e-6, dt=BF16, ws=P_W, wsb=1 << 30, events=None, n_events=0):
+    if events is None:
+        return L.sana_linattn_bwd(q, k, v, g, dq, dk, dv, B, N, H, d, eps, dt, ws, wsb, None)
+    return L.sana_linattn_bwd_profiled(q, k, v, g, dq, dk, dv, B, N, H, d, eps, dt, ws, wsb,
+                                       events, n_events, None)
+
+
+def test_bwd_rejects_invalid_arguments(L):
+    assert bwd(L, B=0) == INVALID
+    assert bwd(L, d=16) == UNSUPPORTED
+    assert bwd(L, dt=F32) == UNSUPPORTED
+    for name in ("q", "k", "v", "g", "dq", "dk", "dv"):
+        assert bwd(L, **{name: None}) == INVALID, name
+        assert bwd(L, **{name: A * 11 + 8}) == ALIGNMENT, name
+    for eps in (-1.0, math.nan, math.inf):
+        assert bwd(L, eps=eps) == INVALID
+    # outputs overlapping an input, each other, or the workspace (8 KB tensors)
+    assert bwd(L, dq=P_Q + 4096) == INVALID
+    assert bwd(L, dk=P_G) == INVALID
+    assert bwd(L, dv=P_DK + 4096) == INVALID
+    need = bws(L, 1, 64, 2)[1]
+    assert bwd(L, dq=P_W, wsb=need) == INVALID
+    # inputs may alias each other (q used as dout too)
+    # (no launch happens here because the workspace below is missing)
+    assert bwd(L, g=P_Q, ws=None) == WORKSPACE
+    assert bwd(L, wsb=need - 1) == WORKSPACE
+    assert bwd(L, ws=P_W + 64, wsb=need) == ALIGNMENT
+    # the profiled form needs 4 events
+    events = (ctypes.c_void_p * 3)(None, None, None)
+    assert bwd(L, events=events, n_events=3) == INVALID
+    assert L.sana_linattn_bwd_profiled(P_Q, P_K, P_V, P_G, P_DQ, P_DK, P_DV, 1, 64, 2, 32, 1e-6,
+                                       BF16, P_W, 1 << 30, None, 4, None) == INVALID
