@@ -109,6 +109,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H) {
   const size_t bf16_partials =
       static_cast<size_t>(p.units) * static_cast<size_t>(p.slots) * 2 * kStateFloats * 4;
   p.partial_bytes = align_up(std::max(f32_partials, bf16_partials));
+  p.bf16_partial_bytes = align_up(bf16_partials);
   p.state_bytes = align_up(bh * kStateFloats * 4);
   p.ctl_bytes = align_up(static_cast<size_t>(p.units) * sizeof(unsigned long long));
   p.workspace_bytes = p.partial_bytes + p.state_bytes + p.ctl_bytes;
@@ -210,8 +211,8 @@ sana_status_t to_status(hipError_t e) { return e == hipSuccess ? SANA_OK : SANA_
 
 constexpr int kBwdKernels = 3;
 
-// Backward workspace: the forward reduction's partials, then bwd_q's.
-size_t bwd_workspace_bytes(const Plan& p) { return 2 * p.partial_bytes; }
+// Backward workspace (bf16): the forward reduction's partials, then bwd_q's.
+size_t bwd_workspace_bytes(const Plan& p) { return 2 * p.bf16_partial_bytes; }
 
 bool valid_variant(int variant) {
   return variant == SANA_VARIANT_AUTO || variant == SANA_VARIANT_SPLIT ||
@@ -378,7 +379,8 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
   fit_plan_to_device(fp, dtype);
   auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
   float* fwd_parts = static_cast<float*>(workspace);
-  float* grad_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.partial_bytes);
+  float* grad_parts =
+      reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.bf16_partial_bytes);
   if (!mark(0)) return SANA_ERR_HIP;
   if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream) != hipSuccess)
     return SANA_ERR_HIP;

@@ -37,7 +37,8 @@ struct Plan {
   int64_t app_chunks;
   int64_t bkv_chunk;      // backward k/v pass (bf16): tokens per chunk, chunks per unit
   int64_t bkv_chunks;
-  size_t partial_bytes;   // workspace bytes for partials
+  size_t partial_bytes;   // workspace bytes for partials (either dtype)
+  size_t bf16_partial_bytes;  // of which the bf16 partials need
   size_t state_bytes;     // workspace bytes for the combined state
   size_t ctl_bytes;       // workspace bytes for the per-unit control words
   size_t workspace_bytes; // total

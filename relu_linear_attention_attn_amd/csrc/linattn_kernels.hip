@@ -633,7 +633,7 @@ __device__ __forceinline__ PairCoords pair_coords(int64_t pairs, int64_t units, 
 // end of each head pair's range to fold the waves' sums (34 floats per lane).
 constexpr int kFoldFloats = 34;  // 32 accumulator registers + ksum of both heads
 template <int S>
-union RedLds {
+union alignas(16) RedLds {
   unsigned char slot[S][2 * kTileBytes];
   float xchg[S][kFoldFloats][kWave];
 };
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     int64_t Qr, unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
     int64_t units, int64_t T, int64_t C, int64_t Qa, int64_t X) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
-  __shared__ unsigned char slots[S][kTileBytes];
+  __shared__ alignas(16) unsigned char slots[S][kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t x = blockIdx.x % X, k = blockIdx.x / X;
@@ -1053,7 +1053,10 @@ __device__ __forceinline__ int dn_off(int t, int c) {
 
 // LDS of one wave in bwd_q: the q and g tiles (whole lines, swizzled as in
 // the forward), the dnum tiles (hi and lo) and the dden row of one head.
-struct BwdQWaveLds {
+// 16-byte alignment is stated so the 16-byte accesses stay single
+// ds_read/write_b128 instructions: at 4-byte alignment the compiler splits
+// them into 8-byte pairs, whose 16-byte lane stride conflicts 4 ways.
+struct alignas(16) BwdQWaveLds {
   unsigned char q[kTileBytes];
   unsigned char g[kTileBytes];
   unsigned char dn_hi[kDnTileBytes];
@@ -1371,7 +1374,7 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     float* __restrict__ grad_parts, float eps, int64_t N, int64_t H, int64_t pairs, int64_t T,
     int64_t Qb, int64_t F, int64_t slots) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
-  union Lds {
+  union alignas(16) Lds {
     BwdQWaveLds wave[S];
     float xchg[S][kFoldFloats][kWave];
   };
@@ -1398,6 +1401,8 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
 
 // bwd_kv, one block per (unit, chunk), grouped by XCD exactly like the apply;
 // a unit's [dS | dz] is the sum of bwd_q's partials (slots of grid Qr).
+// (Balanced ranges of the flattened index, as in the reduction, measured
+// slower: a block that straddles two units pays the state prologue twice.)
 template <int S, int U>
 __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
@@ -1405,7 +1410,7 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
     const float* __restrict__ grad_parts, int64_t N, int64_t H, int64_t pairs, int64_t units,
     int64_t T, int64_t C, int64_t Qa, int64_t X, int64_t Qr, int64_t slots) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
-  __shared__ unsigned char tiles[S][2 * kTileBytes];
+  __shared__ alignas(16) unsigned char tiles[S][2 * kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t x = blockIdx.x % X, k = blockIdx.x / X;
