@@ -1441,14 +1441,17 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
 #define SANA_BWQ_U 2
 #endif
 #ifndef SANA_BWKV_U
-#define SANA_BWKV_U 2
+#define SANA_BWKV_U 1
+#endif
+#ifndef SANA_BWKV_S
+#define SANA_BWKV_S 8
 #endif
 // token sub-streams per head (S) and tiles in flight per wave (U)
 constexpr int kRedS = SANA_RED_S, kRedU = SANA_RED_U;
 constexpr int kAppS = SANA_APP_S, kAppU = SANA_APP_U;
 constexpr int kFusS = 8, kFusU = 2;
 constexpr int kBwqS = 8, kBwqU = SANA_BWQ_U;
-constexpr int kBwkvS = 8, kBwkvU = SANA_BWKV_U;
+constexpr int kBwkvS = SANA_BWKV_S, kBwkvU = SANA_BWKV_U;
 // XCDs of MI355X (the round-robin width of block dispatch). Fewer units than
 // that: plain order (grouping would leave most blocks empty).
 constexpr int64_t kXcds = 8;
