@@ -1042,25 +1042,15 @@ __device__ __forceinline__ float token_sum(float x) {
   return x;
 }
 
-// A dnum tile of one head: 16 token rows of 32 bf16 channels; rows 8..15
-// sit 64 bytes further on, so the two token halves of the 32x32x16 operand
-// gather fall in different LDS banks.
-constexpr int kDnRowBytes = 2 * kD;
-constexpr int kDnTileBytes = kTile * kDnRowBytes + 64;
-__device__ __forceinline__ int dn_off(int t, int c) {
-  return t * kDnRowBytes + (t >= 8 ? 64 : 0) + 2 * c;
-}
-
 // LDS of one wave in bwd_q: the q and g tiles (whole lines, swizzled as in
-// the forward), the dnum tiles (hi and lo) and the dden row of one head.
+// the forward) and, for one head, the 1 / den and dden rows of the tile.
 // 16-byte alignment is stated so the 16-byte accesses stay single
 // ds_read/write_b128 instructions: at 4-byte alignment the compiler splits
 // them into 8-byte pairs, whose 16-byte lane stride conflicts 4 ways.
 struct alignas(16) BwdQWaveLds {
   unsigned char q[kTileBytes];
   unsigned char g[kTileBytes];
-  unsigned char dn_hi[kDnTileBytes];
-  unsigned char dn_lo[kDnTileBytes];
+  float rv[kTile];
   float dd[kTile];
 };
 
@@ -1071,9 +1061,11 @@ struct alignas(16) BwdQWaveLds {
 // loads are out. One product per token carries the step: with u = S g,
 // g . num = phi(q) . u (num = phi(q) S), and since dnum = g / den,
 // S dnum = u / den, so dphi(q) = u / den + z dden. den = phi(q) . z + eps is
-// summed on the VALU from z. Padded tokens (n >= n_hi) read row n_lo, are
-// zeroed in the q tile and get dnum = dden = 0, so they add nothing even
-// where eps = 0.
+// summed on the VALU from z. The token reduction uses the same fact:
+// phi(q)^T dnum = (phi(q) / den)^T g, so the 32x32x16 MFMA takes g exactly
+// (gathered from the g tile) and phi(q) / den split into bf16 hi + lo.
+// Padded tokens (n >= n_hi) read row n_lo, are zeroed in the q tile and get
+// 1 / den = dden = 0, so they add nothing even where eps = 0.
 template <int U, class MakeOps>
 __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restrict__ Q,
                                                  const unsigned short* __restrict__ G,
@@ -1137,45 +1129,46 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       const float rinv = 1.0f / (token_sum(dp) + eps);
       p = token_sum(p);
       const float dden = valid ? -p * rinv * rinv : 0.0f;
-      float dn[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) dn[m] = valid ? gf[m] * rinv : 0.0f;
-      bf16x8 dh, dl;
-      split_bf16x8(dn, dh, dl);
       // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the ReLU gate
       const s16x8 qs = __builtin_bit_cast(s16x8, qraw);
       bf16x8 dq;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
         dq[m] = qs[m] > 0 ? (__bf16)(u[m] * rinv + ro[hh].last[m] * dden) : (__bf16)0.0f;
-      // the token reduction: dnum and dden to LDS, gathered transposed
-      *reinterpret_cast<bf16x8*>(w.dn_hi + dn_off(col, 8 * g)) = dh;
-      *reinterpret_cast<bf16x8*>(w.dn_lo + dn_off(col, 8 * g)) = dl;
-      if (g == 0) w.dd[col] = dden;
+      // the token reduction: 1 / den and dden rows to LDS, the operands
+      // gathered transposed (k = the lane's 8 tokens, channel l%32)
+      if (g == 0) {
+        w.rv[col] = valid ? rinv : 0.0f;
+        w.dd[col] = dden;
+      }
       wave_lds_order();
-      s16x8 a, bh, bl;
-      float ddv[8];
+      s16x8 a, b;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int o = tile_off(rt + s, hh * 4 + (rc >> 3)) + 2 * (rc & 7);
         a[s] = *reinterpret_cast<const short*>(w.q + o);
-        bh[s] = *reinterpret_cast<const short*>(w.dn_hi + dn_off(rt + s, rc));
-        bl[s] = *reinterpret_cast<const short*>(w.dn_lo + dn_off(rt + s, rc));
-        ddv[s] = w.dd[rt + s];
+        b[s] = *reinterpret_cast<const short*>(w.g + o);
       }
+      const f32x4 rv0 = *reinterpret_cast<const f32x4*>(w.rv + rt);
+      const f32x4 rv1 = *reinterpret_cast<const f32x4*>(w.rv + rt + 4);
+      const f32x4 dd0 = *reinterpret_cast<const f32x4*>(w.dd + rt);
+      const f32x4 dd1 = *reinterpret_cast<const f32x4*>(w.dd + rt + 4);
       wave_lds_order();
-      const s16x8 pa = __builtin_elementwise_max(a, (s16x8)0);
-      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                        __builtin_bit_cast(bf16x8, bh),
-                                                        acc[hh], 0, 0, 0);
-      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pa),
-                                                        __builtin_bit_cast(bf16x8, bl),
-                                                        acc[hh], 0, 0, 0);
-      float pf[8];
-      widen_bf16x8(__builtin_bit_cast(u32x4, pa), pf);
+      float pf[8], sc[8];
+      widen_bf16x8(relu_bf16x8(__builtin_bit_cast(u32x4, a)), pf);
       float zs = 0.0f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) zs += pf[s] * ddv[s];
+      for (int s = 0; s < 4; ++s) {
+        sc[s] = pf[s] * rv0[s];
+        sc[4 + s] = pf[4 + s] * rv1[s];
+        zs += pf[s] * dd0[s];
+        zs += pf[4 + s] * dd1[s];
+      }
+      bf16x8 ah, al;
+      split_bf16x8(sc, ah, al);
+      const bf16x8 bg = __builtin_bit_cast(bf16x8, b);
+      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bg, acc[hh], 0, 0, 0);
+      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bg, acc[hh], 0, 0, 0);
       ks[hh] += zs;
       // dq replaces the g piece this lane read (no other lane reads it)
       *reinterpret_cast<bf16x8*>(w.g + po) = dq;
