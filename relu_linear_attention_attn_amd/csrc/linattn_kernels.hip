@@ -1036,6 +1036,9 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf
 }
 
 // Sum over the 4 lanes that hold one token's 32 channels (l, l^16, l^32, l^48).
+// (gfx950's permlane16/32_swap builtins would avoid the LDS round trip, but
+// this compiler folds the two results of a swap of x with itself into one
+// register, giving wrong sums; the shuffles are kept.)
 __device__ __forceinline__ float token_sum(float x) {
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
@@ -1126,7 +1129,7 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
         dp += pq[m] * ro[hh].last[m];  // phi(q) . z over the lane's channels
         p += pq[m] * u[m];             // g . num = phi(q) . (S g)
       }
-      const float rinv = 1.0f / (token_sum(dp) + eps);
+      const float rinv = __builtin_amdgcn_rcpf(token_sum(dp) + eps);  // 1 ulp
       p = token_sum(p);
       const float dden = valid ? -p * rinv * rinv : 0.0f;
       // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the ReLU gate
