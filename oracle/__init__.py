@@ -18,3 +18,8 @@ from .linattn_bwd import (  # noqa: F401,E402
     linattn_bwd_from_inputs,
     state_grad_head,
 )
+from .linattn_block_causal import (  # noqa: F401,E402
+    block_causal_fp64,
+    block_causal_from_inputs,
+    masked_quadratic_fp64,
+)
