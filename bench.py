@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E spec peak
 METRIC = "linear-attn fwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
 METRIC_BWD = "linear-attn bwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
+METRIC_BC = "block-causal linear-attn fwd tokens/s + achieved HBM GB/s (% roofline)"
 CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "traffic_latent_4096px.json"),
                  "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json")}
@@ -40,8 +41,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd"],
-                    help="forward pass (the headline) or backward pass")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "block_causal"],
+                    help="forward pass (the headline), backward pass, or block-causal "
+                         "forward (default workload: the 16-frame video, one block per frame)")
+    ap.add_argument("--block", type=int, default=65536,
+                    help="tokens per block for --op block_causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
     ap.add_argument("--quiet", action="store_true")
@@ -97,6 +101,7 @@ def _counter_rows(folder: str):
 
 def _kernel_key(name: str) -> str:
     for k, v in (("reduce_bf16_kernel", "reduce"), ("apply_bf16_kernel", "apply"),
+                 ("scan_block_states_kernel", "scan"),
                  ("fused_bf16_kernel", "fused"), ("bwd_q_bf16_kernel", "bwd_q"),
                  ("bwd_kv_bf16_kernel", "bwd_kv"), ("bitwise_not", "copy")):
         if k in name:
@@ -345,6 +350,125 @@ def run_bwd(args, w):
     print(json.dumps(result), flush=True)
 
 
+def cpu_baseline_block_causal(w, inputs, block: int, budget_s: float):
+    """The block-causal oracle on whole heads until the budget is spent."""
+    import oracle.linattn as L
+    import oracle.linattn_block_causal as BC
+
+    threads = _blas_threads()
+    done, decode_s = 0, 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for b in range(w.B):
+            for h in range(w.H):
+                ta = time.perf_counter()
+                q, k, v = (L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkv")
+                decode_s += time.perf_counter() - ta
+                BC.block_causal_head(q, k, v, block, w.eps)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    wall = time.perf_counter() - t0
+    return {
+        "value": done * w.N / wall / w.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} (b, h) head passes of {w.B * w.H} x all {w.N} tokens of {w.name}, "
+                  f"blocks of {block}, float64 NumPy ({wall:.1f} s wall incl. {decode_s:.1f} s "
+                  f"bf16 decode); tokens/s = token-heads/s / H",
+        "seconds": wall,
+    }
+
+
+def run_block_causal(args, w):
+    """Block-causal forward: one JSON line like the forward's (see main)."""
+    import numpy as np
+    import torch
+
+    import relu_linear_attention_attn_amd as R
+
+    block = args.block
+    log(args, f"workload {w.name} {w.shape} {w.dtype} block-causal, blocks of {block}: "
+              "generating inputs")
+    from relu_linear_attention_attn_amd import workloads as W
+    x = W.generate(w)
+    if w.dtype == "bf16":
+        dev = {t: torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).cuda() for t in "qkv"}
+    else:
+        dev = {t: torch.from_numpy(x[t]).cuda() for t in "qkv"}
+    out = torch.empty_like(dev["q"])
+    dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
+    ws = torch.empty(R.block_causal_workspace_size(w.B, w.N, w.H, block, w.d, dt),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(events=None):
+        R.forward_block_causal(dev["q"], dev["k"], dev["v"], block, eps=w.eps, out=out,
+                               workspace=ws, events=events)
+
+    names = ["reduce", "scan", "apply"]
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    log(args, f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
+    per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+                  for j, n in enumerate(names)}
+    step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
+    elem = w.B * w.N * w.H * w.d * w.itemsize
+    alg_bytes = {"reduce": 2 * elem, "apply": 2 * elem}
+    dominant = max(alg_bytes, key=lambda n: per_kernel[n])
+    achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-3) / 1e9
+    path_gbps = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC_BC,
+        "value": w.B * w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "block_causal", "block": block, "B": w.B,
+                   "N": w.N, "H": w.H, "d": w.d, "D": w.D, "eps": w.eps},
+        "achieved_hbm_gbps": path_gbps,
+        "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
+        "kernel_ms": per_kernel,
+        "ms_per_step_with_kernel_events": ms_events,
+        "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None},
+    }
+    if args.copy_mib == 0:
+        ceil = copy_ceiling(dev["q"].device)
+        result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
+    if args.cpu_seconds > 0:
+        log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_block_causal(w, x, block, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -373,6 +497,10 @@ def main():
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         R.lib()
         return run_bwd(args, w)
+    if args.op == "block_causal":
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        R.lib()
+        return run_block_causal(args, W.WORKLOADS[args.workload or "video_1m_tokens"])
     variant = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}[args.variant]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.lib()

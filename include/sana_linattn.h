@@ -214,6 +214,43 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
                                         int dtype, void* workspace, size_t workspace_bytes,
                                         hipEvent_t* events, int n_events, hipStream_t stream);
 
+/*
+ * Block-causal forward pass. The N tokens of each batch item form N / block
+ * consecutive blocks of `block` tokens (a video frame is such a block); a
+ * query in block c attends to every key in blocks 0..c - its own block
+ * included, earlier blocks in full:
+ *
+ *     S_c   = sum over tokens n in blocks 0..c of phi(k_n)^T [v_n | 1]
+ *     out_i = phi(q_i) S_c(i)[:, :d] / (phi(q_i) . S_c(i)[:, d] + eps)
+ *
+ * The Linear-DiT 4K blog, section "技术演进", names Block Causal Linear
+ * Attention (SANA-Video) without a formula; this is its plainest reading.
+ * block = N is sana_linattn_fwd's non-causal attention; block = 1 is
+ * token-causal attention (correct but slow: the work is done per block).
+ * N must be a multiple of block (SANA_ERR_INVALID_ARG otherwise). Tensors,
+ * dtypes, eps, alignment and overlap rules as for sana_linattn_fwd;
+ * workspace: at least sana_linattn_block_causal_workspace_size(...) bytes,
+ * 256-byte aligned, contents irrelevant on entry. Three kernels: the state
+ * reduction per block, an inclusive prefix sum over each batch item's blocks
+ * (fixed order: results are bitwise repeatable), the apply.
+ */
+sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,
+                                                      int64_t d, int64_t block, int dtype,
+                                                      size_t* bytes);
+sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const void* v,
+                                            void* out, int64_t B, int64_t N, int64_t H,
+                                            int64_t d, int64_t block, float eps, int dtype,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
+/* The same, recording events[0] before and events[1..3] after its three
+ * kernels (n_events >= 4, caller-created events). */
+sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* k, const void* v,
+                                                     void* out, int64_t B, int64_t N, int64_t H,
+                                                     int64_t d, int64_t block, float eps,
+                                                     int dtype, void* workspace,
+                                                     size_t workspace_bytes, hipEvent_t* events,
+                                                     int n_events, hipStream_t stream);
+
 const char* sana_linattn_strerror(int status);
 
 /* SANA_LINATTN_VERSION of the built library. */

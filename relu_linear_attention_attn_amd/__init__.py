@@ -1,4 +1,5 @@
-"""ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward and backward.
+"""ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward (non-causal and
+block-causal) and backward.
 
 The compute runs in hand-written HIP kernels behind a C ABI
 (``libsana_linattn.so``, declared in ``include/sana_linattn.h``); this package
@@ -14,8 +15,10 @@ from .binding import (  # noqa: F401
     SanaError,
     apply,
     backward,
+    block_causal_workspace_size,
     bwd_workspace_size,
     forward,
+    forward_block_causal,
     forward_profiled,
     kv_state,
     lib,

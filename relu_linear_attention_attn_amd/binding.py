@@ -41,6 +41,9 @@ EXPORTS = (
     "sana_linattn_bwd_workspace_size",
     "sana_linattn_bwd",
     "sana_linattn_bwd_profiled",
+    "sana_linattn_block_causal_workspace_size",
+    "sana_linattn_fwd_block_causal",
+    "sana_linattn_fwd_block_causal_profiled",
     "sana_linattn_strerror",
     "sana_linattn_version",
 )
@@ -93,6 +96,15 @@ def lib() -> ctypes.CDLL:
                                                                 _vp, _sz, _vp]
         L.sana_linattn_bwd_profiled.argtypes = [_vp] * 7 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+        L.sana_linattn_block_causal_workspace_size.argtypes = [_i64] * 5 + [
+            ctypes.c_int, ctypes.POINTER(_sz)]
+        L.sana_linattn_fwd_block_causal.argtypes = [_vp] * 4 + [_i64] * 5 + [
+            ctypes.c_float, ctypes.c_int, _vp, _sz, _vp]
+        L.sana_linattn_fwd_block_causal_profiled.argtypes = [_vp] * 4 + [_i64] * 5 + [
+            ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+        for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
+                     "sana_linattn_fwd_block_causal_profiled"):
+            getattr(L, name).restype = ctypes.c_int
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
                      "sana_linattn_fwd", "sana_linattn_fwd_variant", "sana_linattn_fwd_profiled",
                      "sana_linattn_kv_state", "sana_linattn_apply",
@@ -325,3 +337,46 @@ def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grad
                                                workspace.data_ptr(), wb, arr, len(events),
                                                _stream(q)), "sana_linattn_bwd_profiled")
     return grads
+
+
+def block_causal_workspace_size(B: int, N: int, H: int, block: int, d: int = HEAD_DIM,
+                                dtype: int = DTYPE_BF16) -> int:
+    n = _sz(0)
+    _check(lib().sana_linattn_block_causal_workspace_size(B, N, H, d, block, dtype,
+                                                          ctypes.byref(n)),
+           "sana_linattn_block_causal_workspace_size")
+    return n.value
+
+
+def forward_block_causal(q, k, v, block: int, eps: float = 1e-6, heads: Optional[int] = None,
+                         out=None, workspace=None, events=None):
+    """Block-causal forward: a query in block c (of `block` tokens) sees keys
+    in blocks 0..c. Same tensors as forward(); events: optional list of 4
+    torch.cuda.Event recorded around the three kernels."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q)
+    _check_tensor(v, "v", q)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q)
+    if workspace is None:
+        workspace = torch.empty(max(block_causal_workspace_size(B, N, H, block, d, dt), 1),
+                                dtype=torch.uint8, device=q.device)
+    wb = workspace.numel() * workspace.element_size()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, N, H, d, int(block),
+            float(eps), dt, workspace.data_ptr(), wb)
+    if events is None:
+        _check(lib().sana_linattn_fwd_block_causal(*args, _stream(q)),
+               "sana_linattn_fwd_block_causal")
+    else:
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event on first record
+                e.record()
+        arr = (_vp * len(events))(*[e.cuda_event for e in events])
+        _check(lib().sana_linattn_fwd_block_causal_profiled(*args, arr, len(events), _stream(q)),
+               "sana_linattn_fwd_block_causal_profiled")
+    return out

@@ -334,6 +334,75 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   return mark(2) ? SANA_OK : SANA_ERR_HIP;
 }
 
+// Block-causal attention (blocks of L tokens): the plan treats each block
+// as a batch item; the workspace holds that plan's parts and the prefix
+// states.
+struct BlockCausalPlan {
+  Plan p;               // batch items = the B * F blocks of L tokens
+  int64_t F;            // blocks per batch item
+  size_t prefix_bytes;  // [B * F][H][d][d+1] fp32
+  size_t workspace_bytes;
+};
+
+sana_status_t plan_block_causal(int64_t B, int64_t N, int64_t H, int64_t d, int64_t L,
+                                int dtype, BlockCausalPlan* bc, size_t* tensor_bytes) {
+  sana_status_t s = check_shape(B, N, H, d, dtype, tensor_bytes);
+  if (s != SANA_OK) return s;
+  if (L < 1 || N % L != 0) return SANA_ERR_INVALID_ARG;
+  const int64_t F = N / L;
+  // the blocks as batch items: B * F < 2^62 since B * N * H * d is
+  if ((s = check_shape(B * F, L, H, d, dtype, nullptr)) != SANA_OK) return s;
+  if (scan_grid_blocks(B, cdiv(H, kHeadsPerBlock)) > INT32_MAX) return SANA_ERR_INVALID_ARG;
+  bc->p = make_plan(B * F, L, H);
+  bc->F = F;
+  bc->prefix_bytes = align_up(static_cast<size_t>(B * F * H) * kStateFloats * 4);
+  bc->workspace_bytes = bc->p.workspace_bytes + bc->prefix_bytes;
+  return SANA_OK;
+}
+
+// events (may be NULL) are recorded before the first kernel and after each of
+// the three (reduction, scan, apply).
+sana_status_t block_causal(const void* q, const void* k, const void* v, void* out, int64_t B,
+                           int64_t N, int64_t H, int64_t d, int64_t L, float eps, int dtype,
+                           void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                           int n_events, hipStream_t stream) {
+  BlockCausalPlan bc;
+  size_t tb = 0;
+  sana_status_t s = plan_block_causal(B, N, H, d, L, dtype, &bc, &tb);
+  if (s != SANA_OK) return s;
+  if (events) {
+    if (n_events < 4) return SANA_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+      if (!events[i]) return SANA_ERR_INVALID_ARG;
+  }
+  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
+  if ((s = check_eps(eps)) != SANA_OK) return s;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return SANA_ERR_ALIGNMENT;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+    return SANA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < bc.workspace_bytes) return SANA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
+  if (overlaps(out, tb, workspace, bc.workspace_bytes)) return SANA_ERR_INVALID_ARG;
+
+  (void)hipGetLastError();
+  Plan fp = bc.p;
+  fit_plan_to_device(fp, dtype);
+  const WorkspaceParts w = split_workspace(fp, workspace);
+  float* prefix = reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.workspace_bytes);
+  auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+  const bool bf16 = dtype == SANA_DTYPE_BF16;
+  if (!mark(0)) return SANA_ERR_HIP;
+  if (launch_reduce(fp, dtype, !bf16, k, v, w.partials, w.state, w.ctl, next_epoch(), stream) !=
+      hipSuccess)
+    return SANA_ERR_HIP;
+  if (!mark(1)) return SANA_ERR_HIP;
+  if (launch_scan_blocks(fp, dtype, bc.F, w.partials, w.state, prefix, stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  if (!mark(2)) return SANA_ERR_HIP;
+  if (launch_apply(fp, dtype, q, prefix, out, eps, stream) != hipSuccess) return SANA_ERR_HIP;
+  return mark(3) ? SANA_OK : SANA_ERR_HIP;
+}
+
 // The backward pass (bf16): the forward state reduction (partials only),
 // bwd_q (dq and the [dS | dz] partials), bwd_kv (dk, dv). events (may be
 // NULL) are recorded before the first kernel and after each of the three.
@@ -499,6 +568,38 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
   if (!events) return SANA_ERR_INVALID_ARG;
   return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
                         workspace_bytes, events, n_events, stream);
+}
+
+sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,
+                                                      int64_t d, int64_t block, int dtype,
+                                                      size_t* bytes) {
+  if (!bytes) return SANA_ERR_INVALID_ARG;
+  *bytes = 0;
+  sana::BlockCausalPlan bc;
+  const sana_status_t s = sana::plan_block_causal(B, N, H, d, block, dtype, &bc, nullptr);
+  if (s != SANA_OK) return s;
+  *bytes = bc.workspace_bytes;
+  return SANA_OK;
+}
+
+sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const void* v,
+                                            void* out, int64_t B, int64_t N, int64_t H,
+                                            int64_t d, int64_t block, float eps, int dtype,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+  return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
+                            workspace_bytes, nullptr, 0, stream);
+}
+
+sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* k, const void* v,
+                                                     void* out, int64_t B, int64_t N, int64_t H,
+                                                     int64_t d, int64_t block, float eps,
+                                                     int dtype, void* workspace,
+                                                     size_t workspace_bytes, hipEvent_t* events,
+                                                     int n_events, hipStream_t stream) {
+  if (!events) return SANA_ERR_INVALID_ARG;
+  return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
+                            workspace_bytes, events, n_events, stream);
 }
 
 const char* sana_linattn_strerror(int status) {

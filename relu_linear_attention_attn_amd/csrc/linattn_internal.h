@@ -74,6 +74,14 @@ hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
                         const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream);
 hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
                          const float* grad_parts, hipStream_t stream);
+// Block-causal attention: p's batch items are the F blocks of each of the
+// p.B / F original batch items. Inclusive prefix sums over the blocks of the
+// reduction's result (bf16: its partials, launch_reduce(fold = false);
+// fp32: its folded state) into prefix, a [p.B][H][d][d+1] state for
+// launch_apply.
+hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* partials,
+                              const float* state, float* prefix, hipStream_t stream);
+int64_t scan_grid_blocks(int64_t B, int64_t pairs);  // grid size of that launch
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k,
                         const void* v, void* out, float eps, hipStream_t stream);
 

@@ -830,14 +830,29 @@ __device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, i
   if (threadIdx.x + blockDim.x < n4) stage[threadIdx.x + blockDim.x] = a1;
 }
 
-// Apply, one block per (unit, token chunk of Qa tiles), C chunks per unit.
-// The hardware deals blocks to the XCDs round robin (block g to XCD g % X on
-// MI355X, X = 8), and each XCD has its own L2: block g takes item g / X of
-// XCD g % X's list, which holds units g % X, g % X + X, ... with their C
-// chunks in a row. A unit's chunk blocks then share one L2, which fetches the
-// unit's partials once instead of once per block. Blocks past the last unit
-// exit (the grid is X * ceil(units / X) * C). X = 1 keeps the plain order;
-// the mapping is a bijection either way, only locality depends on X.
+// XCD-grouped (unit, chunk) items. The hardware deals blocks to the XCDs
+// round robin (block g to XCD g % X on MI355X, X = 8), and each XCD has its
+// own L2. The units * C items, unit-major, are cut into X contiguous runs of
+// `per` = ceil(units * C / X) items; block g takes item g / X of run g % X.
+// Every XCD then gets the same number of blocks, and a unit's chunk blocks
+// share one L2 (or two, where a run boundary splits the unit), which fetches
+// the unit's partials about once instead of once per block. The grid is
+// X * per blocks; the few past the last item exit. X = 1 keeps the plain
+// order; the mapping is a bijection either way, only locality depends on X.
+struct Item {
+  int64_t unit, chunk;
+  bool valid;
+};
+__device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
+  const int64_t items = units * C;
+  const int64_t per = (items + X - 1) / X;
+  const int64_t item = (blockIdx.x % X) * per + blockIdx.x / X;
+  const int64_t unit = item / C;
+  return {unit, item - unit * C, item < items};
+}
+
+// Apply, one block per (unit, token chunk of Qa tiles), C chunks per unit,
+// grouped by XCD (xcd_item).
 // The state of a unit is the sum of `count`
 // consecutive [2][d][d+1] slots at src + b * sb + p * sp (+ j * 2 * kSF),
 // count from slot_range(unit, T, Qr) when Qr > 0 (the partials of the
@@ -853,10 +868,10 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
   __shared__ alignas(16) unsigned char slots[S][kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t x = blockIdx.x % X, k = blockIdx.x / X;
-  const int64_t unit = x + X * (k / C);
-  if (unit >= units) return;  // the whole block
-  const int64_t f_lo = unit * T + (k % C) * Qa;
+  const Item it = xcd_item(units, C, X);
+  if (!it.valid) return;  // the whole block
+  const int64_t unit = it.unit;
+  const int64_t f_lo = unit * T + it.chunk * Qa;
   const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
   {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
@@ -1409,16 +1424,54 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
   __shared__ alignas(16) unsigned char tiles[S][2 * kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t x = blockIdx.x % X, k = blockIdx.x / X;
-  const int64_t unit = x + X * (k / C);
-  if (unit >= units) return;  // the whole block
-  const int64_t f_lo = unit * T + (k % C) * Qa;
+  const Item it = xcd_item(units, C, X);
+  if (!it.valid) return;  // the whole block
+  const int64_t unit = it.unit;
+  const int64_t f_lo = unit * T + it.chunk * Qa;
   const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
   const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
   const StateOps ops{reinterpret_cast<const f32x4*>(grad_parts + unit * slots * 2 * kSF),
                      slot_range(unit, T, Qr).count, sg.two, stage};
   grad_kv_pair_wave<U>(K, V, dK, dV, ops, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi,
                        sub, S, sg.two, tiles[sub]);
+}
+
+// ------------------------------------------------------ block-causal scan
+//
+// Block-causal attention runs the forward kernels on a plan whose batch
+// items are the blocks (a [B][N][H][d] tensor is the same memory as
+// [B * F][L][H][d] for F blocks of L tokens). Between the reduction and the
+// apply, this kernel turns block states into inclusive prefix sums over the
+// F blocks of each batch item. Unit u = (b * F + f) * pairs + p of that plan
+// has the state sum_{j < count} src[b' * sb + p * sp + j * 2 * kSF + e]
+// (b' = b * F + f; count from slot_range(u, T, Qr) when Qr > 0, else 1).
+// Thread (b, p, e) walks f = 0 .. F-1, adds block f's element e (slots in
+// ascending order) to its running sum and writes the sum to
+// dst[(b' * H + h) * kSF + e % kSF], the [B * F][H][d][d+1] layout the apply
+// reads. Fixed order throughout, so the result is bitwise repeatable.
+constexpr int kScanThreads = 256;
+constexpr int kScanBlocksPerPair = (2 * kSF + kScanThreads - 1) / kScanThreads;
+
+__global__ __launch_bounds__(kScanThreads) void scan_block_states_kernel(
+    const float* __restrict__ src, int64_t sb, int64_t sp, int64_t Qr, int64_t T,
+    float* __restrict__ dst, int64_t F, int64_t H, int64_t pairs) {
+  const int64_t bp = blockIdx.x / kScanBlocksPerPair;  // b * pairs + p
+  const int e = (blockIdx.x - bp * kScanBlocksPerPair) * kScanThreads + threadIdx.x;
+  if (e >= 2 * kSF) return;
+  const int64_t b = bp / pairs, p = bp - b * pairs;
+  const int hh = e >= kSF ? 1 : 0;
+  const int64_t h = 2 * p + hh;
+  if (h >= H) return;
+  float run = 0.0f;
+  for (int64_t f = 0; f < F; ++f) {
+    const int64_t b2 = b * F + f;
+    const int64_t count = Qr > 0 ? slot_range(b2 * pairs + p, T, Qr).count : 1;
+    const float* x = src + b2 * sb + p * sp + e;
+    float sum = x[0];
+    for (int64_t j = 1; j < count; ++j) sum += x[j * 2 * kSF];
+    run = f == 0 ? sum : run + sum;
+    dst[(b2 * H + h) * kSF + (e - hh * kSF)] = run;
+  }
 }
 
 #ifndef SANA_RED_S
@@ -1449,9 +1502,10 @@ constexpr int kFusS = 8, kFusU = 2;
 constexpr int kBwqS = 8, kBwqU = SANA_BWQ_U;
 constexpr int kBwkvS = SANA_BWKV_S, kBwkvU = SANA_BWKV_U;
 // XCDs of MI355X (the round-robin width of block dispatch). Fewer units than
-// that: plain order (grouping would leave most blocks empty).
+// that: plain order (a unit's chunks are spread over the XCDs anyway).
 constexpr int64_t kXcds = 8;
 int64_t apply_xcds(const Plan& p) { return p.units >= kXcds ? kXcds : 1; }
+int64_t xcd_grid(int64_t items, int64_t X) { return X * ((items + X - 1) / X); }
 constexpr int kF32S = 2, kF32U = 2;
 
 }  // namespace
@@ -1520,7 +1574,7 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
   if (dtype == 1) {
     const int64_t X = apply_xcds(p);
     hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>),
-                       dim3((unsigned)(X * ((p.units + X - 1) / X) * p.app_chunks)),
+                       dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)),
                        dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), state,
                        p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
                        eps, p.N, p.H, p.pairs, p.units, p.tiles, p.app_chunks,
@@ -1538,7 +1592,7 @@ hipError_t launch_apply_partials(const Plan& p, const void* q, const float* part
   const int64_t sp = p.slots * 2 * kSF;
   const int64_t X = apply_xcds(p);
   hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>),
-                     dim3((unsigned)(X * ((p.units + X - 1) / X) * p.app_chunks)),
+                     dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)),
                      dim3(64 * kAppS), 0, stream, static_cast<const unsigned short*>(q), partials,
                      p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
                      p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
@@ -1559,13 +1613,27 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
                          const float* grad_parts, hipStream_t stream) {
   const int64_t X = apply_xcds(p);
   hipLaunchKernelGGL((bwd_kv_bf16_kernel<kBwkvS, kBwkvU>),
-                     dim3((unsigned)(X * ((p.units + X - 1) / X) * p.bkv_chunks)),
+                     dim3((unsigned)xcd_grid(p.units * p.bkv_chunks, X)),
                      dim3(64 * kBwkvS), 0, stream, static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(dk),
                      static_cast<unsigned short*>(dv), grad_parts, p.N, p.H, p.pairs, p.units,
                      p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, p.red_q, p.slots);
   return hipGetLastError();
 }
+
+hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* partials,
+                              const float* state, float* prefix, hipStream_t stream) {
+  const int64_t B = p.B / F;
+  const bool bf16 = dtype == 1;
+  const int64_t sb = bf16 ? p.pairs * p.slots * 2 * kSF : p.H * kSF;
+  const int64_t sp = bf16 ? p.slots * 2 * kSF : int64_t(2 * kSF);
+  hipLaunchKernelGGL(scan_block_states_kernel, dim3((unsigned)(B * p.pairs * kScanBlocksPerPair)),
+                     dim3(kScanThreads), 0, stream, bf16 ? partials : state, sb, sp,
+                     bf16 ? p.red_q : int64_t(0), p.tiles, prefix, F, p.H, p.pairs);
+  return hipGetLastError();
+}
+
+int64_t scan_grid_blocks(int64_t B, int64_t pairs) { return B * pairs * kScanBlocksPerPair; }
 
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k, const void* v,
                         void* out, float eps, hipStream_t stream) {

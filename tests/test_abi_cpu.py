@@ -227,3 +227,33 @@ def test_bwd_rejects_invalid_arguments(L):
     assert bwd(L, events=events, n_events=3) == INVALID
     assert L.sana_linattn_bwd_profiled(P_Q, P_K, P_V, P_G, P_DQ, P_DK, P_DV, 1, 64, 2, 32, 1e-6,
                                        BF16, P_W, 1 << 30, None, 4, None) == INVALID
+
+
+def bcws(L, B, N, H, blk, d=32, dt=BF16):
+    n = ctypes.c_size_t(123)
+    st = L.sana_linattn_block_causal_workspace_size(B, N, H, d, blk, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_block_causal_workspace_and_errors(L):
+    st, n = bcws(L, 1, 1 << 20, 36, 1 << 16)
+    assert st == OK and n % 256 == 0 and n >= 16 * 36 * 32 * 33 * 4   # holds the prefix states
+    assert bcws(L, 2, 4096, 36, 1024, dt=F32)[0] == OK                # both dtypes
+    assert bcws(L, 1, 1000, 2, 3) == (INVALID, 0)                      # N not a multiple of block
+    assert bcws(L, 1, 1000, 2, 0) == (INVALID, 0)
+    assert bcws(L, 1, 1000, 2, -8) == (INVALID, 0)
+    assert bcws(L, 1, 1000, 2, 1000, d=16) == (UNSUPPORTED, 0)
+    assert L.sana_linattn_block_causal_workspace_size(1, 16, 2, 32, 16, BF16, None) == INVALID
+    need = bcws(L, 1, 64, 2, 16)[1]
+    f = L.sana_linattn_fwd_block_causal
+    assert f(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 5, 1e-6, BF16, P_W, need, None) == INVALID
+    assert f(P_Q, P_K, P_V, None, 1, 64, 2, 32, 16, 1e-6, BF16, P_W, need, None) == INVALID
+    assert f(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, -1.0, BF16, P_W, need, None) == INVALID
+    assert f(P_Q + 8, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6, BF16, P_W, need, None) == ALIGNMENT
+    assert f(P_Q, P_K, P_V, P_Q + 64, 1, 64, 2, 32, 16, 1e-6, BF16, P_W, need, None) == INVALID
+    assert f(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6, BF16, P_W, need - 1, None) == WORKSPACE
+    assert f(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6, BF16, P_W + 16, need, None) == ALIGNMENT
+    assert f(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6, BF16, P_O, need, None) == INVALID
+    events = (ctypes.c_void_p * 3)(None, None, None)
+    assert L.sana_linattn_fwd_block_causal_profiled(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6,
+                                                    BF16, P_W, need, events, 3, None) == INVALID
