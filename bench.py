@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of ReLU linear self-attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op fwd|bwd]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--op fwd|bwd|block_causal] [--block L]
 
 A step is one full forward pass (the state reduction over token ranges into
 per-block partials, then the apply, which sums them) - or, with --op bwd, one
 full backward pass (the state reduction, the q pass that also reduces the
-state gradient, the k/v pass) - over one batch of synthetic input already
+state gradient, the k/v pass), or with --op block_causal one block-causal
+forward pass (per-block states, their prefix scan, the apply) - over one batch of synthetic input already
 resident in HBM. Prints one JSON line: tokens/s (B*N per step), the whole
 path's achieved HBM GB/s, a roofline record for the dominant kernel (its
 duration from HIP events recorded on the launch stream in a second timed
@@ -31,7 +33,9 @@ METRIC_BWD = "linear-attn bwd tokens/s + achieved HBM GB/s (% roofline), N=16384
 METRIC_BC = "block-causal linear-attn fwd tokens/s + achieved HBM GB/s (% roofline)"
 CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "traffic_latent_4096px.json"),
-                 "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json")}
+                 "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json"),
+                 "block_causal": os.path.join(ROOT, "profiles",
+                                              "traffic_block_causal_video_1m_tokens.json")}
 
 
 def parse():
@@ -74,15 +78,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str, op: str = "fwd"):
+def measured_traffic(kernel: str, workload: str, op: str = "fwd", block=None):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source."""
+    summary, or None when absent or taken on a different kernel source (or,
+    block-causal, a different block length)."""
     try:
         with open(TRAFFIC_FILES[op]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    if block is not None and rec.get("block") != block:
         return None
     k = rec.get("kernels", {}).get(kernel)
     if not k:
@@ -458,11 +465,17 @@ def run_block_causal(args, w):
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None},
+                     "traffic": measured_traffic(dominant, w.name, "block_causal", block)},
     }
     if args.copy_mib == 0:
         ceil = copy_ceiling(dev["q"].device)
         result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
+    else:  # counter calibration, outside every timed region
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
     if args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline_block_causal(w, x, block, args.cpu_seconds)
@@ -473,9 +486,12 @@ def main():
     args = parse()
     if args.summarize_counters:
         from relu_linear_attention_attn_amd import workloads as W
+        default = "video_1m_tokens" if args.op == "block_causal" else W.HEADLINE
         rec = summarize_counters(*args.summarize_counters, args.copy_mib or 256,
-                                 args.workload or W.HEADLINE)
+                                 args.workload or default)
         rec["op"] = args.op
+        if args.op == "block_causal":
+            rec["block"] = args.block
         print(json.dumps(rec, indent=1))
         return
     if args.gpus != 1:

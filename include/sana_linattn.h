@@ -46,7 +46,8 @@
  * Domain. B, N, H >= 1; d == 32 (other head widths return
  * SANA_ERR_UNSUPPORTED); B*N*H*d must fit in int64, every tensor must be
  * addressable (total bytes < 2^62) and B*ceil(H/2), the number of head pairs,
- * must be below 2^31 (one kernel grid covers them). eps must be finite and
+ * must be at most 2^22 (kernel grids over head pairs must stay within 2^32
+ * work-items). eps must be finite and
  * >= 0; with
  * eps = 0 a query row with phi(q_i) = 0 gives 0/0 = NaN, otherwise such a row
  * gives exactly 0. Tensor pointers must be 16-byte aligned

@@ -21,6 +21,10 @@ namespace {
 
 constexpr int64_t kMinReduceChunk = 256;       // tokens: 8 tiles per wave at 2 sub-streams
 constexpr int64_t kMinApplyChunk = 256;
+constexpr int64_t kChunkCostTokens = 64;       // a (unit, chunk) block's fixed cost, in tokens
+constexpr int64_t kMaxChunkRounds = 8;         // rounds the chunk search looks at
+constexpr int64_t kMaxUnits = int64_t(1) << 22;  // head pairs per call; also the largest
+                                                 // searched (unit, chunk) grid
 constexpr int64_t kWorkspaceBlocks = 4096;     // reduction blocks the workspace allows for
 constexpr int64_t kMaxReduceChunks = 64;
 constexpr int64_t kFusedMaxN = 1024;           // AUTO picks the fused kernel up to this N
@@ -64,11 +68,11 @@ sana_status_t check_shape(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
       __builtin_mul_overflow(t, d, &t) || __builtin_mul_overflow(t, item, &t) ||
       t >= (int64_t(1) << 62))
     return SANA_ERR_INVALID_ARG;
-  // head pairs index one grid dimension (every grid has at most
-  // max(units, co-resident blocks) blocks); the state and workspace sizes
-  // stay far below the tensor limit then
+  // head pairs: no grid has more blocks than max(kMaxUnits, 16 x the
+  // co-resident blocks), so every launch stays within 2^32 work-items; the
+  // state and workspace sizes stay far below the tensor limit then
   int64_t units = 0;
-  if (__builtin_mul_overflow(B, cdiv(H, kHeadsPerBlock), &units) || units > INT32_MAX)
+  if (__builtin_mul_overflow(B, cdiv(H, kHeadsPerBlock), &units) || units > kMaxUnits)
     return SANA_ERR_INVALID_ARG;
   if (tensor_bytes) *tensor_bytes = static_cast<size_t>(t);
   return SANA_OK;
@@ -147,6 +151,29 @@ const DeviceCaps& device_caps() {
 
 }  // namespace
 
+// Chunks per unit for a (unit, chunk) grid on `slots` co-resident blocks.
+// One round when the units fit it and fill at least 3/4 of the slots
+// (measured: the idle rest costs less than an extra round, since fewer
+// blocks each stream faster); otherwise the count that minimises the
+// modelled time, rounds of blocks times one block's tokens plus a fixed
+// per-block cost, so that a grid that would leave many slots idle is cut
+// into more, shorter chunks.
+int64_t grid_chunks(int64_t units, int64_t N, int64_t slots) {
+  const int64_t max_c = std::max<int64_t>(1, cdiv(N, kMinApplyChunk));
+  const int64_t one = clamp64(slots / units, 1, max_c);
+  if (units <= slots && 4 * units * cdiv(N, chunk_tokens(N, one)) >= 3 * slots) return one;
+  const int64_t last = std::min(max_c, kMaxChunkRounds * cdiv(slots, units));
+  int64_t best = 1, best_t = INT64_MAX;
+  for (int64_t c = 1; c <= last; ++c) {
+    const int64_t chunk = chunk_tokens(N, c);
+    const int64_t items = units * cdiv(N, chunk);
+    if (c > 1 && items > kMaxUnits) break;
+    const int64_t t = cdiv(items, slots) * (chunk + kChunkCostTokens);
+    if (t < best_t) best_t = t, best = c;
+  }
+  return best;
+}
+
 void fit_plan_to_device(Plan& p, int dtype) {
   const DeviceCaps& c = device_caps();
   const int dt = dtype == SANA_DTYPE_BF16 ? 1 : 0;
@@ -174,17 +201,15 @@ void fit_plan_to_device(Plan& p, int dtype) {
     p.red_chunk = chunk_tokens(p.N, rc);
     p.red_chunks = cdiv(p.N, p.red_chunk);
   }
-  // apply: (unit, chunk) grid of at most one round of co-resident blocks
-  // (measured: extra rounds cost more than idle slots in the one round)
-  int64_t ac = clamp64(acap / p.units, 1, std::max<int64_t>(1, cdiv(p.N, kMinApplyChunk)));
+  // apply and backward k/v pass: (unit, chunk) grids, each for its kernel's
+  // occupancy
+  int64_t ac = grid_chunks(p.units, p.N, acap);
 #ifdef SANA_TUNING
   if (const char* e = getenv("SANA_APP_CHUNKS")) ac = std::max<int64_t>(1, atoll(e));
 #endif
   p.app_chunk = chunk_tokens(p.N, ac);
   p.app_chunks = cdiv(p.N, p.app_chunk);
-  // backward k/v pass: the apply's rule with its own occupancy
-  const int64_t bcap = static_cast<int64_t>(c.cus) * c.occ_bwd_kv;
-  int64_t bc = clamp64(bcap / p.units, 1, std::max<int64_t>(1, cdiv(p.N, kMinApplyChunk)));
+  int64_t bc = grid_chunks(p.units, p.N, static_cast<int64_t>(c.cus) * c.occ_bwd_kv);
 #ifdef SANA_TUNING
   if (const char* e = getenv("SANA_BKV_CHUNKS")) bc = std::max<int64_t>(1, atoll(e));
 #endif
@@ -352,7 +377,7 @@ sana_status_t plan_block_causal(int64_t B, int64_t N, int64_t H, int64_t d, int6
   const int64_t F = N / L;
   // the blocks as batch items: B * F < 2^62 since B * N * H * d is
   if ((s = check_shape(B * F, L, H, d, dtype, nullptr)) != SANA_OK) return s;
-  if (scan_grid_blocks(B, cdiv(H, kHeadsPerBlock)) > INT32_MAX) return SANA_ERR_INVALID_ARG;
+  if (scan_grid_threads(B, cdiv(H, kHeadsPerBlock)) > UINT32_MAX) return SANA_ERR_INVALID_ARG;
   bc->p = make_plan(B * F, L, H);
   bc->F = F;
   bc->prefix_bytes = align_up(static_cast<size_t>(B * F * H) * kStateFloats * 4);

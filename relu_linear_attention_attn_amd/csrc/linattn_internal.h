@@ -81,7 +81,7 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
 // launch_apply.
 hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* partials,
                               const float* state, float* prefix, hipStream_t stream);
-int64_t scan_grid_blocks(int64_t B, int64_t pairs);  // grid size of that launch
+int64_t scan_grid_threads(int64_t B, int64_t pairs);  // work-items of that launch
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k,
                         const void* v, void* out, float eps, hipStream_t stream);
 

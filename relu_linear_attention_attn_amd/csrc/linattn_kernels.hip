@@ -1633,7 +1633,9 @@ hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* 
   return hipGetLastError();
 }
 
-int64_t scan_grid_blocks(int64_t B, int64_t pairs) { return B * pairs * kScanBlocksPerPair; }
+int64_t scan_grid_threads(int64_t B, int64_t pairs) {
+  return B * pairs * kScanBlocksPerPair * kScanThreads;
+}
 
 hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k, const void* v,
                         void* out, float eps, hipStream_t stream) {

@@ -74,10 +74,11 @@ def test_workspace_size_rules(L):
     assert ws_size(L, 1, 1 << 40, 1 << 16)[0] == INVALID   # exactly 2^62 bytes
     assert ws_size(L, 1, 1 << 40, 1 << 15)[0] == OK        # 2^61 bytes is addressable
     assert ws_size(L, 1 << 62, 1 << 62, 1)[0] == INVALID
-    # head pairs B*ceil(H/2) index one grid dimension: below 2^31
-    assert ws_size(L, 1 << 16, 1, (1 << 16) - 2)[0] == OK    # 2^31 - 2^16 pairs
-    assert ws_size(L, 1 << 16, 1, (1 << 16) + 1)[0] == INVALID
-    assert ws_size(L, 1 << 31, 1, 2)[0] == INVALID          # exactly 2^31 pairs
+    # head pairs B*ceil(H/2): at most 2^22 (grids stay within 2^32 work-items)
+    assert ws_size(L, 1 << 11, 1, 1 << 12)[0] == OK          # exactly 2^22 pairs
+    assert ws_size(L, 1 << 11, 1, (1 << 12) + 1)[0] == INVALID
+    assert ws_size(L, 1 << 22, 1, 2)[0] == OK
+    assert ws_size(L, (1 << 22) + 1, 1, 1)[0] == INVALID
     # the state does not grow with n: constant once N is large
     sizes = {ws_size(L, 2, n, 70)[1] for n in (1 << 16, 1 << 18, 1 << 20, 1 << 24)}
     assert len(sizes) == 1
@@ -243,6 +244,12 @@ def test_block_causal_workspace_and_errors(L):
     assert bcws(L, 1, 1000, 2, 0) == (INVALID, 0)
     assert bcws(L, 1, 1000, 2, -8) == (INVALID, 0)
     assert bcws(L, 1, 1000, 2, 1000, d=16) == (UNSUPPORTED, 0)
+    # blocks as batch items: B * (N / L) * ceil(H/2) at most 2^22 head pairs
+    assert bcws(L, 1, 1 << 22, 2, 1)[0] == OK
+    assert bcws(L, 2, 1 << 22, 2, 1)[0] == INVALID
+    # the prefix scan runs 2304 work-items per (b, head pair): within 2^32
+    assert bcws(L, 1 << 20, 16, 2, 16)[0] == OK
+    assert bcws(L, 1 << 21, 16, 2, 16)[0] == INVALID
     assert L.sana_linattn_block_causal_workspace_size(1, 16, 2, 32, 16, BF16, None) == INVALID
     need = bcws(L, 1, 64, 2, 16)[1]
     f = L.sana_linattn_fwd_block_causal
