@@ -52,6 +52,10 @@ def parse():
                     help="tokens per block for --op block_causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--input-sets", type=int, default=0,
+                    help="copies of the step's tensors the timed loops cycle through "
+                         "(0: enough that the other copies span 4x the Infinity Cache; "
+                         "1: rerun one set, warm cache)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run two plain device copies of this size (the "
@@ -143,6 +147,53 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, workload: 
             "calibration": {"copy_mib": copy_mib, "fetch_scale": f_scale,
                             "write_scale": w_scale},
             "kernels": kernels}
+
+
+CACHE_BYTES = 256 << 20   # MI355X Infinity Cache, the last level in front of HBM
+
+
+def n_input_sets(args, set_bytes: int) -> int:
+    """Copies of a step's tensors (inputs and outputs) that the timed loops
+    cycle through, step i on copy i % n: the other copies span at least 4x
+    the Infinity Cache, so no step finds its inputs cached by the step
+    before it (a rerun of one set would: Q, read with ordinary loads, stays
+    in the cache between steps at the smaller shapes)."""
+    if args.input_sets > 0:
+        return args.input_sets
+    return 1 + -(-4 * CACHE_BYTES // set_bytes)
+
+
+def device_sets(x, names, dtype: str, outs, n: int):
+    """n copies on the GPU: the host arrays `names` of x, plus `outs` fresh
+    tensors shaped like the first one."""
+    import numpy as np
+    import torch
+
+    def put(a):
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    base = {t: put(x[t]) for t in names}
+    sets = [base] + [{t: v.clone() for t, v in base.items()} for _ in range(n - 1)]
+    for d in sets:
+        for o in outs:
+            d[o] = torch.empty_like(base[names[0]])
+    torch.cuda.synchronize()
+    return sets
+
+
+def time_steps(step, steps: int, first: int = 0) -> float:
+    """Wall-clock ms per step over `steps` calls step(first + i), bracketed by
+    device synchronisation."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(first + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def copy_ceiling(device, mib: int = 1024, reps: int = 10):
@@ -278,18 +329,20 @@ def run_bwd(args, w):
         raise SystemExit("the backward pass is bf16 only")
     log(args, f"workload {w.name} {w.shape} bf16 backward: generating inputs")
     x = W.generate(w, grad=True)
-    dev = {t: torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).cuda() for t in "qkvg"}
-    grads = tuple(torch.empty_like(dev["q"]) for _ in range(3))
+    elem = w.B * w.N * w.H * w.d * w.itemsize
+    n_sets = n_input_sets(args, 7 * elem)
+    sets = device_sets(x, "qkvg", "bf16", ("dq", "dk", "dv"), n_sets)
     ws = torch.empty(R.bwd_workspace_size(w.B, w.N, w.H), dtype=torch.uint8, device="cuda")
 
-    def step(events=None):
-        R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps, grads=grads,
+    def step(i, events=None):
+        d = sets[i % n_sets]
+        R.backward(d["q"], d["k"], d["v"], d["g"], eps=w.eps, grads=(d["dq"], d["dk"], d["dv"]),
                    workspace=ws, events=events)
 
     names = ["reduce", "bwd_q", "bwd_kv"]
-    log(args, f"warmup {args.warmup} steps ({len(names)} kernels per step)")
-    for _ in range(args.warmup):
-        step()
+    log(args, f"warmup {args.warmup} steps ({len(names)} kernels per step, {n_sets} input sets)")
+    for i in range(args.warmup):
+        step(i)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
     for ev in events:
@@ -297,21 +350,13 @@ def run_bwd(args, w):
             e.record(stream)
     torch.cuda.synchronize()
     log(args, f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = time_steps(step, args.steps)
     log(args, f"timing {args.steps} steps with per-kernel events")
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
+    ms_events = time_steps(lambda i: step(i, events[i]), args.steps)
+    ms_one_set = time_steps(lambda i: step(0), args.steps)
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
     step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
-    elem = w.B * w.N * w.H * w.d * w.itemsize
     alg_bytes = {"reduce": 2 * elem, "bwd_q": 3 * elem, "bwd_kv": 4 * elem}
     total_bytes = sum(alg_bytes.values())
     dominant = max(per_kernel, key=per_kernel.get)
@@ -331,22 +376,23 @@ def run_bwd(args, w):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "op": "bwd", "B": w.B, "N": w.N, "H": w.H, "d": w.d,
-                   "D": w.D, "eps": w.eps},
+                   "D": w.D, "eps": w.eps, "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": total_bytes,
         "kernel_ms": per_kernel,
         "ms_per_step_with_kernel_events": ms_events,
+        "ms_per_step_one_input_set": ms_one_set,
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(dominant, w.name, "bwd")},
     }
     if args.copy_mib == 0:
-        ceil = copy_ceiling(dev["q"].device)
+        ceil = copy_ceiling(ws.device)
         result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
     else:
-        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=ws.device)
         dst = torch.empty_like(src)
         for _ in range(2):
             torch.bitwise_not(src, out=dst)
@@ -402,43 +448,34 @@ def run_block_causal(args, w):
               "generating inputs")
     from relu_linear_attention_attn_amd import workloads as W
     x = W.generate(w)
-    if w.dtype == "bf16":
-        dev = {t: torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).cuda() for t in "qkv"}
-    else:
-        dev = {t: torch.from_numpy(x[t]).cuda() for t in "qkv"}
-    out = torch.empty_like(dev["q"])
+    elem = w.B * w.N * w.H * w.d * w.itemsize
+    n_sets = n_input_sets(args, 4 * elem)
+    sets = device_sets(x, "qkv", w.dtype, ("out",), n_sets)
     dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
     ws = torch.empty(R.block_causal_workspace_size(w.B, w.N, w.H, block, w.d, dt),
                      dtype=torch.uint8, device="cuda")
 
-    def step(events=None):
-        R.forward_block_causal(dev["q"], dev["k"], dev["v"], block, eps=w.eps, out=out,
+    def step(i, events=None):
+        d = sets[i % n_sets]
+        R.forward_block_causal(d["q"], d["k"], d["v"], block, eps=w.eps, out=d["out"],
                                workspace=ws, events=events)
 
     names = ["reduce", "scan", "apply"]
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
     for ev in events:
         for e in ev:
             e.record(stream)
     torch.cuda.synchronize()
-    log(args, f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
+    log(args, f"timing {args.steps} steps ({n_sets} input sets)")
+    ms_per_step = time_steps(step, args.steps)
+    ms_events = time_steps(lambda i: step(i, events[i]), args.steps)
+    ms_one_set = time_steps(lambda i: step(0), args.steps)
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
     step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
-    elem = w.B * w.N * w.H * w.d * w.itemsize
     alg_bytes = {"reduce": 2 * elem, "apply": 2 * elem}
     dominant = max(alg_bytes, key=lambda n: per_kernel[n])
     achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-3) / 1e9
@@ -457,21 +494,22 @@ def run_block_causal(args, w):
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "op": "block_causal", "block": block, "B": w.B,
-                   "N": w.N, "H": w.H, "d": w.d, "D": w.D, "eps": w.eps},
+                   "N": w.N, "H": w.H, "d": w.d, "D": w.D, "eps": w.eps, "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "kernel_ms": per_kernel,
         "ms_per_step_with_kernel_events": ms_events,
+        "ms_per_step_one_input_set": ms_one_set,
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(dominant, w.name, "block_causal", block)},
     }
     if args.copy_mib == 0:
-        ceil = copy_ceiling(dev["q"].device)
+        ceil = copy_ceiling(ws.device)
         result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
     else:  # counter calibration, outside every timed region
-        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=ws.device)
         dst = torch.empty_like(src)
         for _ in range(2):
             torch.bitwise_not(src, out=dst)
@@ -522,57 +560,53 @@ def main():
     R.lib()
     log(args, f"workload {wname} {w.shape} {w.dtype}: generating inputs")
     x = W.generate(w)
-    if w.dtype == "bf16":
-        dev = {t: torch.from_numpy(x[t].view(np.int16)).view(torch.bfloat16).cuda() for t in "qkv"}
-    else:
-        dev = {t: torch.from_numpy(x[t]).cuda() for t in "qkv"}
-    out = torch.empty_like(dev["q"])
+    elem = w.B * w.N * w.H * w.d * w.itemsize
+    n_sets = n_input_sets(args, 4 * elem)
+    sets = device_sets(x, "qkv", w.dtype, ("out",), n_sets)
     dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
-    ws = R.binding.alloc_workspace(w.B, w.N, w.H, dt, dev["q"].device)
+    ws = R.binding.alloc_workspace(w.B, w.N, w.H, dt, sets[0]["q"].device)
     stream = torch.cuda.current_stream()
 
     def make_events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
-    # number of kernels of this variant
-    _, nk = R.forward_profiled(dev["q"], dev["k"], dev["v"], make_events(3), eps=w.eps, out=out,
-                               workspace=ws, variant=variant)
-    log(args, f"warmup {args.warmup} steps ({nk} kernels per step)")
-    for _ in range(args.warmup):
-        R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, out=out, workspace=ws, variant=variant)
+    def step(i):
+        d = sets[i % n_sets]
+        R.forward(d["q"], d["k"], d["v"], eps=w.eps, out=d["out"], workspace=ws, variant=variant)
+
+    def step_profiled(i, events):
+        d = sets[i % n_sets]
+        return R.forward_profiled(d["q"], d["k"], d["v"], events, eps=w.eps, out=d["out"],
+                                  workspace=ws, variant=variant)
+
+    _, nk = step_profiled(0, make_events(3))  # number of kernels of this variant
+    log(args, f"warmup {args.warmup} steps ({nk} kernels per step, {n_sets} input sets)")
+    for i in range(args.warmup):
+        step(i)
     events = [make_events(nk + 1) for _ in range(args.steps)]
     for ev in events:  # create the HIP events outside the timed region
         for e in ev:
             e.record(stream)
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` forward passes, bracketed by synchronize.
+    # Timed region: exactly `steps` forward passes, bracketed by synchronize,
+    # step i on input set i % n_sets.
     log(args, f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, out=out, workspace=ws, variant=variant)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = time_steps(step, args.steps)
 
     # The same steps again with a HIP event recorded on the launch stream
     # around every kernel (the library records them between its launches):
     # per-kernel durations. Event records add a few microseconds per step,
     # which is why `value` comes from the region above.
     log(args, f"timing {args.steps} steps with per-kernel events")
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        R.forward_profiled(dev["q"], dev["k"], dev["v"], events[i], eps=w.eps, out=out,
-                           workspace=ws, variant=variant)
-    torch.cuda.synchronize()
-    ms_events = (time.perf_counter() - t1) * 1e3 / args.steps
+    ms_events = time_steps(lambda i: step_profiled(i, events[i]), args.steps)
+    # and one input set rerun (warm Infinity Cache), for context only
+    ms_one_set = time_steps(lambda i: step(0), args.steps)
 
     step_ms = sorted(ev[0].elapsed_time(ev[nk]) for ev in events)
     names = ["fused"] if nk == 1 else ["reduce", "apply"]
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
-    elem = w.B * w.N * w.H * w.d * w.itemsize
     alg_bytes = {"reduce": 2 * elem, "apply": 2 * elem, "fused": 4 * elem}
     dominant = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dominant]
@@ -595,11 +629,12 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wname, "B": w.B, "N": w.N, "H": w.H, "d": w.d, "D": w.D,
-                   "variant": args.variant, "eps": w.eps},
+                   "variant": args.variant, "eps": w.eps, "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "kernel_ms": per_kernel,
         "ms_per_step_with_kernel_events": ms_events,
+        "ms_per_step_one_input_set": ms_one_set,
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
@@ -608,11 +643,11 @@ def main():
     if args.copy_mib == 0:
         # achievable-bandwidth reference, outside every timed region (not in
         # counter runs, whose calibration keys on the one bitwise_not below)
-        ceil = copy_ceiling(dev["q"].device)
+        ceil = copy_ceiling(ws.device)
         result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
     else:  # counter calibration, outside every timed region
         # a plain streaming kernel that reads and writes exactly copy_mib MiB
-        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev["q"].device)
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=ws.device)
         dst = torch.empty_like(src)
         for _ in range(2):
             torch.bitwise_not(src, out=dst)
