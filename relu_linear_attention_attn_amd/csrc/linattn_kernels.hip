@@ -67,11 +67,11 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
-// Streaming (nontemporal) accesses for data touched exactly once per call: K
-// and V in the reduction, the output in the apply. They keep the single-use
-// lines from displacing others in L2 and the Infinity Cache, and let output
-// lines go to HBM while the apply runs instead of being evicted, dirty, during
-// the next call's reads. (Q is read with ordinary loads: measured faster.)
+// Streaming (nontemporal) accesses for data touched exactly once per call:
+// the token tensors every kernel reads (Q, K, V, dOut) and writes (Out, dQ,
+// dK, dV). They keep the single-use lines from displacing others in L2 and
+// the Infinity Cache, and let output lines go to HBM while the kernel runs
+// instead of being evicted, dirty, during the next call's reads.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -365,7 +365,7 @@ __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int64_t n = n0 + 8 * h2;
-      qd[h2] = ld16(Q + base + (n < n_hi ? n : n_lo) * row + 8 * jl);
+      qd[h2] = ld16_stream(Q + base + (n < n_hi ? n : n_lo) * row + 8 * jl);
     }
   };
 #pragma unroll
@@ -1110,7 +1110,7 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
     for (int h2 = 0; h2 < 2; ++h2) {
       const int64_t n = n0 + 8 * h2;
       const int64_t off = base + (n < n_hi ? n : n_lo) * row + 8 * jl;
-      qd[h2] = ld16(Q + off);
+      qd[h2] = ld16_stream(Q + off);
       gd[h2] = ld16_stream(G + off);
     }
   };
@@ -1487,7 +1487,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_block_states_kernel(
 #define SANA_APP_U 2
 #endif
 #ifndef SANA_BWQ_U
-#define SANA_BWQ_U 2
+#define SANA_BWQ_U 1
 #endif
 #ifndef SANA_BWKV_U
 #define SANA_BWKV_U 1
