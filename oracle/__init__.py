@@ -23,3 +23,8 @@ from .linattn_block_causal import (  # noqa: F401,E402
     block_causal_from_inputs,
     masked_quadratic_fp64,
 )
+from .linattn_feature_maps import (  # noqa: F401,E402
+    FEATURE_MAPS,
+    linattn_fmap_fp64,
+    linattn_fmap_from_inputs,
+)
