@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "block_causal"],
                     help="forward pass (the headline), backward pass, or block-causal "
                          "forward (default workload: the 16-frame video, one block per frame)")
+    ap.add_argument("--fmap", default="relu", choices=["relu", "elu1", "cos"],
+                    help="feature map of the forward (other than relu: the split kernels)")
     ap.add_argument("--block", type=int, default=65536,
                     help="tokens per block for --op block_causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -234,12 +236,13 @@ def _blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(w, inputs, budget_s: float):
+def cpu_baseline(w, inputs, budget_s: float, fmap: str = "relu"):
     """Time the CPU oracle on whole heads of the workload until the budget is
     spent; report token-heads/s converted to tokens/s (all H heads of a
     token)."""
     import numpy as np
     import oracle.linattn as L
+    import oracle.linattn_feature_maps as FM
 
     threads = _blas_threads()
     # whole passes over the workload's (b, h) heads until the budget is spent
@@ -255,8 +258,12 @@ def cpu_baseline(w, inputs, budget_s: float):
                 v = L.to_f64(inputs["v"][b, :, h, :], w.dtype)
                 q = L.to_f64(inputs["q"][b, :, h, :], w.dtype)
                 tb = time.perf_counter()
-                kv, ks = L.kv_state(k, v)
-                L.apply_state(q, kv, ks, w.eps)
+                if fmap == "relu":
+                    kv, ks = L.kv_state(k, v)
+                    L.apply_state(q, kv, ks, w.eps)
+                else:
+                    kv, ks = FM.state_head(k, v, fmap)
+                    FM.apply_head(q, kv, ks, w.eps, fmap)
                 decode_s += tb - ta
                 done += 1
                 if time.perf_counter() - t0 >= budget_s:
@@ -572,10 +579,18 @@ def main():
 
     def step(i):
         d = sets[i % n_sets]
+        if args.fmap != "relu":
+            R.forward_fmap(d["q"], d["k"], d["v"], args.fmap, eps=w.eps, out=d["out"],
+                           workspace=ws)
+            return
         R.forward(d["q"], d["k"], d["v"], eps=w.eps, out=d["out"], workspace=ws, variant=variant)
 
     def step_profiled(i, events):
         d = sets[i % n_sets]
+        if args.fmap != "relu":
+            R.forward_fmap(d["q"], d["k"], d["v"], args.fmap, eps=w.eps, out=d["out"],
+                           workspace=ws, events=events[:3])
+            return None, 2
         return R.forward_profiled(d["q"], d["k"], d["v"], events, eps=w.eps, out=d["out"],
                                   workspace=ws, variant=variant)
 
@@ -611,7 +626,7 @@ def main():
     dominant = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dominant]
     achieved = alg_bytes[dominant] / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(dominant, wname)
+    traffic = measured_traffic(dominant, wname) if args.fmap == "relu" else None
     path_gbps = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = w.B * w.N / (ms_per_step * 1e-3)
 
@@ -629,7 +644,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wname, "B": w.B, "N": w.N, "H": w.H, "d": w.d, "D": w.D,
-                   "variant": args.variant, "eps": w.eps, "input_sets": n_sets},
+                   "variant": args.variant if args.fmap == "relu" else "split",
+                   "fmap": args.fmap, "eps": w.eps, "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "kernel_ms": per_kernel,
@@ -654,7 +670,7 @@ def main():
         torch.cuda.synchronize()
     if rank == 0 and args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, args.fmap)
     if rank == 0:
         print(json.dumps(result), flush=True)
 

@@ -90,6 +90,16 @@ typedef enum {
                               then apply; for short sequences */
 } sana_variant_t;
 
+/* Feature maps phi for sana_linattn_fwd_fmap (Sana course notes, "Linear
+ * Attention 的原理": ReLU, or another non-linear kernel such as ELU + 1 or
+ * cos, chosen by a kernel-function parameter). Applied element by element. */
+typedef enum {
+  SANA_FMAP_RELU = 0,  /* max(x, 0): the forward of sana_linattn_fwd */
+  SANA_FMAP_ELU1 = 1,  /* ELU(x) + 1, alpha = 1: x + 1 for x > 0, exp(x) otherwise */
+  SANA_FMAP_COS = 2    /* cos(x); can be negative, so den + eps can vanish or turn
+                          negative: the formula is evaluated as it stands */
+} sana_fmap_t;
+
 /*
  * Bytes of device workspace that sana_linattn_fwd, sana_linattn_fwd_variant
  * and sana_linattn_kv_state need for this shape. The size depends on
@@ -143,6 +153,24 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
                                         int dtype, int variant, void* workspace,
                                         size_t workspace_bytes, hipEvent_t* events,
                                         int n_events, int* n_kernels, hipStream_t stream);
+
+/*
+ * The forward pass with feature map `fmap` (sana_fmap_t) in place of ReLU:
+ * out_i = phi(q_i) KV / (phi(q_i) . ksum + eps) with KV = phi(K)^T V and
+ * ksum = phi(K)^T 1 (course notes, "Linear Attention 的原理", with the blog's
+ * normalised form, "核心架构"). Same tensors, layout, dtypes, workspace
+ * (sana_linattn_workspace_size), checks and errors as sana_linattn_fwd;
+ * always the SPLIT kernels. SANA_FMAP_RELU computes exactly what
+ * sana_linattn_fwd_variant(SPLIT) computes. In bf16, phi of ELU + 1 and cos
+ * is evaluated in fp32 and split into bf16 hi + lo parts for the MFMAs. An
+ * fmap outside sana_fmap_t returns SANA_ERR_UNSUPPORTED. events may be NULL;
+ * otherwise n_events >= 3 and events[0..2] are recorded before the state
+ * reduction, after it and after the apply (else SANA_ERR_INVALID_ARG).
+ */
+sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v, void* out,
+                                    int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                    int dtype, int fmap, void* workspace, size_t workspace_bytes,
+                                    hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
  * First half of the forward pass: the augmented state of every (b, h),

@@ -1,5 +1,5 @@
 """ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward (non-causal and
-block-causal) and backward.
+block-causal, ReLU or another feature map) and backward.
 
 The compute runs in hand-written HIP kernels behind a C ABI
 (``libsana_linattn.so``, declared in ``include/sana_linattn.h``); this package
@@ -9,6 +9,7 @@ loaded on first use and every call raises if it has not been built.
 from .binding import (  # noqa: F401
     DTYPE_BF16,
     DTYPE_F32,
+    FMAPS,
     VARIANT_AUTO,
     VARIANT_FUSED,
     VARIANT_SPLIT,
@@ -19,6 +20,7 @@ from .binding import (  # noqa: F401
     bwd_workspace_size,
     forward,
     forward_block_causal,
+    forward_fmap,
     forward_profiled,
     kv_state,
     lib,

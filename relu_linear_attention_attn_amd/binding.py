@@ -44,6 +44,7 @@ EXPORTS = (
     "sana_linattn_block_causal_workspace_size",
     "sana_linattn_fwd_block_causal",
     "sana_linattn_fwd_block_causal_profiled",
+    "sana_linattn_fwd_fmap",
     "sana_linattn_strerror",
     "sana_linattn_version",
 )
@@ -102,8 +103,11 @@ def lib() -> ctypes.CDLL:
             ctypes.c_float, ctypes.c_int, _vp, _sz, _vp]
         L.sana_linattn_fwd_block_causal_profiled.argtypes = [_vp] * 4 + [_i64] * 5 + [
             ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+        L.sana_linattn_fwd_fmap.argtypes = [_vp] * 4 + [_i64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
+            ctypes.c_int, _vp]
         for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
-                     "sana_linattn_fwd_block_causal_profiled"):
+                     "sana_linattn_fwd_block_causal_profiled", "sana_linattn_fwd_fmap"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
                      "sana_linattn_fwd", "sana_linattn_fwd_variant", "sana_linattn_fwd_profiled",
@@ -379,4 +383,41 @@ def forward_block_causal(q, k, v, block: int, eps: float = 1e-6, heads: Optional
         arr = (_vp * len(events))(*[e.cuda_event for e in events])
         _check(lib().sana_linattn_fwd_block_causal_profiled(*args, arr, len(events), _stream(q)),
                "sana_linattn_fwd_block_causal_profiled")
+    return out
+
+
+FMAPS = {"relu": 0, "elu1": 1, "cos": 2}
+
+
+def forward_fmap(q, k, v, fmap: str = "relu", eps: float = 1e-6, heads: Optional[int] = None,
+                 out=None, workspace=None, events=None):
+    """Forward pass with feature map fmap ("relu", "elu1" = ELU + 1, "cos")
+    in place of ReLU (split kernels). Same tensors as forward(); events:
+    optional list of 3 torch.cuda.Event recorded around the two kernels."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q)
+    _check_tensor(v, "v", q)
+    dt = _dtype_code(q)
+    if fmap not in FMAPS:
+        raise ValueError(f"unknown feature map {fmap!r}; one of {sorted(FMAPS)}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q)
+    if workspace is None:
+        workspace = alloc_workspace(B, N, H, dt, q.device)
+    arr, n = None, 0
+    if events is not None:
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event on first record
+                e.record()
+        arr, n = (_vp * len(events))(*[e.cuda_event for e in events]), len(events)
+    _check(lib().sana_linattn_fwd_fmap(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       B, N, H, d, float(eps), dt, FMAPS[fmap],
+                                       workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), arr, n,
+                                       _stream(q)),
+           "sana_linattn_fwd_fmap")
     return out

@@ -308,16 +308,23 @@ sana_status_t sana_linattn_state_size(int64_t B, int64_t H, int64_t d, size_t* b
 namespace sana {
 namespace {
 
+bool valid_fmap(int fmap) {
+  return fmap == SANA_FMAP_RELU || fmap == SANA_FMAP_ELU1 || fmap == SANA_FMAP_COS;
+}
+
 // The forward pass behind every fwd entry point. events (may be NULL) are
-// recorded before the first kernel and after each kernel.
+// recorded before the first kernel and after each kernel. Feature maps
+// other than ReLU run the split kernels only.
 sana_status_t forward(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t N, int64_t H, int64_t d, float eps, int dtype, int variant,
                       void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
-                      int* n_kernels, hipStream_t stream) {
+                      int* n_kernels, hipStream_t stream, int fmap = SANA_FMAP_RELU) {
   size_t tb = 0;
   sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
   if (s != SANA_OK) return s;
-  if (!valid_variant(variant)) return SANA_ERR_UNSUPPORTED;
+  if (!valid_variant(variant) || !valid_fmap(fmap)) return SANA_ERR_UNSUPPORTED;
+  if (fmap != SANA_FMAP_RELU && variant == SANA_VARIANT_FUSED) return SANA_ERR_UNSUPPORTED;
+  if (fmap != SANA_FMAP_RELU) variant = SANA_VARIANT_SPLIT;
   const Plan p = make_plan(B, N, H);
   const int run = resolve_variant(p, variant);
   const int nk = kernels_of(run);
@@ -349,12 +356,12 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   // split: bf16 hands the reduction's partials straight to the apply (no
   // fold at the end of the reduction); fp32 folds, then applies the state
   const bool bf16 = dtype == SANA_DTYPE_BF16;
-  if (launch_reduce(fp, dtype, !bf16, k, v, w.partials, w.state, w.ctl, next_epoch(), stream) !=
-      hipSuccess)
+  if (launch_reduce(fp, dtype, !bf16, k, v, w.partials, w.state, w.ctl, next_epoch(), stream,
+                    fmap) != hipSuccess)
     return SANA_ERR_HIP;
   if (!mark(1)) return SANA_ERR_HIP;
-  const hipError_t e = bf16 ? launch_apply_partials(fp, q, w.partials, out, eps, stream)
-                            : launch_apply(fp, dtype, q, w.state, out, eps, stream);
+  const hipError_t e = bf16 ? launch_apply_partials(fp, q, w.partials, out, eps, stream, fmap)
+                            : launch_apply(fp, dtype, q, w.state, out, eps, stream, fmap);
   if (e != hipSuccess) return SANA_ERR_HIP;
   return mark(2) ? SANA_OK : SANA_ERR_HIP;
 }
@@ -515,6 +522,14 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
   }
   return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, variant, workspace, workspace_bytes,
                        events, n_events, n_kernels, stream);
+}
+
+sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v, void* out,
+                                    int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                    int dtype, int fmap, void* workspace, size_t workspace_bytes,
+                                    hipEvent_t* events, int n_events, hipStream_t stream) {
+  return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, SANA_VARIANT_SPLIT, workspace,
+                       workspace_bytes, events, n_events, nullptr, stream, fmap);
 }
 
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,

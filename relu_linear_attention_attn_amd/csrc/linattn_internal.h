@@ -58,15 +58,16 @@ int block_waves(KernelKind kind, int dtype);  // waves per block
 // partials; with fold (always for fp32) the last block of each head pair
 // also folds them into `state`, without (bf16) the partials are the result
 // and launch_apply_partials sums them where it needs them.
+// fmap is the feature map (sana_fmap_t; the bf16 fold is ReLU only).
 hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, const void* v,
                          float* partials, float* state, unsigned long long* ctl,
-                         unsigned long long epoch, hipStream_t stream);
+                         unsigned long long epoch, hipStream_t stream, int fmap = 0);
 // Apply from a folded [B][H][d][d+1] state.
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state,
-                        void* out, float eps, hipStream_t stream);
+                        void* out, float eps, hipStream_t stream, int fmap = 0);
 // bf16 apply from the partials of launch_reduce(fold = false) with the same plan.
 hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
-                                 float eps, hipStream_t stream);
+                                 float eps, hipStream_t stream, int fmap = 0);
 // Backward (bf16). bwd_q runs on the reduction's grid: it sums the partials of
 // launch_reduce(fold = false) for the state, writes dq and writes [dS | dz]
 // partials on the same slots; bwd_kv sums those and writes dk and dv.

@@ -36,6 +36,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "linattn_internal.h"
 
 namespace sana {
@@ -88,6 +90,55 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
   return __builtin_bit_cast(u32x4, s);
 }
 
+// 8 packed bf16 -> fp32 (exact: a bf16 is the top half of a binary32).
+__device__ __forceinline__ void widen_bf16x8(u32x4 w, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+    x[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+  }
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x to ~2^-17 relative).
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const __bf16 h = (__bf16)x[m];
+    hi[m] = h;
+    lo[m] = (__bf16)(x[m] - (float)h);
+  }
+}
+
+// Feature maps phi, element by element in fp32 (the values of sana_fmap_t):
+// ReLU; ELU + 1 with alpha = 1 (x + 1 above 0, exp(x) at or below); cos.
+// ReLU of a bf16 is a bf16, and the bf16 kernels keep their packed ReLU
+// path for it; the other maps are not exact in bf16, so the bf16 kernels
+// split phi into bf16 hi + lo parts for the MFMAs.
+constexpr int kFmapRelu = 0, kFmapElu1 = 1, kFmapCos = 2;
+template <int Fm>
+__device__ __forceinline__ float fmap_f32(float x) {
+  if (Fm == kFmapElu1) return x > 0.0f ? x + 1.0f : expf(x);
+  if (Fm == kFmapCos) return cosf(x);
+  return fmaxf(x, 0.0f);
+}
+// The same maps from the hardware's transcendental instructions, for the
+// bf16 kernels, whose phi feeds bf16 hi + lo MFMA operands: exp(x) as
+// 2^(x log2 e) (v_exp_f32) and cos(x) as v_cos_f32 of the fraction of
+// x / (2 pi) in revolutions. Measured against double-precision exp and cos:
+// cos within 4e-7 absolute for |x| < 4 (3e-6 for |x| < 40, the argument
+// scaling's rounding), exp within 2e-6 relative on (-40, 0] - far below the
+// bf16 output rounding (2^-9). The library routines cost several times as
+// many instructions and made both kernels compute-bound (ELU + 1 forward at
+// 2 x 16384 x 70: 164 -> 133 us; cos: 195 -> 129 us).
+template <int Fm>
+__device__ __forceinline__ float fmap_hw(float x) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kInv2Pi = 0.15915494309189535f;
+  if (Fm == kFmapElu1) return x > 0.0f ? x + 1.0f : __builtin_amdgcn_exp2f(x * kLog2e);
+  if (Fm == kFmapCos) return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(x * kInv2Pi));
+  return fmaxf(x, 0.0f);
+}
+
 // -------------------------------------------------- line tiles in LDS
 //
 // A wave owns a head pair (h, h+1): per token that is one 128-byte line of
@@ -125,7 +176,7 @@ __device__ __forceinline__ void put(float* p, float x) {
 // exists (H odd leaves the last pair with one head: its lanes then read the
 // first head's half-line again, which stays inside the tensor, and the second
 // head's sums are discarded).
-template <int U>
+template <int U, int Fm = kFmapRelu>
 __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V,
                                                  int64_t row, int64_t base, int64_t n_lo,
@@ -143,8 +194,9 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
 
   // Loads are never predicated: a token outside the range (ragged tail, or a
   // tile past the end) reads row n_lo instead, which is always inside the
-  // tensor, and its k is zeroed when staged (phi(0) = 0 drops the token from
-  // both KV and ksum). Unconditional loads keep U tiles in flight.
+  // tensor, and its k is zeroed when staged (ReLU(0) = 0 drops the token from
+  // both KV and ksum; for the other maps phi itself is zeroed past the
+  // tile's `valid` tokens). Unconditional loads keep U tiles in flight.
   u32x4 kb[U][2], vb[U][2];
   auto issue = [&](int64_t i, u32x4 (&kd)[2], u32x4 (&vd)[2]) {
     const int64_t n0 = n_lo + (sub + i * S) * kTile + t0;
@@ -168,7 +220,11 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
       *reinterpret_cast<u32x4*>(slot + kTileBytes + o) = vin[h2];
     }
   };
-  auto consume = [&]() {
+  auto valid_in = [&](int64_t i) {
+    const int64_t left = n_hi - (n_lo + (sub + i * S) * kTile);
+    return static_cast<int>(left < kTile ? left : kTile);
+  };
+  auto consume = [&](int valid) {
     wave_lds_order();
     s16x8 a[2], bv[2];
 #pragma unroll
@@ -181,21 +237,43 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
       }
     }
     wave_lds_order();
+    if (Fm == kFmapRelu) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const s16x8 pk = __builtin_elementwise_max(a[hh], (s16x8)0);   // phi(k), packed
-      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
-                                                        __builtin_bit_cast(bf16x8, bv[hh]),
-                                                        acc[hh], 0, 0, 0);
-      // ksum: widen each bf16 exactly (it is the top half of a binary32) and add
-      const u32x4 w = __builtin_bit_cast(u32x4, pk);
-      float sum = 0.0f;
+      for (int hh = 0; hh < 2; ++hh) {
+        const s16x8 pk = __builtin_elementwise_max(a[hh], (s16x8)0);   // phi(k), packed
+        acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                          __builtin_bit_cast(bf16x8, bv[hh]),
+                                                          acc[hh], 0, 0, 0);
+        // ksum: widen each bf16 exactly (it is the top half of a binary32) and add
+        const u32x4 w = __builtin_bit_cast(u32x4, pk);
+        float sum = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sum += __builtin_bit_cast(float, w[e] << 16);
-        sum += __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+        for (int e = 0; e < 4; ++e) {
+          sum += __builtin_bit_cast(float, w[e] << 16);
+          sum += __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
+        }
+        ks[hh] += sum;
       }
-      ks[hh] += sum;
+    } else {
+      // phi in fp32, zero past the tile's valid tokens, split hi + lo
+      // against the exact v (two MFMAs); ksum from the fp32 values
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float x[8];
+        widen_bf16x8(__builtin_bit_cast(u32x4, a[hh]), x);
+        float sum = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          x[s] = rt + s < valid ? fmap_hw<Fm>(x[s]) : 0.0f;
+          sum += x[s];
+        }
+        bf16x8 hi, lo;
+        split_bf16x8(x, hi, lo);
+        const bf16x8 vb8 = __builtin_bit_cast(bf16x8, bv[hh]);
+        acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, vb8, acc[hh], 0, 0, 0);
+        acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, vb8, acc[hh], 0, 0, 0);
+        ks[hh] += sum;
+      }
     }
   };
   // Main loop: whole groups of U tiles and no branches inside, so the load
@@ -208,14 +286,14 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
       // refill kb[u], vb[u] only after their last use, so they keep their registers
       __builtin_amdgcn_sched_barrier(0);
       issue(i0 + u + U, kb[u], vb[u]);
-      consume();
+      consume(valid_in(i0 + u));
     }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (i0 + u < mine) {
       stage(i0 + u, kb[u], vb[u]);
-      consume();
+      consume(valid_in(i0 + u));
     }
   }
 }
@@ -317,14 +395,36 @@ __device__ __forceinline__ ApplyOperands make_apply_operands(const float* st) {
 // One head's 16-token output: phi(q) from the operand-layout piece, six
 // MFMAs, one reciprocal per token, bf16 rounding. Returns the lane's 8
 // output channels (one 16-byte piece) of token l%16.
+// For maps other than ReLU, phi(q) is split into hi + lo too and three
+// more MFMAs add the state's hi parts times phi(q)'s lo part.
+template <int Fm = kFmapRelu>
 __device__ __forceinline__ u32x4 apply_head(const ApplyOperands& op, u32x4 qpiece, float eps) {
-  const bf16x8 qv = __builtin_bit_cast(bf16x8, relu_bf16x8(qpiece));
-  f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qv, (f32x4)0, 0, 0, 0);
-  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, qv, a0, 0, 0, 0);
-  f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, qv, (f32x4)0, 0, 0, 0);
-  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, qv, a1, 0, 0, 0);
-  f32x4 ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, qv, (f32x4)0, 0, 0, 0);
-  ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_lo, qv, ad, 0, 0, 0);
+  f32x4 a0, a1, ad;
+  if (Fm == kFmapRelu) {
+    const bf16x8 qv = __builtin_bit_cast(bf16x8, relu_bf16x8(qpiece));
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qv, (f32x4)0, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, qv, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, qv, (f32x4)0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, qv, a1, 0, 0, 0);
+    ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, qv, (f32x4)0, 0, 0, 0);
+    ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_lo, qv, ad, 0, 0, 0);
+  } else {
+    float x[8];
+    widen_bf16x8(qpiece, x);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) x[m] = fmap_hw<Fm>(x[m]);
+    bf16x8 qh, ql;
+    split_bf16x8(x, qh, ql);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qh, (f32x4)0, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, qh, a0, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, ql, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, qh, (f32x4)0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, qh, a1, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, ql, a1, 0, 0, 0);
+    ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, qh, (f32x4)0, 0, 0, 0);
+    ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_lo, qh, ad, 0, 0, 0);
+    ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, ql, ad, 0, 0, 0);
+  }
   const float rinv = 1.0f / (ad[0] + eps);
   bf16x8 o;
 #pragma unroll
@@ -341,7 +441,7 @@ __device__ __forceinline__ u32x4 apply_head(const ApplyOperands& op, u32x4 qpiec
 // make_ops(op) fills the two heads' operands; it runs after the first U tiles'
 // loads are issued, so whatever it waits for (the state's loads, a block
 // barrier: every wave of the block calls it) overlaps those loads.
-template <int U, class MakeOps>
+template <int U, int Fm = kFmapRelu, class MakeOps>
 __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict__ Q,
                                                 unsigned short* __restrict__ Out,
                                                 MakeOps&& make_ops, float eps,
@@ -387,7 +487,8 @@ __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict
     wave_lds_order();
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
-      *reinterpret_cast<u32x4*>(slot + tile_off(col, hh * 4 + g)) = apply_head(op[hh], qp[hh], eps);
+      *reinterpret_cast<u32x4*>(slot + tile_off(col, hh * 4 + g)) =
+          apply_head<Fm>(op[hh], qp[hh], eps);
     wave_lds_order();
   };
   auto out_line = [&](int h2) {
@@ -463,7 +564,7 @@ __device__ __forceinline__ void combine_substreams(float (&regs)[R], float* xchg
 
 
 // Lane l owns state rows c = l/2, columns 16*(l%2) .. +15, and ksum[c].
-template <int U>
+template <int U, int Fm = kFmapRelu>
 __device__ __forceinline__ void reduce_f32_wave(const float* __restrict__ K,
                                                 const float* __restrict__ V, int64_t row,
                                                 int64_t base, int64_t n_lo, int64_t n_hi,
@@ -504,9 +605,13 @@ __device__ __forceinline__ void reduce_f32_wave(const float* __restrict__ K,
         }
         issue(i0 + u + U, kb[u], vb[u]);
         wave_lds_order();
+        const int64_t left = n_hi - (n_lo + (sub + (i0 + u) * S) * kTile);
+        const int valid = static_cast<int>(left < kTile ? left : kTile);
 #pragma unroll 4
         for (int t = 0; t < kTile; ++t) {
-          const float kc = fmaxf(ks[t * kD + c], 0.0f);
+          // staged k is 0 past the range: ReLU drops those tokens by itself
+          const float kc = Fm == kFmapRelu ? fmaxf(ks[t * kD + c], 0.0f)
+                                           : (t < valid ? fmap_f32<Fm>(ks[t * kD + c]) : 0.0f);
 #pragma unroll
           for (int m = 0; m < 16; ++m) acc[m] = __builtin_fmaf(kc, vs[t * kD + jh + m], acc[m]);
           acc[16] += kc;
@@ -540,6 +645,7 @@ __device__ __forceinline__ void stage_state_padded(float* dst, const float* st) 
 }
 
 // Lane l computes token n_lo + 64*tile + l of one head.
+template <int Fm = kFmapRelu>
 __device__ __forceinline__ void apply_f32_wave(const float* __restrict__ Q, float* __restrict__ Out,
                                                const float* stp /*padded LDS*/, float eps,
                                                int64_t row, int64_t base, int64_t n_lo,
@@ -557,7 +663,7 @@ __device__ __forceinline__ void apply_f32_wave(const float* __restrict__ Q, floa
       // mis-lowered by this compiler (it reads element 0)
       const f32x4 x = __builtin_bit_cast(f32x4, ld16(qp + 4 * c4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[4 * c4 + e] = fmaxf(x[e], 0.0f);
+      for (int e = 0; e < 4; ++e) q[4 * c4 + e] = fmap_f32<Fm>(x[e]);
     }
     float num[kD + 1];
 #pragma unroll
@@ -742,7 +848,7 @@ __device__ __forceinline__ SlotRange slot_range(int64_t unit, int64_t T, int64_t
 // unit's contributing blocks also folds the unit's partials, in order, into
 // the state; without, the partials are the result (the apply sums them).
 // Partials: [units][slots][2 heads][d][d+1].
-template <int S, int U, bool Fold>
+template <int S, int U, bool Fold, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
     float* __restrict__ partials, float* __restrict__ state, unsigned long long* __restrict__ ctl,
@@ -758,7 +864,8 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const int64_t base = (sg.b * N * H + sg.h) * kD;
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
-    reduce_pair_wave<U>(K, V, H * kD, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub], acc, ks);
+    reduce_pair_wave<U, Fm>(K, V, H * kD, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub],
+                            acc, ks);
     const SlotRange sr = slot_range(unit, T, Qb);
     float* part = partials + ((unit * slots) + (g - sr.first)) * 2 * kSF;
     block_sum_state<S, Fold>(acc, ks, lds.xchg, sub, part, sg.two);
@@ -769,7 +876,7 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
   }
 }
 
-template <int S, int U>
+template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
     const float* __restrict__ K, const float* __restrict__ V, float* __restrict__ partials,
     float* __restrict__ state, unsigned long long* __restrict__ ctl, unsigned long long epoch,
@@ -784,8 +891,8 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
 #pragma unroll
   for (int r = 0; r < 17; ++r) acc[r] = 0.0f;
   if (bc.active)
-    reduce_f32_wave<U>(K, V, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S,
-                       slot[threadIdx.x >> 6], acc);
+    reduce_f32_wave<U, Fm>(K, V, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S,
+                           slot[threadIdx.x >> 6], acc);
   combine_substreams<S, 17>(acc, xchg, bc.hh, bc.sub);
   if (bc.active && bc.sub == 0)
     store_state_from_f32<true>(partials + (bc.p * BH + bc.b * H + bc.h) * kSF, acc);
@@ -859,7 +966,7 @@ __device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
 // reduction, summed here in ascending slot order, as fold_partials does), else
 // 1 (a folded state). The block sums them once into LDS; each wave then builds
 // its MFMA operands from there.
-template <int S, int U>
+template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     const unsigned short* __restrict__ Q, const float* __restrict__ src, int64_t sb, int64_t sp,
     int64_t Qr, unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
@@ -885,12 +992,12 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
       op[0] = make_apply_operands(stf);
       op[1] = sg.two ? make_apply_operands(stf + kSF) : op[0];
     };
-    apply_pair_wave<U>(Q, Out, make_ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
-                       sg.n_hi, sub, S, sg.two, slots[sub]);
+    apply_pair_wave<U, Fm>(Q, Out, make_ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
+                           sg.n_hi, sub, S, sg.two, slots[sub]);
   }
 }
 
-template <int S>
+template <int S, int Fm = kFmapRelu>
 __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ state, float* __restrict__ Out,
     float eps, int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk) {
@@ -901,7 +1008,8 @@ __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
   if (!bc.active) return;
   const int64_t n_lo = bc.p * chunk;
   const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
-  apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S);
+  apply_f32_wave<Fm>(Q, Out, stp[bc.hh], eps, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi,
+                     bc.sub, S);
 }
 
 // One block per (b, head pair) over all N tokens: reduce into registers,
@@ -1031,24 +1139,7 @@ __device__ __forceinline__ void col_product(const ApplyOperands& op, bf16x8 px, 
   }
 }
 
-// 8 packed bf16 -> fp32 (exact: a bf16 is the top half of a binary32).
-__device__ __forceinline__ void widen_bf16x8(u32x4 w, float (&x)[8]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __builtin_bit_cast(float, w[e] << 16);
-    x[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xFFFF0000u);
-  }
-}
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x to ~2^-17 relative).
-__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const __bf16 h = (__bf16)x[m];
-    hi[m] = h;
-    lo[m] = (__bf16)(x[m] - (float)h);
-  }
-}
 
 // Sum over the 4 lanes that hold one token's 32 channels (l, l^16, l^32, l^48).
 // (gfx950's permlane16/32_swap builtins would avoid the LDS round trip, but
@@ -1514,27 +1605,43 @@ int64_t apply_xcds(const Plan& p) { return p.units >= kXcds ? kXcds : 1; }
 int64_t xcd_grid(int64_t items, int64_t X) { return X * ((items + X - 1) / X); }
 constexpr int kF32S = 2, kF32U = 2;
 
+// Runs f(std::integral_constant<int, Fm>) for the feature map fmap.
+template <class F>
+hipError_t with_fmap(int fmap, F&& f) {
+  switch (fmap) {
+    case kFmapRelu: return f(std::integral_constant<int, kFmapRelu>{});
+    case kFmapElu1: return f(std::integral_constant<int, kFmapElu1>{});
+    case kFmapCos: return f(std::integral_constant<int, kFmapCos>{});
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, const void* v,
                          float* partials, float* state, unsigned long long* ctl,
-                         unsigned long long epoch, hipStream_t stream) {
+                         unsigned long long epoch, hipStream_t stream, int fmap) {
   const int64_t BH = p.B * p.H;
-  if (dtype == 1) {
-    auto* kernel = fold ? reduce_bf16_kernel<kRedS, kRedU, true>
-                        : reduce_bf16_kernel<kRedS, kRedU, false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)p.red_blocks), dim3(64 * kRedS), 0, stream,
-                       static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
-                       partials, state, ctl, epoch, p.N, p.H, p.pairs, p.tiles, p.red_q,
-                       p.units * p.tiles, p.slots);
-  } else {
-    if (!fold) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U>), dim3((unsigned)(p.units * p.red_chunks)),
-                       dim3(128 * kF32S), 0, stream, static_cast<const float*>(k),
-                       static_cast<const float*>(v), partials, state, ctl, epoch, p.N, p.H,
-                       p.pairs, p.units, p.red_chunk, p.red_chunks, BH);
-  }
-  return hipGetLastError();
+  if (dtype == 1 && fold && fmap != kFmapRelu) return hipErrorInvalidValue;
+  if (dtype != 1 && !fold) return hipErrorInvalidValue;
+  return with_fmap(fmap, [&](auto fm) {
+    constexpr int Fm = decltype(fm)::value;
+    if (dtype == 1) {
+      auto* kernel = fold ? reduce_bf16_kernel<kRedS, kRedU, true, kFmapRelu>
+                          : reduce_bf16_kernel<kRedS, kRedU, false, Fm>;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)p.red_blocks), dim3(64 * kRedS), 0, stream,
+                         static_cast<const unsigned short*>(k),
+                         static_cast<const unsigned short*>(v), partials, state, ctl, epoch, p.N,
+                         p.H, p.pairs, p.tiles, p.red_q, p.units * p.tiles, p.slots);
+    } else {
+      hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U, Fm>),
+                         dim3((unsigned)(p.units * p.red_chunks)), dim3(128 * kF32S), 0, stream,
+                         static_cast<const float*>(k), static_cast<const float*>(v), partials,
+                         state, ctl, epoch, p.N, p.H, p.pairs, p.units, p.red_chunk, p.red_chunks,
+                         BH);
+    }
+    return hipGetLastError();
+  });
 }
 
 int block_waves(KernelKind kind, int dtype) {
@@ -1576,33 +1683,39 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
 }
 
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state, void* out,
-                        float eps, hipStream_t stream) {
-  if (dtype == 1) {
-    const int64_t X = apply_xcds(p);
-    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>),
-                       dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)),
-                       dim3(64 * kAppS), kApplyLdsPad, stream, static_cast<const unsigned short*>(q), state,
-                       p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
-                       eps, p.N, p.H, p.pairs, p.units, p.tiles, p.app_chunks,
-                       p.app_chunk / kTile, X);
-  } else {
-    hipLaunchKernelGGL((apply_f32_kernel<kF32S>), dim3((unsigned)(p.units * p.app_chunks)),
-                       dim3(128 * kF32S), 0, stream, static_cast<const float*>(q), state,
-                       static_cast<float*>(out), eps, p.N, p.H, p.pairs, p.units, p.app_chunk);
-  }
-  return hipGetLastError();
+                        float eps, hipStream_t stream, int fmap) {
+  return with_fmap(fmap, [&](auto fm) {
+    constexpr int Fm = decltype(fm)::value;
+    if (dtype == 1) {
+      const int64_t X = apply_xcds(p);
+      hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>),
+                         dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
+                         kApplyLdsPad, stream, static_cast<const unsigned short*>(q), state,
+                         p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
+                         eps, p.N, p.H, p.pairs, p.units, p.tiles, p.app_chunks,
+                         p.app_chunk / kTile, X);
+    } else {
+      hipLaunchKernelGGL((apply_f32_kernel<kF32S, Fm>), dim3((unsigned)(p.units * p.app_chunks)),
+                         dim3(128 * kF32S), 0, stream, static_cast<const float*>(q), state,
+                         static_cast<float*>(out), eps, p.N, p.H, p.pairs, p.units, p.app_chunk);
+    }
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
-                                 float eps, hipStream_t stream) {
+                                 float eps, hipStream_t stream, int fmap) {
   const int64_t sp = p.slots * 2 * kSF;
   const int64_t X = apply_xcds(p);
-  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU>),
-                     dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)),
-                     dim3(64 * kAppS), kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
-                     p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
-                     p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
-  return hipGetLastError();
+  return with_fmap(fmap, [&](auto fm) {
+    constexpr int Fm = decltype(fm)::value;
+    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>),
+                       dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
+                       kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
+                       p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
+                       p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,

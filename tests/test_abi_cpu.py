@@ -264,3 +264,28 @@ def test_block_causal_workspace_and_errors(L):
     events = (ctypes.c_void_p * 3)(None, None, None)
     assert L.sana_linattn_fwd_block_causal_profiled(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6,
                                                     BF16, P_W, need, events, 3, None) == INVALID
+
+
+def test_fwd_fmap_rejects_invalid_arguments(L):
+    need = ws_size(L, 1, 64, 2)[1]
+
+    def f(fmap=1, B=1, eps=1e-6, q=P_Q, o=P_O, ws=P_W, wsb=None, ev=None, nev=0, dt=BF16):
+        return L.sana_linattn_fwd_fmap(q, P_K, P_V, o, B, 64, 2, 32, eps, dt, fmap, ws,
+                                       need if wsb is None else wsb, ev, nev, None)
+
+    for fmap in (-1, 3, 99):
+        assert f(fmap=fmap) == UNSUPPORTED, fmap
+    for fmap in (0, 1, 2):
+        assert f(fmap=fmap, B=0) == INVALID
+        assert f(fmap=fmap, eps=-1.0) == INVALID
+        assert f(fmap=fmap, q=P_Q + 8) == ALIGNMENT
+        assert f(fmap=fmap, o=P_Q + 64) == INVALID
+        assert f(fmap=fmap, wsb=need - 1) == WORKSPACE
+        assert f(fmap=fmap, ws=None) == WORKSPACE
+        assert f(fmap=fmap, dt=5) == UNSUPPORTED
+    # events: at least 3, none NULL
+    two = (ctypes.c_void_p * 2)(1, 2)
+    assert f(ev=two, nev=2) == INVALID
+    holes = (ctypes.c_void_p * 3)(1, None, 3)
+    assert f(ev=holes, nev=3, eps=-1.0) == INVALID
+    assert f(ev=holes, nev=3) == INVALID
