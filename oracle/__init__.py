@@ -28,3 +28,9 @@ from .linattn_feature_maps import (  # noqa: F401,E402
     linattn_fmap_fp64,
     linattn_fmap_from_inputs,
 )
+from .linattn_qkv import (  # noqa: F401,E402
+    project,
+    qkv_attention_fp64,
+    qkv_attention_from_inputs,
+    round_bf16,
+)

@@ -29,7 +29,11 @@ workloads - rounded to bfloat16 with round-to-nearest-even):
     degrees of freedom is ``2g/nu``);
   * "rows made all-negative": exactly ``round(frac * B * N)`` token rows,
     chosen without replacement by ``PCG64(SeedSequence([seed, 3, 0]))``,
-    get every channel replaced by ``-|x|`` (the sign bit set).
+    get every channel replaced by ``-|x|`` (the sign bit set);
+  * the QKV projection's inputs (``projection_inputs``): token features x
+    ``[B][N][C]`` ~ N(0, 1) (tensor 5) and the weight ``[3 D][C]`` ~
+    N(0, 1/C) (tensor 6, so each projected channel has unit variance), drawn
+    in chunks of ``CHUNK_ROWS`` rows the same way, always bfloat16.
 """
 from __future__ import annotations
 
@@ -41,7 +45,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 CHUNK_ROWS = 8192
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "g": 4}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "g": 4, "x": 5, "w": 6}
 MASK_STREAM = 3
 
 
@@ -235,3 +239,36 @@ def custom(name: str, B: int, N: int, H: int, dtype: str = "bf16", seed: int = 1
            mask_tensor: Optional[str] = None, mask_frac: float = 0.0) -> Workload:
     """A workload of arbitrary shape with the same recipe (for ragged cases)."""
     return Workload(name, seed, B, N, H, d, dtype, eps, q, k, v, mask_tensor, mask_frac)
+
+
+def generate_matrix(seed: int, tid: int, rows: int, width: int, dist: Dist,
+                    workers: Optional[int] = None) -> np.ndarray:
+    """A [rows, width] bf16 matrix (uint16 bits) drawn chunk by chunk of
+    CHUNK_ROWS rows from PCG64(SeedSequence([seed, tid, chunk]))."""
+    out = np.empty((rows, width), dtype=np.uint16)
+
+    def one(c: int) -> None:
+        a = c * CHUNK_ROWS
+        b = min(a + CHUNK_ROWS, rows)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, c])))
+        out[a:b] = f32_to_bf16_bits(_draw(dist, rng, (b - a) * width).astype(np.float32)
+                                    .reshape(b - a, width))
+
+    chunks = range((rows + CHUNK_ROWS - 1) // CHUNK_ROWS)
+    nw = workers or _workers()
+    if nw == 1 or len(chunks) <= 1:
+        for c in chunks:
+            one(c)
+    else:
+        with ThreadPoolExecutor(nw) as ex:
+            list(ex.map(one, chunks))
+    return out
+
+
+def projection_inputs(w: Workload, C: int, workers: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the QKV projection for workload w's attention shape:
+    {'x': [B, N, C], 'w': [3 D, C]}, bf16 bits."""
+    x = generate_matrix(w.seed, TENSOR_IDS["x"], w.B * w.N, C, STD, workers)
+    wt = generate_matrix(w.seed, TENSOR_IDS["w"], 3 * w.D, C, Dist("normal", 0.0, C ** -0.5),
+                         workers)
+    return {"x": x.reshape(w.B, w.N, C), "w": wt}
