@@ -173,6 +173,42 @@ sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v,
                                     hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
+ * QKV projection with the attention state in its epilogue, then the forward
+ * pass (Sana review, section 4: the deployment kernels fold linear
+ * attention's ReLU(K)^T V into the QKV projection layer). bf16 only.
+ *
+ *   [q | k | v] = x W^T, each rounded to bf16 (round to nearest even), then
+ *   out = the forward of sana_linattn_fwd on (q, k, v).
+ *
+ * x:     [B][N][C] bf16 token features (device, read-only).
+ * w_qkv: [3 D][C] bf16 weight, D = H d, the [out][in] layout of a linear
+ *        layer without bias: rows 0..D-1 give q, D..2D-1 k, 2D..3D-1 v, head
+ *        h at rows h d .. h d + d - 1 of each (device, read-only).
+ * q:     [B][N][H][d] bf16, written: the projected, rounded q.
+ * out:   [B][N][H][d] bf16, written.
+ * k and v are never written to memory: the projection's blocks that compute
+ * a head pair's k and v columns reduce them to that pair's state over their
+ * 256 tokens (one fp32 partial state each, in the workspace), and the apply
+ * sums a pair's partials in fixed order. The result equals, up to fp32
+ * summation order, sana_linattn_fwd on the q, k, v an unfused bf16
+ * projection would store.
+ *
+ * Domain: d == 32; C >= 1 and C % 8 == 0 (else SANA_ERR_UNSUPPORTED for C);
+ * B, N, H as for sana_linattn_fwd; x, w_qkv, q, out 16-byte aligned;
+ * q and out must not overlap x, w_qkv, each other or the workspace. The
+ * workspace (256-byte aligned, >= sana_linattn_qkv_workspace_size) needs no
+ * clearing. events may be NULL; otherwise n_events >= 3 and events[0..2]
+ * are recorded before the projection, after it and after the apply.
+ * Checks run before any HIP call; a failed launch returns SANA_ERR_HIP.
+ */
+sana_status_t sana_linattn_qkv_workspace_size(int64_t B, int64_t N, int64_t C, int64_t H,
+                                              int64_t d, size_t* bytes);
+sana_status_t sana_linattn_qkv_fwd(const void* x, const void* w_qkv, void* q, void* out, int64_t B,
+                                   int64_t N, int64_t C, int64_t H, int64_t d, float eps,
+                                   void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                                   int n_events, hipStream_t stream);
+
+/*
  * First half of the forward pass: the augmented state of every (b, h),
  * written to `state` as fp32 [B][H][d][d+1] (see the layout note above), by
  * a split-N reduction over token chunks and a fixed-order sum of the chunk

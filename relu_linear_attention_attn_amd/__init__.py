@@ -1,5 +1,6 @@
 """ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward (non-causal and
-block-causal, ReLU or another feature map) and backward.
+block-causal, ReLU or another feature map; also from the QKV projection, with the
+state formed in the projection's epilogue) and backward.
 
 The compute runs in hand-written HIP kernels behind a C ABI
 (``libsana_linattn.so``, declared in ``include/sana_linattn.h``); this package
@@ -22,8 +23,10 @@ from .binding import (  # noqa: F401
     forward_block_causal,
     forward_fmap,
     forward_profiled,
+    forward_qkv,
     kv_state,
     lib,
+    qkv_workspace_size,
     state_size,
     strerror,
     workspace_size,

@@ -45,6 +45,8 @@ EXPORTS = (
     "sana_linattn_fwd_block_causal",
     "sana_linattn_fwd_block_causal_profiled",
     "sana_linattn_fwd_fmap",
+    "sana_linattn_qkv_workspace_size",
+    "sana_linattn_qkv_fwd",
     "sana_linattn_strerror",
     "sana_linattn_version",
 )
@@ -106,8 +108,12 @@ def lib() -> ctypes.CDLL:
         L.sana_linattn_fwd_fmap.argtypes = [_vp] * 4 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
             ctypes.c_int, _vp]
+        L.sana_linattn_qkv_workspace_size.argtypes = [_i64] * 5 + [ctypes.POINTER(_sz)]
+        L.sana_linattn_qkv_fwd.argtypes = [_vp] * 4 + [_i64] * 5 + [
+            ctypes.c_float, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
-                     "sana_linattn_fwd_block_causal_profiled", "sana_linattn_fwd_fmap"):
+                     "sana_linattn_fwd_block_causal_profiled", "sana_linattn_fwd_fmap",
+                     "sana_linattn_qkv_workspace_size", "sana_linattn_qkv_fwd"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
                      "sana_linattn_fwd", "sana_linattn_fwd_variant", "sana_linattn_fwd_profiled",
@@ -421,3 +427,50 @@ def forward_fmap(q, k, v, fmap: str = "relu", eps: float = 1e-6, heads: Optional
                                        _stream(q)),
            "sana_linattn_fwd_fmap")
     return out
+
+
+def qkv_workspace_size(B: int, N: int, C: int, H: int, d: int = HEAD_DIM) -> int:
+    n = _sz(0)
+    _check(lib().sana_linattn_qkv_workspace_size(B, N, C, H, d, ctypes.byref(n)),
+           "sana_linattn_qkv_workspace_size")
+    return n.value
+
+
+def forward_qkv(x, w_qkv, heads: int, eps: float = 1e-6, q=None, out=None, workspace=None,
+                events=None):
+    """QKV projection x W^T (bf16) with the attention state formed in the
+    projection's epilogue, then the forward pass. x: contiguous bf16 GPU
+    tensor (B, N, C); w_qkv: (3 D, C), D = heads * 32. Returns (q, out), both
+    (B, N, heads, 32). events: optional list of 3 torch.cuda.Event recorded
+    around the projection and the apply."""
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("x must be (B, N, C)")
+    B, N, C = (int(s) for s in x.shape)
+    H, d = int(heads), HEAD_DIM
+    _check_tensor(x, "x")
+    _check_tensor(w_qkv, "w_qkv")
+    if x.dtype != torch.bfloat16 or w_qkv.dtype != torch.bfloat16 or w_qkv.device != x.device:
+        raise ValueError("x and w_qkv must be bf16 tensors on one device")
+    if tuple(w_qkv.shape) != (3 * H * d, C):
+        raise ValueError(f"w_qkv must be ({3 * H * d}, {C})")
+    if q is None:
+        q = torch.empty((B, N, H, d), dtype=x.dtype, device=x.device)
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(qkv_workspace_size(B, N, C, H, d), 1), dtype=torch.uint8,
+                                device=x.device)
+    arr, n = None, 0
+    if events is not None:
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event on first record
+                e.record()
+        arr, n = (_vp * len(events))(*[e.cuda_event for e in events]), len(events)
+    _check(lib().sana_linattn_qkv_fwd(x.data_ptr(), w_qkv.data_ptr(), q.data_ptr(),
+                                      out.data_ptr(), B, N, C, H, d, float(eps),
+                                      workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), arr, n,
+                                      _stream(x)),
+           "sana_linattn_qkv_fwd")
+    return q, out

@@ -435,6 +435,86 @@ sana_status_t block_causal(const void* q, const void* k, const void* v, void* ou
   return mark(3) ? SANA_OK : SANA_ERR_HIP;
 }
 
+// QKV projection + attention (bf16): sizes and checks shared by the size
+// query and the call. x [B][N][C], w [3D][C], q and out [B][N][H][d].
+struct QkvPlan {
+  Plan p;                 // the attention's plan (apply grid)
+  int64_t J;              // 256-token tiles per batch item: partial slots per head pair
+  size_t x_bytes, w_bytes, t_bytes;  // x, w and q / out tensor bytes
+  size_t workspace_bytes; // the partial states
+};
+
+sana_status_t plan_qkv(int64_t B, int64_t N, int64_t C, int64_t H, int64_t d, QkvPlan* qp) {
+  size_t tb = 0;
+  sana_status_t s = check_shape(B, N, H, d, SANA_DTYPE_BF16, &tb);
+  if (s != SANA_OK) return s;
+  if (C < 1) return SANA_ERR_INVALID_ARG;
+  if (C % 8 != 0) return SANA_ERR_UNSUPPORTED;  // 16-byte pieces of x and w rows
+  int64_t xb = 0, wb = 0;
+  if (__builtin_mul_overflow(B * N, C, &xb) || __builtin_mul_overflow(xb, int64_t(2), &xb) ||
+      xb >= (int64_t(1) << 62))
+    return SANA_ERR_INVALID_ARG;
+  if (__builtin_mul_overflow(3 * H * d, C, &wb) || __builtin_mul_overflow(wb, int64_t(2), &wb) ||
+      wb >= (int64_t(1) << 62))
+    return SANA_ERR_INVALID_ARG;
+  // the projection's grid (256 threads a block) within 2^32 work-items
+  if (qkv_grid_blocks(B, N, H) > (int64_t(1) << 24)) return SANA_ERR_INVALID_ARG;
+  qp->p = make_plan(B, N, H);
+  qp->J = qkv_m_tiles(N);
+  qp->x_bytes = static_cast<size_t>(xb);
+  qp->w_bytes = static_cast<size_t>(wb);
+  qp->t_bytes = tb;
+  qp->workspace_bytes =
+      align_up(static_cast<size_t>(qp->p.units * qp->J) * 2 * kStateFloats * 4);
+  return SANA_OK;
+}
+
+constexpr int64_t kQkvGroupM = 4;  // M tiles per group of the projection's block order
+
+sana_status_t qkv_forward(const void* x, const void* w, void* q, void* out, int64_t B, int64_t N,
+                          int64_t C, int64_t H, int64_t d, float eps, void* workspace,
+                          size_t workspace_bytes, hipEvent_t* events, int n_events,
+                          hipStream_t stream) {
+  QkvPlan qp;
+  sana_status_t s = plan_qkv(B, N, C, H, d, &qp);
+  if (s != SANA_OK) return s;
+  if (events) {
+    if (n_events < 3) return SANA_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i)
+      if (!events[i]) return SANA_ERR_INVALID_ARG;
+  }
+  if (!x || !w || !q || !out) return SANA_ERR_INVALID_ARG;
+  if ((s = check_eps(eps)) != SANA_OK) return s;
+  if (misaligned(x) || misaligned(w) || misaligned(q) || misaligned(out)) return SANA_ERR_ALIGNMENT;
+  const size_t tb = qp.t_bytes;
+  if (overlaps(q, tb, x, qp.x_bytes) || overlaps(q, tb, w, qp.w_bytes) ||
+      overlaps(out, tb, x, qp.x_bytes) || overlaps(out, tb, w, qp.w_bytes) ||
+      overlaps(out, tb, q, tb))
+    return SANA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < qp.workspace_bytes) return SANA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
+  if (overlaps(workspace, qp.workspace_bytes, q, tb) ||
+      overlaps(workspace, qp.workspace_bytes, out, tb))
+    return SANA_ERR_INVALID_ARG;
+
+  (void)hipGetLastError();
+  Plan fp = qp.p;
+  fit_plan_to_device(fp, SANA_DTYPE_BF16);
+  int64_t gm = kQkvGroupM;
+#ifdef SANA_TUNING
+  if (const char* e = getenv("SANA_QKV_GM")) gm = std::max<int64_t>(1, atoll(e));
+#endif
+  float* partials = static_cast<float*>(workspace);
+  auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+  if (!mark(0)) return SANA_ERR_HIP;
+  if (launch_qkv_state(x, w, q, partials, B, N, C, H, gm, stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  if (!mark(1)) return SANA_ERR_HIP;
+  if (launch_apply_slots(fp, q, partials, qp.J, out, eps, stream) != hipSuccess)
+    return SANA_ERR_HIP;
+  return mark(2) ? SANA_OK : SANA_ERR_HIP;
+}
+
 // The backward pass (bf16): the forward state reduction (partials only),
 // bwd_q (dq and the [dS | dz] partials), bwd_kv (dk, dv). events (may be
 // NULL) are recorded before the first kernel and after each of the three.
@@ -640,6 +720,25 @@ sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* 
   if (!events) return SANA_ERR_INVALID_ARG;
   return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
                             workspace_bytes, events, n_events, stream);
+}
+
+sana_status_t sana_linattn_qkv_workspace_size(int64_t B, int64_t N, int64_t C, int64_t H,
+                                              int64_t d, size_t* bytes) {
+  if (!bytes) return SANA_ERR_INVALID_ARG;
+  *bytes = 0;
+  sana::QkvPlan qp;
+  const sana_status_t s = sana::plan_qkv(B, N, C, H, d, &qp);
+  if (s != SANA_OK) return s;
+  *bytes = qp.workspace_bytes;
+  return SANA_OK;
+}
+
+sana_status_t sana_linattn_qkv_fwd(const void* x, const void* w_qkv, void* q, void* out, int64_t B,
+                                   int64_t N, int64_t C, int64_t H, int64_t d, float eps,
+                                   void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                                   int n_events, hipStream_t stream) {
+  return sana::qkv_forward(x, w_qkv, q, out, B, N, C, H, d, eps, workspace, workspace_bytes,
+                           events, n_events, stream);
 }
 
 const char* sana_linattn_strerror(int status) {

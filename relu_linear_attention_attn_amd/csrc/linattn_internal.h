@@ -68,6 +68,17 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
 // bf16 apply from the partials of launch_reduce(fold = false) with the same plan.
 hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
                                  float eps, hipStream_t stream, int fmap = 0);
+// bf16 apply from `count` partial slots per unit laid out [units][count][2][d][d+1].
+hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partials, int64_t count,
+                              void* out, float eps, hipStream_t stream);
+// QKV projection with the state in its epilogue (qkv_kernels.hip): writes q
+// [B][N][H][d] bf16 and one partial state per (batch item, head pair,
+// 256-token tile), [B][pairs][qkv_m_tiles(N)][2][d][d+1] fp32. GM: M tiles
+// per group of the block order.
+int64_t qkv_m_tiles(int64_t N);
+int64_t qkv_grid_blocks(int64_t B, int64_t N, int64_t H);
+hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partials, int64_t B,
+                            int64_t N, int64_t C, int64_t H, int64_t GM, hipStream_t stream);
 // Backward (bf16). bwd_q runs on the reduction's grid: it sums the partials of
 // launch_reduce(fold = false) for the state, writes dq and writes [dS | dz]
 // partials on the same slots; bwd_kv sums those and writes dk and dv.

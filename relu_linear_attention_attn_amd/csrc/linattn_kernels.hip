@@ -963,8 +963,9 @@ __device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
 // The state of a unit is the sum of `count`
 // consecutive [2][d][d+1] slots at src + b * sb + p * sp (+ j * 2 * kSF),
 // count from slot_range(unit, T, Qr) when Qr > 0 (the partials of the
-// reduction, summed here in ascending slot order, as fold_partials does), else
-// 1 (a folded state). The block sums them once into LDS; each wave then builds
+// reduction, summed here in ascending slot order, as fold_partials does), -Qr
+// when Qr < 0 (a fixed number of slots per unit), else 1 (a folded state).
+// The block sums them once into LDS; each wave then builds
 // its MFMA operands from there.
 template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
@@ -982,7 +983,7 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
   const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
   {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
-    const int64_t count = Qr > 0 ? slot_range(unit, T, Qr).count : 1;
+    const int64_t count = Qr > 0 ? slot_range(unit, T, Qr).count : (Qr < 0 ? -Qr : 1);
     const f32x4* st = reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp);
     const int n4 = (sg.two ? 2 : 1) * kSF / 4;
     auto make_ops = [&](ApplyOperands (&op)[2]) {
@@ -1716,6 +1717,18 @@ hipError_t launch_apply_partials(const Plan& p, const void* q, const float* part
                        p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
     return hipGetLastError();
   });
+}
+
+hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partials, int64_t count,
+                              void* out, float eps, hipStream_t stream) {
+  const int64_t sp = count * 2 * kSF;
+  const int64_t X = apply_xcds(p);
+  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, kFmapRelu>),
+                     dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
+                     kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
+                     p.pairs * sp, sp, -count, static_cast<unsigned short*>(out), eps, p.N, p.H,
+                     p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,

@@ -289,3 +289,44 @@ def test_fwd_fmap_rejects_invalid_arguments(L):
     holes = (ctypes.c_void_p * 3)(1, None, 3)
     assert f(ev=holes, nev=3, eps=-1.0) == INVALID
     assert f(ev=holes, nev=3) == INVALID
+
+
+def qkv_ws(L, B, N, C, H, d=32):
+    n = ctypes.c_size_t(12345)
+    st = L.sana_linattn_qkv_workspace_size(B, N, C, H, d, ctypes.byref(n))
+    return st, n.value
+
+
+def test_qkv_workspace_and_errors(L):
+    st, n = qkv_ws(L, 2, 16384, 2240, 70)
+    # one [2][d][d+1] fp32 partial per (b, head pair, 256-token tile)
+    assert st == OK and n >= 2 * 35 * 64 * 2 * 32 * 33 * 4 and n % 256 == 0
+    assert qkv_ws(L, 1, 1, 8, 1)[0] == OK
+    assert qkv_ws(L, 1, 16, 12, 2) == (UNSUPPORTED, 0)     # C % 8 != 0
+    assert qkv_ws(L, 1, 16, 16, 2, d=64) == (UNSUPPORTED, 0)
+    assert qkv_ws(L, 0, 16, 16, 2) == (INVALID, 0)
+    assert qkv_ws(L, 1, 16, 0, 2) == (INVALID, 0)
+    assert qkv_ws(L, 1, 1 << 40, 1 << 20, 2)[0] == INVALID  # x beyond 2^62 bytes
+    assert L.sana_linattn_qkv_workspace_size(1, 16, 16, 2, 32, None) == INVALID
+    need = qkv_ws(L, 1, 64, 64, 2)[1]
+    P_X, P_WQ = P_Q, P_K   # placeholders: x 1*64*64*2 = 8 KB, w 192*64*2 = 24 KB
+
+    def f(x=P_X, w=P_WQ, q=P_V, o=P_O, C=64, eps=1e-6, ws=P_W, wsb=None, ev=None, nev=0):
+        return L.sana_linattn_qkv_fwd(x, w, q, o, 1, 64, C, 2, 32, eps, ws,
+                                      need if wsb is None else wsb, ev, nev, None)
+
+    assert f(C=60) == UNSUPPORTED
+    for name in ("x", "w", "q", "o"):
+        assert f(**{name: None}) == INVALID, name
+        assert f(**{name: A * 5 + 8}) == ALIGNMENT, name
+    assert f(eps=-1.0) == INVALID
+    assert f(o=P_V + 64) == INVALID            # out overlaps q
+    assert f(q=P_X + 4096) == INVALID          # q overlaps x
+    assert f(wsb=need - 1) == WORKSPACE
+    assert f(ws=None) == WORKSPACE
+    assert f(ws=P_W + 16) == ALIGNMENT
+    assert f(ws=P_O) == INVALID                # workspace overlaps out
+    two = (ctypes.c_void_p * 2)(1, 2)
+    assert f(ev=two, nev=2) == INVALID
+    holes = (ctypes.c_void_p * 3)(1, None, 3)
+    assert f(ev=holes, nev=3) == INVALID
