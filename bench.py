@@ -2,13 +2,15 @@
 """Throughput of ReLU linear self-attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op fwd|bwd|block_causal] [--block L]
+                    [--op fwd|bwd|block_causal|qkv] [--block L] [--fmap relu|elu1|cos]
 
 A step is one full forward pass (the state reduction over token ranges into
 per-block partials, then the apply, which sums them) - or, with --op bwd, one
 full backward pass (the state reduction, the q pass that also reduces the
-state gradient, the k/v pass), or with --op block_causal one block-causal
-forward pass (per-block states, their prefix scan, the apply) - over one batch of synthetic input already
+state gradient, the k/v pass), with --op block_causal one block-causal
+forward pass (per-block states, their prefix scan, the apply), or with --op
+qkv the QKV projection with the state in its epilogue, then the apply - over
+one batch of synthetic input already
 resident in HBM. Prints one JSON line: tokens/s (B*N per step), the whole
 path's achieved HBM GB/s, a roofline record for the dominant kernel (its
 duration from HIP events recorded on the launch stream in a second timed
@@ -31,6 +33,8 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E spec peak
 METRIC = "linear-attn fwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
 METRIC_BWD = "linear-attn bwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
 METRIC_BC = "block-causal linear-attn fwd tokens/s + achieved HBM GB/s (% roofline)"
+METRIC_QKV = "QKV projection + linear-attn fwd tokens/s (state in the projection epilogue)"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "traffic_latent_4096px.json"),
                  "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json"),
@@ -45,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "block_causal"],
+    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "block_causal", "qkv"],
                     help="forward pass (the headline), backward pass, or block-causal "
                          "forward (default workload: the 16-frame video, one block per frame)")
     ap.add_argument("--fmap", default="relu", choices=["relu", "elu1", "cos"],
@@ -114,7 +118,7 @@ def _counter_rows(folder: str):
 
 def _kernel_key(name: str) -> str:
     for k, v in (("reduce_bf16_kernel", "reduce"), ("apply_bf16_kernel", "apply"),
-                 ("scan_block_states_kernel", "scan"),
+                 ("scan_block_states_kernel", "scan"), ("qkv_state_kernel", "projection"),
                  ("fused_bf16_kernel", "fused"), ("bwd_q_bf16_kernel", "bwd_q"),
                  ("bwd_kv_bf16_kernel", "bwd_kv"), ("bitwise_not", "copy")):
         if k in name:
@@ -527,6 +531,131 @@ def run_block_causal(args, w):
     print(json.dumps(result), flush=True)
 
 
+def run_qkv(args, w, C: int = 2240):
+    """QKV projection with the state in its epilogue, then the apply: one
+    JSON line; the roofline record is the projection's (MFMA-bound)."""
+    import numpy as np
+    import torch
+
+    import relu_linear_attention_attn_amd as R
+    from relu_linear_attention_attn_amd import workloads as W
+
+    log(args, f"workload {w.name} {w.shape} bf16, projection width C={C}: generating inputs")
+    x = W.projection_inputs(w, C)
+    D = w.D
+    set_bytes = (w.B * w.N * C + 3 * D * C + 2 * w.B * w.N * D) * 2
+    n_sets = n_input_sets(args, set_bytes)
+
+    def put(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    base = {"x": put(x["x"]), "w": put(x["w"])}
+    sets = [base] + [{t: v.clone() for t, v in base.items()} for _ in range(n_sets - 1)]
+    for d in sets:
+        d["q"] = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device="cuda")
+        d["out"] = torch.empty_like(d["q"])
+    ws = torch.empty(R.qkv_workspace_size(w.B, w.N, C, w.H), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(i, events=None):
+        d = sets[i % n_sets]
+        R.forward_qkv(d["x"], d["w"], w.H, eps=w.eps, q=d["q"], out=d["out"], workspace=ws,
+                      events=events)
+
+    names = ["projection", "apply"]
+    log(args, f"warmup {args.warmup} steps ({n_sets} input sets)")
+    for i in range(args.warmup):
+        step(i)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+    torch.cuda.synchronize()
+    log(args, f"timing {args.steps} steps")
+    ms_per_step = time_steps(step, args.steps)
+    ms_events = time_steps(lambda i: step(i, events[i]), args.steps)
+    per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
+                  for j, n in enumerate(names)}
+    flops = 2.0 * w.B * w.N * C * 3 * D
+    achieved = flops / (per_kernel["projection"] * 1e-3) / 1e12
+
+    # context: the same step unfused, the library GEMM (torch.matmul) writing
+    # [q | k | v] rows, the three slices copied to [B][N][H][d], then the forward
+    d0 = sets[0]
+    y = torch.empty((w.B * w.N, 3 * D), dtype=torch.bfloat16, device="cuda")
+    kk, vv, qq, oo = (torch.empty_like(d0["q"]) for _ in range(4))
+    fws = R.binding.alloc_workspace(w.B, w.N, w.H, R.DTYPE_BF16, y.device)
+
+    def unfused(i):
+        d = sets[i % n_sets]
+        torch.matmul(d["x"].view(w.B * w.N, C), d["w"].t(), out=y)
+        yv = y.view(w.B, w.N, 3, D)
+        qq.view(w.B, w.N, D).copy_(yv[:, :, 0])
+        kk.view(w.B, w.N, D).copy_(yv[:, :, 1])
+        vv.view(w.B, w.N, D).copy_(yv[:, :, 2])
+        R.forward(qq, kk, vv, eps=w.eps, out=oo, workspace=fws)
+
+    for i in range(3):
+        unfused(i)
+    ms_unfused = time_steps(unfused, min(args.steps, 50))
+    result = {
+        "metric": METRIC_QKV,
+        "value": w.B * w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "qkv", "B": w.B, "N": w.N, "C": C, "H": w.H,
+                   "d": w.d, "D": D, "eps": w.eps, "input_sets": n_sets},
+        "kernel_ms": per_kernel,
+        "ms_per_step_with_kernel_events": ms_events,
+        "projection_tflops": achieved,
+        "unfused_library_gemm_ms_per_step": ms_unfused,
+        "roofline": {"bound": "mfma", "kernel": "projection", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+    }
+    if args.cpu_seconds > 0:
+        log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_qkv(w, x, C, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_qkv(w, inputs, C: int, budget_s: float):
+    """The oracle (float64 projection of one head's q, k, v rows, rounding,
+    attention) over whole heads until the budget is spent."""
+    import numpy as np
+    import oracle.linattn_qkv as QK
+
+    threads = _blas_threads()
+    D = w.D
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        h = done % w.H
+        rows = np.concatenate([np.arange(h * w.d, h * w.d + w.d) + i * D for i in range(3)])
+        QK.qkv_attention_from_inputs(inputs["x"], inputs["w"][rows], 1, w.eps, w.d)
+        done += 1
+    wall = time.perf_counter() - t0
+    return {
+        "value": done * w.B * w.N / wall / w.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} heads (all {w.B} x {w.N} tokens each: float64 projection of the "
+                  f"head's q, k, v rows from C={C}, bf16 rounding, attention) of {w.name}; "
+                  f"tokens/s = token-heads/s / H",
+        "seconds": wall,
+    }
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -562,6 +691,10 @@ def main():
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         R.lib()
         return run_block_causal(args, W.WORKLOADS[args.workload or "video_1m_tokens"])
+    if args.op == "qkv":
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        R.lib()
+        return run_qkv(args, w)
     variant = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}[args.variant]
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.lib()

@@ -193,7 +193,8 @@ sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v,
  * summation order, sana_linattn_fwd on the q, k, v an unfused bf16
  * projection would store.
  *
- * Domain: d == 32; C >= 1 and C % 8 == 0 (else SANA_ERR_UNSUPPORTED for C);
+ * Domain: d == 32; 1 <= C < 2^22 and C % 8 == 0 (C % 8 != 0 returns
+ * SANA_ERR_UNSUPPORTED);
  * B, N, H as for sana_linattn_fwd; x, w_qkv, q, out 16-byte aligned;
  * q and out must not overlap x, w_qkv, each other or the workspace. The
  * workspace (256-byte aligned, >= sana_linattn_qkv_workspace_size) needs no

@@ -450,6 +450,8 @@ sana_status_t plan_qkv(int64_t B, int64_t N, int64_t C, int64_t H, int64_t d, Qk
   if (s != SANA_OK) return s;
   if (C < 1) return SANA_ERR_INVALID_ARG;
   if (C % 8 != 0) return SANA_ERR_UNSUPPORTED;  // 16-byte pieces of x and w rows
+  // 32-bit offsets within a block's 256 x rows (and 64 W rows)
+  if (C >= (int64_t(1) << 22)) return SANA_ERR_INVALID_ARG;
   int64_t xb = 0, wb = 0;
   if (__builtin_mul_overflow(B * N, C, &xb) || __builtin_mul_overflow(xb, int64_t(2), &xb) ||
       xb >= (int64_t(1) << 62))

@@ -35,24 +35,27 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kSC = kStateCols;    // 33
 constexpr int kSF = kStateFloats;  // 1056
-constexpr int kBM = 256, kBN = 128, kBK = 64;
+constexpr int kBM = 256, kBN = 128, kBK = 32;
 constexpr int kThreads = 256;
-constexpr int kATile = kBM * kBK * 2;      // 32 KB
-constexpr int kBTile = kBN * kBK * 2;      // 16 KB
-constexpr int kStage = kATile + kBTile;    // 48 KB
-constexpr int kLds = 2 * kStage;           // 96 KB
+constexpr int kRow = kBK * 2;              // bytes per operand tile row (32 channels)
+constexpr int kATile = kBM * kRow;         // 16 KB
+constexpr int kBTile = kBN * kRow;         // 8 KB
+constexpr int kStage = kATile + kBTile;    // 24 KB
 constexpr int kKVPitch = kBM * 2 + 16;     // bytes per feature row of the transposed K|V tile
 constexpr int kXchg = kBN * kKVPitch;      // exchange area after the K|V tile
-static_assert(kXchg + 2 * 17 * kWave * 4 <= kLds, "epilogue fits the stages");
-static_assert(kBM * kBN * 2 <= kLds, "Q tile fits the stages");
+// LDS: two operand stages during the loop; the epilogue reuses it for the
+// transposed K|V tile and the wave exchange (the larger need, 74.5 KB), so
+// two blocks fit a CU's 160 KB.
+constexpr int kLds = kXchg + 2 * 17 * kWave * 4;
+static_assert(2 * kStage <= kLds && kBM * kBN * 2 <= kLds, "stages and Q tile fit");
 // dword 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle)
 constexpr int kRsrcFlags = 0x00020000;
 
-// Offset of 16-byte piece c of row r in a tile of 128-byte rows: the piece
-// index is XORed with (r / 2) % 8, so the 16 rows an MFMA fragment read
-// touches at once (two 128-byte rows per 256-byte bank sweep) fall on
+// Offset of 16-byte piece c (0..3) of row r in a tile of 64-byte rows: the
+// piece index is XORed with (r / 4) % 4, so the 16 rows an MFMA fragment
+// read touches at once (four 64-byte rows per 256-byte bank sweep) fall on
 // distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return (r << 7) + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int swz(int r, int c) { return (r << 6) + ((c ^ ((r >> 2) & 3)) << 4); }
 
 struct QkvArgs {
   const unsigned short* x;  // [B][N][C]
@@ -68,7 +71,7 @@ struct QkvArgs {
   int64_t items;  // MT * NT
 };
 
-__global__ __launch_bounds__(kThreads) void qkv_state_kernel(QkvArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void qkv_state_kernel(QkvArgs a) {
   __shared__ alignas(16) unsigned char lds[kLds];
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
@@ -120,43 +123,44 @@ __global__ __launch_bounds__(kThreads) void qkv_state_kernel(QkvArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(a.w + w1 * a.C), 0,
                                         static_cast<int>(rows_w1 * a.C * 2), kRsrcFlags)};
 
-  // Global loads of one step: x tile 8 pieces per thread, W tile 4, never
-  // predicated, so they stay in flight while the current step multiplies.
-  // Channels past C (a ragged last step) read the next row's and are zeroed
-  // when stored to LDS.
-  const int lr = tid >> 3, lc = tid & 7;
+  // Global loads of one step: x tile 4 pieces per thread (rows lr + 64 i),
+  // W tile 2 (row lr of each 64-row half), never predicated, so they stay
+  // in flight while the current step multiplies. Channels past C (a ragged
+  // last step) read the next row's and are zeroed when stored to LDS.
+  const int lr = tid >> 2, lc = tid & 3;
   const int off_a = (lr * static_cast<int>(a.C) + 8 * lc) * 2;
-  const int row_a = 32 * static_cast<int>(a.C) * 2;   // bytes between a thread's x rows
-  u32x4 ra[8], rb[4];
+  const int row_a = 64 * static_cast<int>(a.C) * 2;   // bytes between a thread's x rows
+  u32x4 ra[4], rb[2];
   auto load = [&](int64_t k0) {
     const int kb = static_cast<int>(k0) * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       ra[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, off_a + i * row_a + kb, 0, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
       rb[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw_src[i >> 1],
-                                                       off_a + (i & 1) * row_a + kb, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw_src[i], off_a + kb, 0, 0));
   };
-  auto store = [&](int s, int64_t k0) {
+  // store: a step inside C; store_tail: the ragged last step
+  auto store = [&](int s) {
     unsigned char* A = lds + s * kStage;
     unsigned char* Bt = A + kATile;
-    if (k0 + kBK <= a.C) {  // the whole step inside C (uniform)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(A + swz(lr + 32 * i, lc)) = ra[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(A + swz(lr + 64 * i, lc)) = ra[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(Bt + swz(lr + 32 * i, lc)) = rb[i];
-    } else {
-      const bool kin = k0 + 8 * lc < a.C;
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = rb[i];
+  };
+  auto store_tail = [&](int s, int k0) {
+    unsigned char* A = lds + s * kStage;
+    unsigned char* Bt = A + kATile;
+    const bool kin = k0 + 8 * lc < a.C;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(A + swz(lr + 32 * i, lc)) = kin ? ra[i] : (u32x4)0;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(A + swz(lr + 64 * i, lc)) = kin ? ra[i] : (u32x4)0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(Bt + swz(lr + 32 * i, lc)) = kin ? rb[i] : (u32x4)0;
-    }
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = kin ? rb[i] : (u32x4)0;
   };
 
   f32x16 acc[2][4];
@@ -193,17 +197,32 @@ __global__ __launch_bounds__(kThreads) void qkv_state_kernel(QkvArgs a) {
     }
   };
 
-  const int64_t nk = (a.C + kBK - 1) / kBK;
+  // Steps of kBK channels; the last one is ragged when C % kBK != 0 (its
+  // pieces past C are zeroed). Steps whose successor lies inside C run in
+  // the main loop with plain stores; the last one or two after it.
+  const int nk = static_cast<int>((a.C + kBK - 1) / kBK);
+  const int nfull = static_cast<int>(a.C / kBK);
   load(0);
-  store(0, 0);
+  if (nfull > 0) store(0); else store_tail(0, 0);
   __syncthreads();
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int s = static_cast<int>(ks & 1);
-    if (ks + 1 < nk) load((ks + 1) * kBK);
+  int step = 0;
+  for (; step + 1 < nfull; ++step) {
+    const int s = step & 1;
+    load((step + 1) * kBK);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the multiplies
     compute(s);
     // the next step's pieces are waited for only here, after the multiplies
     __builtin_amdgcn_sched_barrier(0);
-    if (ks + 1 < nk) store(s ^ 1, (ks + 1) * kBK);
+    store(s ^ 1);
+    __syncthreads();
+  }
+  for (; step < nk; ++step) {
+    const int s = step & 1;
+    if (step + 1 < nk) load((step + 1) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (step + 1 < nk) store_tail(s ^ 1, (step + 1) * kBK);
     __syncthreads();
   }
 

@@ -306,6 +306,7 @@ def test_qkv_workspace_and_errors(L):
     assert qkv_ws(L, 1, 16, 16, 2, d=64) == (UNSUPPORTED, 0)
     assert qkv_ws(L, 0, 16, 16, 2) == (INVALID, 0)
     assert qkv_ws(L, 1, 16, 0, 2) == (INVALID, 0)
+    assert qkv_ws(L, 1, 16, 1 << 22, 2) == (INVALID, 0)   # 32-bit offsets in a tile
     assert qkv_ws(L, 1, 1 << 40, 1 << 20, 2)[0] == INVALID  # x beyond 2^62 bytes
     assert L.sana_linattn_qkv_workspace_size(1, 16, 16, 2, 32, None) == INVALID
     need = qkv_ws(L, 1, 64, 64, 2)[1]
