@@ -10,15 +10,21 @@
 // tokens on MFMA, and write it as one partial state. The apply of the forward
 // pass then sums a head pair's partials and computes the output from Q.
 //
-// Tiles: 256 tokens x 128 output columns x 64 input channels per step, four
-// waves per block, wave w owning tokens 64w .. 64w + 63 of the tile (2 x 4
-// MFMA 32x32x16 bf16 tiles). Both operand tiles have the input channels
-// contiguous (x rows and W rows), so lane l of an MFMA reads row l % 32 and 8
-// consecutive channels: one 16-byte LDS read from a tile stored as 128-byte
-// rows whose 16-byte pieces are XOR-swizzled by the row. The
-// next step's tiles are loaded into registers while the current one is
-// multiplied, then stored to the other LDS stage (two stages, one barrier per
-// step).
+// Tiles: 256 tokens x 128 output columns x 32 input channels per step, four
+// waves per block and two blocks per CU, wave w owning tokens 64w .. 64w + 63
+// of the tile (2 x 4 MFMA 32x32x16 bf16 tiles). Both operand tiles have the
+// input channels contiguous (x rows and W rows), so lane l of an MFMA reads
+// row l % 32 and 8 consecutive channels: one 16-byte LDS read from a tile
+// stored as 64-byte rows whose 16-byte pieces are XOR-swizzled by the row.
+// Each step's pieces are loaded into registers two steps ahead (two register
+// sets) and stored to the other of two LDS stages between the two halves of
+// the current step's MFMAs; one barrier per step.
+//
+// Measured on the 4096px 1.6B block (x [2, 16384, 2240]): about 1000
+// TFLOP/s, 40% of the bf16 MFMA peak; the same loop with its MFMAs alone
+// runs at 1620 TFLOP/s, and the fragment reads from LDS (12 per 16 MFMAs)
+// account for most of the difference. Loading the stages with buffer loads
+// straight to LDS (three stages, no register staging) measured the same.
 #include <hip/hip_runtime.h>
 
 #include "linattn_internal.h"
@@ -124,26 +130,44 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_state_kernel(QkvArgs a) {
                                         static_cast<int>(rows_w1 * a.C * 2), kRsrcFlags)};
 
   // Global loads of one step: x tile 4 pieces per thread (rows lr + 64 i),
-  // W tile 2 (row lr of each 64-row half), never predicated, so they stay
-  // in flight while the current step multiplies. Channels past C (a ragged
-  // last step) read the next row's and are zeroed when stored to LDS.
+  // W tile 2 (row lr of each 64-row half), never predicated. Two register
+  // sets: step j's pieces go to set j % 2 and are issued two steps before
+  // they are stored to LDS, so they have two steps of multiplies to land.
+  // Channels past C (a ragged last step) read the next row's; they are
+  // overwritten with zeros in LDS after the store.
   const int lr = tid >> 2, lc = tid & 3;
   const int off_a = (lr * static_cast<int>(a.C) + 8 * lc) * 2;
   const int row_a = 64 * static_cast<int>(a.C) * 2;   // bytes between a thread's x rows
-  u32x4 ra[4], rb[2];
-  auto load = [&](int64_t k0) {
-    const int kb = static_cast<int>(k0) * 2;
+  u32x4 ra0[4], rb0[2], ra1[4], rb1[2];
+  // A step inside C passes its channel offset as the scalar offset, so the
+  // per-lane offsets are loop-invariant registers; the ragged last step adds
+  // it to the lane offsets, which the range check covers.
+  int vo_a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vo_a[i] = off_a + i * row_a;
+  auto load_full = [&](int k0, u32x4 (&ra)[4], u32x4 (&rb)[2]) {
+    const int kb = k0 * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       ra[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, off_a + i * row_a + kb, 0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo_a[i], kb, 0));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      rb[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw_src[i], off_a, kb, 0));
+  };
+  auto load = [&](int k0, u32x4 (&ra)[4], u32x4 (&rb)[2]) {
+    const int kb = k0 * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ra[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo_a[i] + kb, 0, 0));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       rb[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw_src[i], off_a + kb, 0, 0));
   };
-  // store: a step inside C; store_tail: the ragged last step
-  auto store = [&](int s) {
+  auto store_full = [&](int s, const u32x4 (&ra)[4], const u32x4 (&rb)[2]) {
     unsigned char* A = lds + s * kStage;
     unsigned char* Bt = A + kATile;
 #pragma unroll
@@ -151,16 +175,16 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_state_kernel(QkvArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = rb[i];
   };
-  auto store_tail = [&](int s, int k0) {
+  auto store = [&](int s, int k0, const u32x4 (&ra)[4], const u32x4 (&rb)[2]) {
     unsigned char* A = lds + s * kStage;
     unsigned char* Bt = A + kATile;
-    const bool kin = k0 + 8 * lc < a.C;
+    store_full(s, ra, rb);
+    if (k0 + kBK > a.C && k0 + 8 * lc >= a.C) {  // a ragged step: this thread's pieces past C
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(A + swz(lr + 64 * i, lc)) = kin ? ra[i] : (u32x4)0;
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(A + swz(lr + 64 * i, lc)) = (u32x4)0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = kin ? rb[i] : (u32x4)0;
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = (u32x4)0;
+    }
   };
 
   f32x16 acc[2][4];
@@ -171,59 +195,81 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_state_kernel(QkvArgs a) {
   // One step's multiplies. The fragments of sub-step kk + 1 are read from
   // LDS before the MFMAs of sub-step kk are issued, so their latency hides
   // behind those MFMAs.
-  auto compute = [&](int s) {
+  // One step's multiplies: both 16-channel sub-steps' fragments are read
+  // from stage s first, then the MFMAs of sub-step 0, then `between` (the
+  // main loop stores the next stage there, overlapping the MFMAs), then
+  // those of sub-step 1.
+  auto compute_with = [&](int s, auto&& between) {
     const unsigned char* A = lds + s * kStage;
     const unsigned char* Bt = A + kATile;
     bf16x8 af[2][2], bfr[2][4];
-    auto read = [&](int kk, bf16x8 (&fa)[2], bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
       const int c = 2 * kk + (l >> 5);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        fa[mi] = *reinterpret_cast<const bf16x8*>(A + swz(64 * wv + 32 * mi + (l & 31), c));
+        af[kk][mi] = *reinterpret_cast<const bf16x8*>(A + swz(64 * wv + 32 * mi + (l & 31), c));
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        fb[ni] = *reinterpret_cast<const bf16x8*>(Bt + swz(32 * ni + (l & 31), c));
-    };
-    read(0, af[0], bfr[0]);
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      if (kk + 1 < kBK / 16) read(kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+        bfr[kk][ni] = *reinterpret_cast<const bf16x8*>(Bt + swz(32 * ni + (l & 31), c));
+    }
+    auto mfmas = [&](int kk) {
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][mi], bfr[kk & 1][ni],
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][mi], bfr[kk][ni],
                                                                 acc[mi][ni], 0, 0, 0);
-    }
+    };
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
   };
+  auto compute = [&](int s) { compute_with(s, [] {}); };
 
-  // Steps of kBK channels; the last one is ragged when C % kBK != 0 (its
-  // pieces past C are zeroed). Steps whose successor lies inside C run in
-  // the main loop with plain stores; the last one or two after it.
+  // Steps of kBK channels (the last one ragged when C % kBK != 0). Step j
+  // multiplies stage j % 2 while step j + 2's pieces load into the register
+  // set step j's used; at its end step j + 1's set is stored to the other
+  // stage. The loop is unrolled by two so the sets stay fixed registers.
   const int nk = static_cast<int>((a.C + kBK - 1) / kBK);
-  const int nfull = static_cast<int>(a.C / kBK);
-  load(0);
-  if (nfull > 0) store(0); else store_tail(0, 0);
+  load(0, ra0, rb0);
+  if (nk > 1) load(kBK, ra1, rb1);
+  store(0, 0, ra0, rb0);
   __syncthreads();
-  int step = 0;
-  for (; step + 1 < nfull; ++step) {
-    const int s = step & 1;
-    load((step + 1) * kBK);
+  // Main loop: steps whose loads (two ahead) and stores are whole steps
+  // inside C, with nothing conditional, so the waits before the stores can
+  // count exactly the loads issued after them. Then the last steps with the
+  // general loads and stores.
+  const int nfull = static_cast<int>(a.C / kBK);
+  auto step_fast = [&](int kt, u32x4 (&ra_free)[4], u32x4 (&rb_free)[2],
+                       const u32x4 (&ra_next)[4], const u32x4 (&rb_next)[2]) {
+    load_full((kt + 2) * kBK, ra_free, rb_free);
     __builtin_amdgcn_sched_barrier(0);  // the loads go out before the multiplies
-    compute(s);
-    // the next step's pieces are waited for only here, after the multiplies
-    __builtin_amdgcn_sched_barrier(0);
-    store(s ^ 1);
+    // step kt + 1's pieces (loaded a step ago) are stored to the other stage
+    // between the two halves of the multiplies
+    compute_with(kt & 1, [&] { store_full((kt & 1) ^ 1, ra_next, rb_next); });
     __syncthreads();
+  };
+  auto step = [&](int kt, u32x4 (&ra_free)[4], u32x4 (&rb_free)[2], const u32x4 (&ra_next)[4],
+                  const u32x4 (&rb_next)[2]) {
+    const int s = kt & 1;
+    if (kt + 2 < nk) load((kt + 2) * kBK, ra_free, rb_free);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) store(s ^ 1, (kt + 1) * kBK, ra_next, rb_next);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 3 < nfull; kt += 2) {
+    step_fast(kt, ra0, rb0, ra1, rb1);
+    step_fast(kt + 1, ra1, rb1, ra0, rb0);
   }
-  for (; step < nk; ++step) {
-    const int s = step & 1;
-    if (step + 1 < nk) load((step + 1) * kBK);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s);
-    __builtin_amdgcn_sched_barrier(0);
-    if (step + 1 < nk) store_tail(s ^ 1, (step + 1) * kBK);
-    __syncthreads();
+  for (; kt < nk; kt += 2) {
+    step(kt, ra0, rb0, ra1, rb1);
+    if (kt + 1 < nk) step(kt + 1, ra1, rb1, ra0, rb0);
   }
 
   // acc[mi][ni] lane l, register r: token 64 wv + 32 mi + 8 (r / 4) + 4 (l / 32)
