@@ -669,9 +669,10 @@ def main():
         print(json.dumps(rec, indent=1))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the state reduction would shard over heads or tokens, see the "
-                          "design notes)"}), flush=True)
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                          "(across GPUs the attention would shard over heads, or over "
+                          "tokens with one all-reduce of the state, which is not "
+                          "implemented)"}), flush=True)
         sys.exit(2)
 
     import numpy as np

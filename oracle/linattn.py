@@ -1,7 +1,7 @@
 """Plain CPU float64 oracle for Sana's ReLU linear self-attention (forward).
 
 TEST INFRASTRUCTURE ONLY. Nothing in the library imports this module; only
-the tests, the graft smoke check and the benchmark's CPU-baseline leg do.
+the tests, the smoke check and the benchmark's CPU-baseline leg do.
 It shares no code with the HIP path: it decodes bfloat16 itself and uses
 nothing but NumPy.
 
@@ -24,7 +24,7 @@ Sources (the web pages on Sana):
     Linear DiT Design", "선형 어텐션 블럭": ReLU linear attention, the shared
     terms (a) and (b) computed once and reused by every query, O(N).
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings where the pages are silent:
   * eps is on no page. It is added to the denominator, outside the dot
     product: den + eps (not max(den, eps)).
   * d is the per-head width; heads never interact. Batches never interact.

@@ -7,7 +7,7 @@ the HIP path and uses nothing but NumPy (and the forward oracle's decoding).
 Source: the Linear-DiT 4K blog, section "技术演进", says SANA-Video extends
 Sana's linear attention to Block Causal Linear Attention (with a causal
 Mix-FFN) for video generation; no page gives its formula. Reading taken
-(listed in the design notes): the n tokens of a batch item form consecutive
+where the page is silent: the n tokens of a batch item form consecutive
 blocks of L tokens (a video frame is such a block; the last block may be
 shorter); a query in block c attends to every key in blocks 0..c, in its own
 block as much as in the earlier ones. Per (b, h), with the forward's

@@ -29,7 +29,7 @@ Attention 的原理"; Linear-DiT 4K blog, "核心架构"; Sana paper review, sec
 which needs these gradients; no page writes them out, so they are derived
 here from the forward definition.
 
-Readings (each listed in the design notes):
+Readings where the pages are silent:
   * The derivative of ReLU at exactly 0 is taken as 0 (the gradient passes
     only where x > 0), the usual subgradient choice.
   * eps is a constant (no gradient).

@@ -21,7 +21,7 @@ with one of these feature maps, applied element by element:
           alpha = 1, its usual form; the notes name the function only)
   "cos"   phi(x) = cos(x)
 
-Readings (listed in the design notes): ELU's alpha is 1; cos is applied to
+Readings where the notes are silent: ELU's alpha is 1; cos is applied to
 each channel as it stands (no reweighting, no scaling); eps is added as in
 the forward. With cos, phi can be negative, so den can be 0 or negative:
 the formula is evaluated as it stands (no clamp), and a row whose den + eps

@@ -18,7 +18,7 @@ attention is the forward of oracle/linattn.py.
   q, k, v rounded to bf16        (the projection's output type)
   out = forward(q, k, v, eps)
 
-Readings (listed in the design notes): the weight has the [out][in] layout
+Readings where the review is silent: the weight has the [out][in] layout
 of a linear layer with no bias (the pages name none); q, k and v are rounded
 to bfloat16, round-to-nearest-even, as a bf16 projection would store them,
 so the fused kernel computes what the unfused bf16 pipeline computes.

@@ -1,7 +1,7 @@
 """GPU parity of the backward pass: dq, dk, dv from the HIP path against the
 CPU float64 backward oracle, element by element, on the same seeded bits.
 
-Tolerance, per gradient tensor (written here; derived in the design notes):
+Tolerance, per gradient tensor:
 
     ||got - ref||_2  <= 5e-3 * ||ref||_2  + 1e-5 * ||scale||_2
     max |got - ref|  <= 1e-2 * max |ref|  + 1e-5 * max |scale|

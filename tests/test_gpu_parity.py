@@ -1,8 +1,13 @@
 """GPU parity: the HIP path against the CPU float64 oracle, element by element,
 through the C ABI (ctypes binding), on the same seeded input bits.
 
-Tolerances (written here, derived in the design notes): bf16 max-abs <= 1e-2
-and rel-L2 <= 5e-3; fp32 rel-L2 <= 1e-5 and max-abs <= 1e-5 * max|ref|.
+Tolerances: bf16 max-abs <= 1e-2 and rel-L2 <= 5e-3; fp32 rel-L2 <= 1e-5 and
+max-abs <= 1e-5 * max|ref|. The bf16 output is rounded once from fp32 (a
+half-ulp is 2^-9 relative, about 1.1e-3 in rel-L2 for uniform rounding
+errors), the fp32 state sum and the hi/lo-split products add less than
+1e-5, and max-abs 1e-2 holds while |out| < 4 (the half-ulp is 0.0078 in
+[2, 4)), which convex averages of N(0, 1) values keep. fp32 products and sums
+round at 2^-24 per operation over at most 2 * 32 + log2 N terms.
 """
 import numpy as np
 import pytest
