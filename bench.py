@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--op fwd|bwd|block_causal|qkv] [--block L] [--fmap relu|elu1|cos]
+                    [--layout contiguous|packed]
 
 A step is one full forward pass (the state reduction over token ranges into
 per-block partials, then the apply, which sums them) - or, with --op bwd, one
@@ -54,6 +55,9 @@ def parse():
                          "forward (default workload: the 16-frame video, one block per frame)")
     ap.add_argument("--fmap", default="relu", choices=["relu", "elu1", "cos"],
                     help="feature map of the forward (other than relu: the split kernels)")
+    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "packed"],
+                    help="forward inputs as three [B][N][H][d] tensors, or read in place "
+                         "from one packed [B][N][3][H][d] projection output (strided entry)")
     ap.add_argument("--block", type=int, default=65536,
                     help="tokens per block for --op block_causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -704,6 +708,14 @@ def main():
     elem = w.B * w.N * w.H * w.d * w.itemsize
     n_sets = n_input_sets(args, 4 * elem)
     sets = device_sets(x, "qkv", w.dtype, ("out",), n_sets)
+    if args.layout == "packed":
+        # q, k, v side by side per token in one [B][N][3 D] buffer per set,
+        # as a fused QKV linear layer writes them; the forward reads them in place
+        for d in sets:
+            buf = torch.cat([d[t].view(w.B, w.N, w.D) for t in "qkv"], dim=2)
+            for i, t in enumerate("qkv"):
+                d[t] = buf[:, :, i * w.D:(i + 1) * w.D].view(w.B, w.N, w.H, w.d)
+        torch.cuda.synchronize()
     dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
     ws = R.binding.alloc_workspace(w.B, w.N, w.H, dt, sets[0]["q"].device)
     stream = torch.cuda.current_stream()
@@ -713,6 +725,10 @@ def main():
 
     def step(i):
         d = sets[i % n_sets]
+        if args.layout == "packed":
+            R.forward_strided(d["q"], d["k"], d["v"], args.fmap, eps=w.eps, out=d["out"],
+                              workspace=ws)
+            return
         if args.fmap != "relu":
             R.forward_fmap(d["q"], d["k"], d["v"], args.fmap, eps=w.eps, out=d["out"],
                            workspace=ws)
@@ -721,6 +737,10 @@ def main():
 
     def step_profiled(i, events):
         d = sets[i % n_sets]
+        if args.layout == "packed":
+            R.forward_strided(d["q"], d["k"], d["v"], args.fmap, eps=w.eps, out=d["out"],
+                              workspace=ws, events=events[:3])
+            return None, 2
         if args.fmap != "relu":
             R.forward_fmap(d["q"], d["k"], d["v"], args.fmap, eps=w.eps, out=d["out"],
                            workspace=ws, events=events[:3])
@@ -760,7 +780,8 @@ def main():
     dominant = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dominant]
     achieved = alg_bytes[dominant] / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(dominant, wname) if args.fmap == "relu" else None
+    traffic = (measured_traffic(dominant, wname)
+               if args.fmap == "relu" and args.layout == "contiguous" else None)
     path_gbps = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = w.B * w.N / (ms_per_step * 1e-3)
 
@@ -778,8 +799,10 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wname, "B": w.B, "N": w.N, "H": w.H, "d": w.d, "D": w.D,
-                   "variant": args.variant if args.fmap == "relu" else "split",
-                   "fmap": args.fmap, "eps": w.eps, "input_sets": n_sets},
+                   "variant": (args.variant if args.fmap == "relu" and args.layout == "contiguous"
+                               else "split"),
+                   "fmap": args.fmap, "layout": args.layout, "eps": w.eps,
+                   "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "kernel_ms": per_kernel,

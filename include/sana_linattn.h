@@ -173,6 +173,30 @@ sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v,
                                     hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
+ * The forward pass of sana_linattn_fwd_fmap on q, k and v read with a token
+ * stride: element (b, n, h, c) of each is at index (b N + n) ld + h d + c
+ * from its pointer. This reads the output of one fused QKV linear layer in
+ * place (Sana review, section 4, projection and attention as one unit):
+ * for a [B][N][3][H][d] tensor qkv, pass q = qkv, k = qkv + H d,
+ * v = qkv + 2 H d and ld = 3 H d; ld = H d is the contiguous layout of
+ * sana_linattn_fwd. out stays contiguous [B][N][H][d].
+ *
+ * ld: elements, >= H d (else SANA_ERR_INVALID_ARG); ld * element size must
+ * be a multiple of 16 bytes (else SANA_ERR_ALIGNMENT), so every token row
+ * stays 16-byte aligned. q, k and v may overlap each other (they are only
+ * read); out must not overlap the (B N - 1) ld + H d elements any of them
+ * spans, nor the workspace. Workspace (sana_linattn_workspace_size with the
+ * same B, N, H, d, dtype), dtypes, fmap, events and the other checks and
+ * errors as sana_linattn_fwd_fmap; always the SPLIT kernels. The result is
+ * bitwise that of sana_linattn_fwd_fmap on contiguous copies of q, k, v.
+ */
+sana_status_t sana_linattn_fwd_strided(const void* q, const void* k, const void* v, int64_t ld,
+                                       void* out, int64_t B, int64_t N, int64_t H, int64_t d,
+                                       float eps, int dtype, int fmap, void* workspace,
+                                       size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                       hipStream_t stream);
+
+/*
  * QKV projection with the attention state in its epilogue, then the forward
  * pass (Sana review, section 4: the deployment kernels fold linear
  * attention's ReLU(K)^T V into the QKV projection layer). bf16 only.

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     forward_fmap,
     forward_profiled,
     forward_qkv,
+    forward_strided,
     kv_state,
     lib,
     qkv_workspace_size,

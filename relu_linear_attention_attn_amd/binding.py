@@ -45,6 +45,7 @@ EXPORTS = (
     "sana_linattn_fwd_block_causal",
     "sana_linattn_fwd_block_causal_profiled",
     "sana_linattn_fwd_fmap",
+    "sana_linattn_fwd_strided",
     "sana_linattn_qkv_workspace_size",
     "sana_linattn_qkv_fwd",
     "sana_linattn_strerror",
@@ -108,11 +109,15 @@ def lib() -> ctypes.CDLL:
         L.sana_linattn_fwd_fmap.argtypes = [_vp] * 4 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
             ctypes.c_int, _vp]
+        L.sana_linattn_fwd_strided.argtypes = [_vp] * 3 + [_i64, _vp] + [_i64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
+            ctypes.c_int, _vp]
         L.sana_linattn_qkv_workspace_size.argtypes = [_i64] * 5 + [ctypes.POINTER(_sz)]
         L.sana_linattn_qkv_fwd.argtypes = [_vp] * 4 + [_i64] * 5 + [
             ctypes.c_float, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
                      "sana_linattn_fwd_block_causal_profiled", "sana_linattn_fwd_fmap",
+                     "sana_linattn_fwd_strided",
                      "sana_linattn_qkv_workspace_size", "sana_linattn_qkv_fwd"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
@@ -426,6 +431,65 @@ def forward_fmap(q, k, v, fmap: str = "relu", eps: float = 1e-6, heads: Optional
                                        workspace.numel() * workspace.element_size(), arr, n,
                                        _stream(q)),
            "sana_linattn_fwd_fmap")
+    return out
+
+
+def _event_array(events):
+    if events is None:
+        return None, 0
+    for e in events:
+        if e.cuda_event == 0:  # torch creates the HIP event on first record
+            e.record()
+    return (_vp * len(events))(*[e.cuda_event for e in events]), len(events)
+
+
+def _token_stride(x, name: str, H: int, d: int) -> int:
+    """ld of a (B, N, H, d) or (B, N, H d) view with packed heads and channels
+    whose tokens are ld elements apart and batch items N ld apart."""
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    B, N = int(x.shape[0]), int(x.shape[1])
+    sb, sn = x.stride()[:2]
+    packed = x.stride()[-1] == 1 and (x.dim() == 3 or H == 1 or x.stride()[2] == d)
+    ld = sn if N > 1 else (sb if B > 1 else H * d)
+    if not packed or (B > 1 and sb != N * ld):
+        raise ValueError(f"{name} must be a (B, N, H, d) view with packed heads and channels and "
+                         "batch stride N * (token stride)")
+    return int(ld)
+
+
+def forward_strided(q, k, v, fmap: str = "relu", eps: float = 1e-6, heads: Optional[int] = None,
+                    out=None, workspace=None, events=None):
+    """Forward pass on q, k, v views whose tokens are ld elements apart (one
+    ld for all three), e.g. q, k, v = qkv.view(B, N, 3, H, d).unbind(2) for
+    the output qkv of one fused linear layer: read in place, no copies.
+    Returns a new contiguous (B, N, H, d) out (or fills ``out``)."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    lds = {_token_stride(x, name, H, d) for x, name in ((q, "q"), (k, "k"), (v, "v"))}
+    if len(lds) != 1:
+        raise ValueError("q, k and v must share one token stride")
+    for x, name in ((k, "k"), (v, "v")):
+        if x.dtype != q.dtype or x.shape != q.shape or x.device != q.device:
+            raise ValueError(f"{name} must match q in dtype, shape and device")
+    dt = _dtype_code(q)
+    if fmap not in FMAPS:
+        raise ValueError(f"unknown feature map {fmap!r}; one of {sorted(FMAPS)}")
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=q.dtype, device=q.device)
+    else:
+        _check_tensor(out, "out")
+        if out.dtype != q.dtype or out.numel() != B * N * H * d or out.device != q.device:
+            raise ValueError("out must hold B * N * H * d elements of q's dtype on q's device")
+    if workspace is None:
+        workspace = alloc_workspace(B, N, H, dt, q.device)
+    arr, n = _event_array(events)
+    _check(lib().sana_linattn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), lds.pop(),
+                                          out.data_ptr(), B, N, H, d, float(eps), dt,
+                                          FMAPS[fmap], workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), arr, n,
+                                          _stream(q)),
+           "sana_linattn_fwd_strided")
     return out
 
 

@@ -90,6 +90,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H) {
   p.B = B;
   p.N = N;
   p.H = H;
+  p.ld = H * kHeadDim;
   p.pairs = cdiv(H, kHeadsPerBlock);
   p.units = B * p.pairs;
   p.tiles = cdiv(N, kTile);
@@ -312,20 +313,42 @@ bool valid_fmap(int fmap) {
   return fmap == SANA_FMAP_RELU || fmap == SANA_FMAP_ELU1 || fmap == SANA_FMAP_COS;
 }
 
+// Bytes a [B][N][H][d] input with token stride ld spans from its first
+// element: (B N - 1) ld + H d elements. 0 when that overflows (or passes
+// 2^62 bytes).
+size_t strided_span(int64_t B, int64_t N, int64_t H, int64_t d, int64_t ld, int64_t item) {
+  int64_t t = 0;
+  if (__builtin_mul_overflow(B, N, &t) || __builtin_mul_overflow(t - 1, ld, &t) ||
+      __builtin_add_overflow(t, H * d, &t) || __builtin_mul_overflow(t, item, &t) ||
+      t >= (int64_t(1) << 62))
+    return 0;
+  return static_cast<size_t>(t);
+}
+
 // The forward pass behind every fwd entry point. events (may be NULL) are
 // recorded before the first kernel and after each kernel. Feature maps
-// other than ReLU run the split kernels only.
+// other than ReLU, and q, k, v with a token stride ld other than H d, run
+// the split kernels only (ld = 0 means H d).
 sana_status_t forward(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t N, int64_t H, int64_t d, float eps, int dtype, int variant,
                       void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
-                      int* n_kernels, hipStream_t stream, int fmap = SANA_FMAP_RELU) {
+                      int* n_kernels, hipStream_t stream, int fmap = SANA_FMAP_RELU,
+                      int64_t ld = 0) {
   size_t tb = 0;
   sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
   if (s != SANA_OK) return s;
   if (!valid_variant(variant) || !valid_fmap(fmap)) return SANA_ERR_UNSUPPORTED;
-  if (fmap != SANA_FMAP_RELU && variant == SANA_VARIANT_FUSED) return SANA_ERR_UNSUPPORTED;
-  if (fmap != SANA_FMAP_RELU) variant = SANA_VARIANT_SPLIT;
-  const Plan p = make_plan(B, N, H);
+  const int64_t item = dtype == SANA_DTYPE_F32 ? 4 : 2;
+  if (ld == 0) ld = H * d;
+  if (ld < H * d) return SANA_ERR_INVALID_ARG;
+  const size_t in_bytes = strided_span(B, N, H, d, ld, item);
+  if (in_bytes == 0) return SANA_ERR_INVALID_ARG;
+  if ((ld * item) % 16 != 0) return SANA_ERR_ALIGNMENT;  // every token row 16-byte aligned
+  const bool split_only = fmap != SANA_FMAP_RELU || ld != H * d;
+  if (split_only && variant == SANA_VARIANT_FUSED) return SANA_ERR_UNSUPPORTED;
+  if (split_only) variant = SANA_VARIANT_SPLIT;
+  Plan p = make_plan(B, N, H);
+  p.ld = ld;
   const int run = resolve_variant(p, variant);
   const int nk = kernels_of(run);
   if (n_kernels) *n_kernels = nk;
@@ -337,7 +360,8 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
   if ((s = check_eps(eps)) != SANA_OK) return s;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return SANA_ERR_ALIGNMENT;
-  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+  if (overlaps(out, tb, q, in_bytes) || overlaps(out, tb, k, in_bytes) ||
+      overlaps(out, tb, v, in_bytes))
     return SANA_ERR_INVALID_ARG;
   if ((s = check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
   if (overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
@@ -612,6 +636,16 @@ sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v,
                                     hipEvent_t* events, int n_events, hipStream_t stream) {
   return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, SANA_VARIANT_SPLIT, workspace,
                        workspace_bytes, events, n_events, nullptr, stream, fmap);
+}
+
+sana_status_t sana_linattn_fwd_strided(const void* q, const void* k, const void* v, int64_t ld,
+                                       void* out, int64_t B, int64_t N, int64_t H, int64_t d,
+                                       float eps, int dtype, int fmap, void* workspace,
+                                       size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                       hipStream_t stream) {
+  if (ld < 1) return SANA_ERR_INVALID_ARG;
+  return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, SANA_VARIANT_SPLIT, workspace,
+                       workspace_bytes, events, n_events, nullptr, stream, fmap, ld);
 }
 
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,

@@ -23,6 +23,8 @@ constexpr int kHeadsPerBlock = 2;                     // a head pair shares 128-
 // sized for the largest counts any device can pick.
 struct Plan {
   int64_t B, N, H;
+  int64_t ld;             // elements between consecutive tokens of q, k and v
+                          // (H * d unless the forward is called strided)
   int64_t pairs;          // ceil(H / 2) head pairs per batch item
   int64_t units;          // B * pairs
   int64_t tiles;          // 16-token tiles per unit, ceil(N / 16)

@@ -441,12 +441,14 @@ __device__ __forceinline__ u32x4 apply_head(const ApplyOperands& op, u32x4 qpiec
 // make_ops(op) fills the two heads' operands; it runs after the first U tiles'
 // loads are issued, so whatever it waits for (the state's loads, a block
 // barrier: every wave of the block calls it) overlaps those loads.
+// row / base locate q as in reduce_pair_wave; orow / obase locate the output.
 template <int U, int Fm = kFmapRelu, class MakeOps>
 __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict__ Q,
                                                 unsigned short* __restrict__ Out,
                                                 MakeOps&& make_ops, float eps,
-                                                int64_t row, int64_t base, int64_t n_lo,
-                                                int64_t n_hi, int sub, int S, bool two,
+                                                int64_t row, int64_t base, int64_t orow,
+                                                int64_t obase, int64_t n_lo, int64_t n_hi,
+                                                int sub, int S, bool two,
                                                 unsigned char* slot) {
   const int l = lane_id();
   const int t0 = l >> 3;
@@ -495,7 +497,7 @@ __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict
     return *reinterpret_cast<const u32x4*>(slot + tile_off(t0 + 8 * h2, j));
   };
   auto out_ptr = [&](int64_t i, int h2) {
-    return Out + base + (n_lo + (sub + i * S) * kTile + t0 + 8 * h2) * row + 8 * j;
+    return Out + obase + (n_lo + (sub + i * S) * kTile + t0 + 8 * h2) * orow + 8 * j;
   };
   // Main loop over this wave's tiles that lie wholly inside the range: no
   // branches, unconditional stores, U tiles in flight.
@@ -644,12 +646,14 @@ __device__ __forceinline__ void stage_state_padded(float* dst, const float* st) 
   }
 }
 
-// Lane l computes token n_lo + 64*tile + l of one head.
+// Lane l computes token n_lo + 64*tile + l of one head. q of token n starts
+// at Q + base + n * row, its output at Out + obase + n * orow.
 template <int Fm = kFmapRelu>
 __device__ __forceinline__ void apply_f32_wave(const float* __restrict__ Q, float* __restrict__ Out,
                                                const float* stp /*padded LDS*/, float eps,
-                                               int64_t row, int64_t base, int64_t n_lo,
-                                               int64_t n_hi, int sub, int S) {
+                                               int64_t row, int64_t base, int64_t orow,
+                                               int64_t obase, int64_t n_lo, int64_t n_hi,
+                                               int sub, int S) {
   const int l = lane_id();
   const int64_t tiles = (n_hi - n_lo + kWave - 1) / kWave;
   for (int64_t t = sub; t < tiles; t += S) {
@@ -681,7 +685,7 @@ __device__ __forceinline__ void apply_f32_wave(const float* __restrict__ Q, floa
       }
     }
     const float rinv = 1.0f / (num[kD] + eps);
-    float* op = Out + base + n * row;
+    float* op = Out + obase + n * orow;
 #pragma unroll
     for (int c4 = 0; c4 < kD / 4; ++c4) {
       f32x4 o;
@@ -847,13 +851,14 @@ __device__ __forceinline__ SlotRange slot_range(int64_t unit, int64_t T, int64_t
 // (g - first block of the unit) of that unit. With Fold, the last of the
 // unit's contributing blocks also folds the unit's partials, in order, into
 // the state; without, the partials are the result (the apply sums them).
-// Partials: [units][slots][2 heads][d][d+1].
+// Partials: [units][slots][2 heads][d][d+1]. Element (b, n, h, c) of k and
+// v is at b * N * ld + n * ld + h * d + c (ld = H * d when contiguous).
 template <int S, int U, bool Fold, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
     float* __restrict__ partials, float* __restrict__ state, unsigned long long* __restrict__ ctl,
-    unsigned long long epoch, int64_t N, int64_t H, int64_t pairs, int64_t T, int64_t Qb,
-    int64_t F, int64_t slots) {
+    unsigned long long epoch, int64_t N, int64_t H, int64_t ld, int64_t pairs, int64_t T,
+    int64_t Qb, int64_t F, int64_t slots) {
   __shared__ RedLds<S> lds;
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = blockIdx.x;
@@ -861,10 +866,10 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
   const int64_t f_hi = f_lo + Qb < F ? f_lo + Qb : F;
   for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
-    const int64_t base = (sg.b * N * H + sg.h) * kD;
+    const int64_t base = sg.b * N * ld + sg.h * kD;
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
-    reduce_pair_wave<U, Fm>(K, V, H * kD, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub],
+    reduce_pair_wave<U, Fm>(K, V, ld, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub],
                             acc, ks);
     const SlotRange sr = slot_range(unit, T, Qb);
     float* part = partials + ((unit * slots) + (g - sr.first)) * 2 * kSF;
@@ -880,8 +885,8 @@ template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
     const float* __restrict__ K, const float* __restrict__ V, float* __restrict__ partials,
     float* __restrict__ state, unsigned long long* __restrict__ ctl, unsigned long long epoch,
-    int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk, int64_t nchunks,
-    int64_t BH) {
+    int64_t N, int64_t H, int64_t ld, int64_t pairs, int64_t units, int64_t chunk,
+    int64_t nchunks, int64_t BH) {
   __shared__ float slot[2 * S][2 * kTile * kD];
   __shared__ float xchg[(S > 1 ? S - 1 : 1) * 2 * 17 * kWave];
   const BlockCoords bc = block_coords(pairs, units, H);
@@ -891,7 +896,7 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
 #pragma unroll
   for (int r = 0; r < 17; ++r) acc[r] = 0.0f;
   if (bc.active)
-    reduce_f32_wave<U, Fm>(K, V, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S,
+    reduce_f32_wave<U, Fm>(K, V, ld, bc.b * N * ld + bc.h * kD, n_lo, n_hi, bc.sub, S,
                            slot[threadIdx.x >> 6], acc);
   combine_substreams<S, 17>(acc, xchg, bc.hh, bc.sub);
   if (bc.active && bc.sub == 0)
@@ -966,12 +971,13 @@ __device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
 // reduction, summed here in ascending slot order, as fold_partials does), -Qr
 // when Qr < 0 (a fixed number of slots per unit), else 1 (a folded state).
 // The block sums them once into LDS; each wave then builds
-// its MFMA operands from there.
+// its MFMA operands from there. q has token stride ld (as k and v in
+// reduce_bf16_kernel); the output is contiguous [B][N][H][d].
 template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     const unsigned short* __restrict__ Q, const float* __restrict__ src, int64_t sb, int64_t sp,
-    int64_t Qr, unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs,
-    int64_t units, int64_t T, int64_t C, int64_t Qa, int64_t X) {
+    int64_t Qr, unsigned short* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t ld,
+    int64_t pairs, int64_t units, int64_t T, int64_t C, int64_t Qa, int64_t X) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
   __shared__ alignas(16) unsigned char slots[S][kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
@@ -993,15 +999,16 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
       op[0] = make_apply_operands(stf);
       op[1] = sg.two ? make_apply_operands(stf + kSF) : op[0];
     };
-    apply_pair_wave<U, Fm>(Q, Out, make_ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
-                           sg.n_hi, sub, S, sg.two, slots[sub]);
+    apply_pair_wave<U, Fm>(Q, Out, make_ops, eps, ld, sg.b * N * ld + sg.h * kD, H * kD,
+                           (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi, sub, S, sg.two,
+                           slots[sub]);
   }
 }
 
 template <int S, int Fm = kFmapRelu>
 __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ state, float* __restrict__ Out,
-    float eps, int64_t N, int64_t H, int64_t pairs, int64_t units, int64_t chunk) {
+    float eps, int64_t N, int64_t H, int64_t ld, int64_t pairs, int64_t units, int64_t chunk) {
   __shared__ float stp[2][kD * kPadCols];
   const BlockCoords bc = block_coords(pairs, units, H);
   if (bc.active && bc.sub == 0) stage_state_padded(stp[bc.hh], state + (bc.b * H + bc.h) * kSF);
@@ -1009,8 +1016,8 @@ __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
   if (!bc.active) return;
   const int64_t n_lo = bc.p * chunk;
   const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
-  apply_f32_wave<Fm>(Q, Out, stp[bc.hh], eps, H * kD, (bc.b * N * H + bc.h) * kD, n_lo, n_hi,
-                     bc.sub, S);
+  apply_f32_wave<Fm>(Q, Out, stp[bc.hh], eps, ld, bc.b * N * ld + bc.h * kD, H * kD,
+                     (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S);
 }
 
 // One block per (b, head pair) over all N tokens: reduce into registers,
@@ -1034,7 +1041,7 @@ __global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
     op[0] = make_apply_operands(st[0]);
     op[1] = make_apply_operands(st[1]);
   };
-  apply_pair_wave<U>(Q, Out, make_ops, eps, H * kD, base, 0, N, pc.sub, S, pc.two,
+  apply_pair_wave<U>(Q, Out, make_ops, eps, H * kD, base, H * kD, base, 0, N, pc.sub, S, pc.two,
                      lds.slot[pc.sub]);
 }
 
@@ -1059,7 +1066,7 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
   if (bc.active && bc.sub == 0) stage_state_padded(stp[bc.hh], st[bc.hh]);
   __syncthreads();
   if (!bc.active) return;
-  apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, base, 0, N, bc.sub, S);
+  apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, base, H * kD, base, 0, N, bc.sub, S);
 }
 
 // ------------------------------------------------------------ bf16 backward
@@ -1633,13 +1640,13 @@ hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, con
       hipLaunchKernelGGL(kernel, dim3((unsigned)p.red_blocks), dim3(64 * kRedS), 0, stream,
                          static_cast<const unsigned short*>(k),
                          static_cast<const unsigned short*>(v), partials, state, ctl, epoch, p.N,
-                         p.H, p.pairs, p.tiles, p.red_q, p.units * p.tiles, p.slots);
+                         p.H, p.ld, p.pairs, p.tiles, p.red_q, p.units * p.tiles, p.slots);
     } else {
       hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U, Fm>),
                          dim3((unsigned)(p.units * p.red_chunks)), dim3(128 * kF32S), 0, stream,
                          static_cast<const float*>(k), static_cast<const float*>(v), partials,
-                         state, ctl, epoch, p.N, p.H, p.pairs, p.units, p.red_chunk, p.red_chunks,
-                         BH);
+                         state, ctl, epoch, p.N, p.H, p.ld, p.pairs, p.units, p.red_chunk,
+                         p.red_chunks, BH);
     }
     return hipGetLastError();
   });
@@ -1693,12 +1700,13 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
                          dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
                          kApplyLdsPad, stream, static_cast<const unsigned short*>(q), state,
                          p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
-                         eps, p.N, p.H, p.pairs, p.units, p.tiles, p.app_chunks,
+                         eps, p.N, p.H, p.ld, p.pairs, p.units, p.tiles, p.app_chunks,
                          p.app_chunk / kTile, X);
     } else {
       hipLaunchKernelGGL((apply_f32_kernel<kF32S, Fm>), dim3((unsigned)(p.units * p.app_chunks)),
                          dim3(128 * kF32S), 0, stream, static_cast<const float*>(q), state,
-                         static_cast<float*>(out), eps, p.N, p.H, p.pairs, p.units, p.app_chunk);
+                         static_cast<float*>(out), eps, p.N, p.H, p.ld, p.pairs, p.units,
+                         p.app_chunk);
     }
     return hipGetLastError();
   });
@@ -1714,7 +1722,7 @@ hipError_t launch_apply_partials(const Plan& p, const void* q, const float* part
                        dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
                        kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
                        p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
-                       p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+                       p.ld, p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
     return hipGetLastError();
   });
 }
@@ -1727,7 +1735,7 @@ hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partial
                      dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
                      kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
                      p.pairs * sp, sp, -count, static_cast<unsigned short*>(out), eps, p.N, p.H,
-                     p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+                     p.ld, p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
   return hipGetLastError();
 }
 

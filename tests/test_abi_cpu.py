@@ -331,3 +331,31 @@ def test_qkv_workspace_and_errors(L):
     assert f(ev=two, nev=2) == INVALID
     holes = (ctypes.c_void_p * 3)(1, None, 3)
     assert f(ev=holes, nev=3) == INVALID
+
+
+def test_fwd_strided_rejects_invalid_arguments(L):
+    need = ws_size(L, 1, 64, 2)[1]
+
+    def f(ld=192, fmap=0, eps=1e-6, q=P_Q, k=P_K, o=P_O, dt=BF16, ws=P_W, wsb=None, ev=None,
+          nev=0):
+        return L.sana_linattn_fwd_strided(q, k, P_V, ld, o, 1, 64, 2, 32, eps, dt, fmap, ws,
+                                          need if wsb is None else wsb, ev, nev, None)
+
+    for ld in (0, -1, -192, 63):           # below H d = 64
+        assert f(ld=ld) == INVALID, ld
+    assert f(ld=1 << 60) == INVALID        # span beyond 2^62 bytes
+    assert f(ld=68) == ALIGNMENT           # 136-byte token rows
+    assert f(ld=72, eps=-1.0) == INVALID   # 144-byte rows pass; eps fails
+    assert f(ld=66, dt=F32) == ALIGNMENT   # 264 bytes
+    assert f(ld=68, dt=F32, eps=-1.0) == INVALID
+    assert f(fmap=3) == UNSUPPORTED
+    assert f(q=P_Q + 8) == ALIGNMENT
+    assert f(q=None) == INVALID
+    # out inside q's strided span (63 * 192 + 64 elements), past a contiguous tensor
+    assert f(o=P_Q + 16384) == INVALID
+    assert f(ld=64, o=P_Q + 16384, eps=-1.0) == INVALID
+    assert f(o=P_K - 4096) == INVALID      # out's end reaches into k
+    assert f(wsb=need - 1) == WORKSPACE
+    assert f(ws=P_O) == INVALID
+    two = (ctypes.c_void_p * 2)(1, 2)
+    assert f(ev=two, nev=2) == INVALID
