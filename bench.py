@@ -600,9 +600,27 @@ def run_qkv(args, w, C: int = 2240):
         vv.view(w.B, w.N, D).copy_(yv[:, :, 2])
         R.forward(qq, kk, vv, eps=w.eps, out=oo, workspace=fws)
 
+    # and the unfused step without the copies: the forward reads q, k, v in
+    # place from the GEMM's rows through the strided entry point
+    def unfused_strided(i):
+        d = sets[i % n_sets]
+        torch.matmul(d["x"].view(w.B * w.N, C), d["w"].t(), out=y)
+        yv = y.view(w.B, w.N, 3, w.H, w.d)
+        R.forward_strided(yv[:, :, 0], yv[:, :, 1], yv[:, :, 2], eps=w.eps, out=oo,
+                          workspace=fws)
+
+    def gemm_only(i):
+        d = sets[i % n_sets]
+        torch.matmul(d["x"].view(w.B * w.N, C), d["w"].t(), out=y)
+
     for i in range(3):
         unfused(i)
-    ms_unfused = time_steps(unfused, min(args.steps, 50))
+        unfused_strided(i)
+        gemm_only(i)
+    n_ctx = min(args.steps, 50)
+    ms_unfused = time_steps(unfused, n_ctx)
+    ms_unfused_strided = time_steps(unfused_strided, n_ctx)
+    ms_gemm = time_steps(gemm_only, n_ctx)
     result = {
         "metric": METRIC_QKV,
         "value": w.B * w.N / (ms_per_step * 1e-3),
@@ -622,6 +640,9 @@ def run_qkv(args, w, C: int = 2240):
         "ms_per_step_with_kernel_events": ms_events,
         "projection_tflops": achieved,
         "unfused_library_gemm_ms_per_step": ms_unfused,
+        "unfused_library_gemm_strided_fwd_ms_per_step": ms_unfused_strided,
+        "library_gemm_ms": ms_gemm,
+        "library_gemm_tflops": flops / (ms_gemm * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": "projection", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
