@@ -40,7 +40,8 @@ CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
 TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "traffic_latent_4096px.json"),
                  "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json"),
                  "block_causal": os.path.join(ROOT, "profiles",
-                                              "traffic_block_causal_video_1m_tokens.json")}
+                                              "traffic_block_causal_video_1m_tokens.json"),
+                 "qkv": os.path.join(ROOT, "profiles", "traffic_qkv_latent_4096px.json")}
 
 
 def parse():
@@ -586,6 +587,7 @@ def run_qkv(args, w, C: int = 2240):
 
     # context: the same step unfused, the library GEMM (torch.matmul) writing
     # [q | k | v] rows, the three slices copied to [B][N][H][d], then the forward
+    # (left out of counter runs, whose apply figures would mix in its launches)
     d0 = sets[0]
     y = torch.empty((w.B * w.N, 3 * D), dtype=torch.bfloat16, device="cuda")
     kk, vv, qq, oo = (torch.empty_like(d0["q"]) for _ in range(4))
@@ -613,14 +615,22 @@ def run_qkv(args, w, C: int = 2240):
         d = sets[i % n_sets]
         torch.matmul(d["x"].view(w.B * w.N, C), d["w"].t(), out=y)
 
-    for i in range(3):
-        unfused(i)
-        unfused_strided(i)
-        gemm_only(i)
-    n_ctx = min(args.steps, 50)
-    ms_unfused = time_steps(unfused, n_ctx)
-    ms_unfused_strided = time_steps(unfused_strided, n_ctx)
-    ms_gemm = time_steps(gemm_only, n_ctx)
+    ms_unfused = ms_unfused_strided = ms_gemm = None
+    if args.copy_mib == 0:
+        for i in range(3):
+            unfused(i)
+            unfused_strided(i)
+            gemm_only(i)
+        n_ctx = min(args.steps, 50)
+        ms_unfused = time_steps(unfused, n_ctx)
+        ms_unfused_strided = time_steps(unfused_strided, n_ctx)
+        ms_gemm = time_steps(gemm_only, n_ctx)
+    else:  # counter calibration: a plain copy of exactly copy_mib MiB each way
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
     result = {
         "metric": METRIC_QKV,
         "value": w.B * w.N / (ms_per_step * 1e-3),
@@ -642,10 +652,11 @@ def run_qkv(args, w, C: int = 2240):
         "unfused_library_gemm_ms_per_step": ms_unfused,
         "unfused_library_gemm_strided_fwd_ms_per_step": ms_unfused_strided,
         "library_gemm_ms": ms_gemm,
-        "library_gemm_tflops": flops / (ms_gemm * 1e-3) / 1e12,
+        "library_gemm_tflops": flops / (ms_gemm * 1e-3) / 1e12 if ms_gemm else None,
         "roofline": {"bound": "mfma", "kernel": "projection", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("projection", w.name, "qkv")},
     }
     if args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
