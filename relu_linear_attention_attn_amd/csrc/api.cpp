@@ -197,8 +197,11 @@ void fit_plan_to_device(Plan& p, int dtype) {
     // about kReduceWavesPerCu waves streaming per CU within one round
     const int64_t waves = static_cast<int64_t>(c.cus) * kReduceWavesPerCu;
     const int64_t want = cdiv(waves, p.units * block_waves(KernelKind::kReduce, dtype));
-    const int64_t rc = clamp64(std::min(want, std::max<int64_t>(1, rcap / p.units)), 1,
-                               p.red_chunks_max);
+    int64_t rc = clamp64(std::min(want, std::max<int64_t>(1, rcap / p.units)), 1,
+                         p.red_chunks_max);
+#ifdef SANA_TUNING
+    if (const char* e = getenv("SANA_F32_RED_CHUNKS")) rc = clamp64(atoll(e), 1, p.red_chunks_max);
+#endif
     p.red_chunk = chunk_tokens(p.N, rc);
     p.red_chunks = cdiv(p.N, p.red_chunk);
   }

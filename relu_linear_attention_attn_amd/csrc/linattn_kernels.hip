@@ -64,9 +64,6 @@ __device__ __forceinline__ void wave_lds_order() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
 __device__ __forceinline__ void st16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
 // Streaming (nontemporal) accesses for data touched exactly once per call:
@@ -565,63 +562,96 @@ __device__ __forceinline__ void combine_substreams(float (&regs)[R], float* xchg
 }
 
 
-// Lane l owns state rows c = l/2, columns 16*(l%2) .. +15, and ksum[c].
+// fp32 tiles of the MFMA paths: 32 tokens of one head, 32 channels of 4 bytes
+// per token (one 128-byte line). A wave's loads cover whole lines: lane l
+// takes 16-byte piece l % 8 of tokens 8 i + l / 8, i < 4.
+constexpr int kF32Tile = 32;
+constexpr int kF32TileFloats = kF32Tile * kD;  // 1024
+
+// Accumulates phi(K)^T V and phi(K)^T 1 for one head over the tiles sub,
+// sub + S, ... of 32 tokens of [n_lo, n_hi), on MFMA 32x32x2 fp32 (exact
+// fp32 products, fp32 sums: the fp32 path's accuracy): output row c (K
+// channel) and column j (V channel); the k index is the token, two per
+// instruction, so both operands are row reads of the staged tiles - lane l
+// takes phi(K[2 i + l/32][l%32]) and V[2 i + l/32][l%32]. ksum falls out of
+// the same phi(K) values. At the end the sums are handed back in the layout
+// of the state helpers: lane l owns state row c = l/2, columns 16*(l%2) ..
+// +15 (acc[0..15]), and ksum[c] (acc[16]). slot: the wave's 2 * 1024 floats
+// of LDS. Loads are never predicated: a token outside the range reads row
+// n_lo and is dropped (phi = 0) when the operands are built.
 template <int U, int Fm = kFmapRelu>
 __device__ __forceinline__ void reduce_f32_wave(const float* __restrict__ K,
                                                 const float* __restrict__ V, int64_t row,
                                                 int64_t base, int64_t n_lo, int64_t n_hi,
-                                                int sub, int S, float* slot /*2*16*32*/,
+                                                int sub, int S, float* slot /*2 * 1024*/,
                                                 float (&acc)[17]) {
   const int l = lane_id();
-  const int lt = l >> 3;        // tokens lt and lt + 8 of the tile
-  const int lq = l & 7;         // 16-byte eighth of the 128-byte row
-  const int c = l >> 1;
-  const int jh = (l & 1) * 16;
-  const int64_t tiles = (n_hi - n_lo + kTile - 1) / kTile;
+  const int lt = l >> 3;        // token lt + 8 i of the tile
+  const int lq = l & 7;         // 16-byte piece of the token's line
+  const int tk = l >> 5;        // MFMA k: token 2 i + tk
+  const int col = l & 31;       // MFMA row (K channel) / column (V channel)
+  const int64_t tiles = (n_hi - n_lo + kF32Tile - 1) / kF32Tile;
   const int64_t mine = tiles > sub ? (tiles - sub + S - 1) / S : 0;
 
-  u32x4 kb[U][2], vb[U][2];
-  auto issue = [&](int64_t i, u32x4 (&kd)[2], u32x4 (&vd)[2]) {
+  u32x4 kb[U][4], vb[U][4];
+  auto issue = [&](int64_t i, u32x4 (&kd)[4], u32x4 (&vd)[4]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kF32Tile + lt;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int64_t n = n_lo + (sub + i * S) * kTile + lt + 8 * h2;
+    for (int h = 0; h < 4; ++h) {
+      const int64_t n = n0 + 8 * h;
       const int64_t off = base + (n < n_hi ? n : n_lo) * row + lq * 4;
-      kd[h2] = ld16(K + off);
-      vd[h2] = ld16(V + off);
+      kd[h] = ld16_stream(K + off);
+      vd[h] = ld16_stream(V + off);
     }
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u, kb[u], vb[u]);
 
-  float* ks = slot;
-  float* vs = slot + kTile * kD;
+  float* ks_t = slot;                   // [32 tokens][32 channels]
+  float* vs_t = slot + kF32TileFloats;  // [32 tokens][32 channels]
+  f32x16 d = (f32x16)0;
+  float ksum = 0.0f;
   for (int64_t i0 = 0; i0 < mine; i0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (i0 + u < mine) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int64_t n = n_lo + (sub + (i0 + u) * S) * kTile + lt + 8 * h2;
-          st16(ks + (lt + 8 * h2) * kD + lq * 4, n < n_hi ? kb[u][h2] : (u32x4)0);
-          st16(vs + (lt + 8 * h2) * kD + lq * 4, vb[u][h2]);
+        for (int h = 0; h < 4; ++h) {
+          st16(ks_t + (lt + 8 * h) * kD + lq * 4, kb[u][h]);
+          st16(vs_t + (lt + 8 * h) * kD + lq * 4, vb[u][h]);
         }
         issue(i0 + u + U, kb[u], vb[u]);
         wave_lds_order();
-        const int64_t left = n_hi - (n_lo + (sub + (i0 + u) * S) * kTile);
-        const int valid = static_cast<int>(left < kTile ? left : kTile);
-#pragma unroll 4
-        for (int t = 0; t < kTile; ++t) {
-          // staged k is 0 past the range: ReLU drops those tokens by itself
-          const float kc = Fm == kFmapRelu ? fmaxf(ks[t * kD + c], 0.0f)
-                                           : (t < valid ? fmap_f32<Fm>(ks[t * kD + c]) : 0.0f);
+        const int64_t left = n_hi - (n_lo + (sub + (i0 + u) * S) * kF32Tile);
+        const int valid = static_cast<int>(left < kF32Tile ? left : kF32Tile);
+        // all operands first, so the LDS reads overlap each other, not the MFMAs
+        float av[kF32Tile / 2], bv[kF32Tile / 2];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) acc[m] = __builtin_fmaf(kc, vs[t * kD + jh + m], acc[m]);
-          acc[16] += kc;
+        for (int t2 = 0; t2 < kF32Tile / 2; ++t2) {
+          av[t2] = ks_t[(2 * t2 + tk) * kD + col];
+          bv[t2] = vs_t[(2 * t2 + tk) * kD + col];
         }
         wave_lds_order();
+#pragma unroll
+        for (int t2 = 0; t2 < kF32Tile / 2; ++t2) {
+          const float a = 2 * t2 + tk < valid ? fmap_f32<Fm>(av[t2]) : 0.0f;
+          ksum += a;
+          d = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv[t2], d, 0, 0, 0);
+        }
       }
     }
   }
+  // back to the state helpers' layout through the slot: [c][33], ksum in column 32
+  ksum += __shfl_xor(ksum, 32);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) slot[(8 * (r >> 2) + 4 * tk + (r & 3)) * kSC + col] = d[r];
+  if (l < 32) slot[col * kSC + kD] = ksum;
+  wave_lds_order();
+  const int c = l >> 1, jh = (l & 1) * 16;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) acc[m] += slot[c * kSC + jh + m];
+  acc[16] += slot[c * kSC + kD];
+  wave_lds_order();
 }
 
 template <bool Coherent>
@@ -646,52 +676,104 @@ __device__ __forceinline__ void stage_state_padded(float* dst, const float* st) 
   }
 }
 
-// Lane l computes token n_lo + 64*tile + l of one head. q of token n starts
-// at Q + base + n * row, its output at Out + obase + n * orow.
+// LDS of one wave in the fp32 apply: the q tile transposed to [channel][token]
+// (row pitch 33 floats, so the operand reads and the staging writes spread
+// over the banks), then the output tile [token][channel] (pitch 36 floats,
+// 16-byte rows for the line reads), and 1 / den per token.
+constexpr int kF32QPitch = 33, kF32OPitch = 36;
+#ifndef SANA_F32_APP_U
+#define SANA_F32_APP_U 2
+#endif
+constexpr int kF32ApplyU = SANA_F32_APP_U;  // tiles in flight per wave
+constexpr int kF32ApplyLds = kF32Tile * kF32OPitch + kF32Tile;  // floats per wave
+
+// Applies one head's state to the tiles sub, sub + S, ... of 32 tokens of
+// [n_lo, n_hi) on MFMA 32x32x2 fp32: num (token x output channel) =
+// phi(q) KV with k = the q channel, two per instruction - lane l feeds
+// phi(q[l%32][2 i + l/32]) and KV[2 i + l/32][l%32], the 16 KV values it
+// needs held in registers for the whole range. den = phi(q) . ksum + eps
+// from the same phi(q) values (each lane half the channels, the halves
+// added by a shuffle). q of token n starts at Q + base + n * row, its output
+// at Out + obase + n * orow; stp: the head's state padded to 36 columns in
+// LDS; lds: the wave's kF32ApplyLds floats. Tokens past n_hi read row n_lo
+// and are not stored.
 template <int Fm = kFmapRelu>
 __device__ __forceinline__ void apply_f32_wave(const float* __restrict__ Q, float* __restrict__ Out,
                                                const float* stp /*padded LDS*/, float eps,
                                                int64_t row, int64_t base, int64_t orow,
                                                int64_t obase, int64_t n_lo, int64_t n_hi,
-                                               int sub, int S) {
+                                               int sub, int S, float* lds) {
   const int l = lane_id();
-  const int64_t tiles = (n_hi - n_lo + kWave - 1) / kWave;
-  for (int64_t t = sub; t < tiles; t += S) {
-    const int64_t n = n_lo + t * kWave + l;
-    if (n >= n_hi) continue;
-    const float* qp = Q + base + n * row;
-    float q[kD];
+  const int lt = l >> 3, lq = l & 7;
+  const int tk = l >> 5, col = l & 31;
+  const int64_t tiles = (n_hi - n_lo + kF32Tile - 1) / kF32Tile;
+  const int64_t mine = tiles > sub ? (tiles - sub + S - 1) / S : 0;
+  float* qt = lds;                        // [32 channels][33]
+  float* ot = lds;                        // [32 tokens][36], after qt is consumed
+  float* rv = lds + kF32Tile * kF32OPitch;
+  float kv[16], ks[16];
 #pragma unroll
-    for (int c4 = 0; c4 < kD / 4; ++c4) {
-      // bit-cast whole vectors only: a bit-cast of one vector element is
-      // mis-lowered by this compiler (it reads element 0)
-      const f32x4 x = __builtin_bit_cast(f32x4, ld16(qp + 4 * c4));
+  for (int i = 0; i < 16; ++i) {
+    kv[i] = stp[(2 * i + tk) * kPadCols + col];
+    ks[i] = stp[(2 * i + tk) * kPadCols + kD];
+  }
+  constexpr int U = kF32ApplyU;
+  u32x4 qb[U][4];
+  auto issue = [&](int64_t i, u32x4 (&qd)[4]) {
+    const int64_t n0 = n_lo + (sub + i * S) * kF32Tile + lt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[4 * c4 + e] = fmap_f32<Fm>(x[e]);
+    for (int h = 0; h < 4; ++h) {
+      const int64_t n = n0 + 8 * h;
+      qd[h] = ld16_stream(Q + base + (n < n_hi ? n : n_lo) * row + lq * 4);
     }
-    float num[kD + 1];
+  };
 #pragma unroll
-    for (int j = 0; j <= kD; ++j) num[j] = 0.0f;
+  for (int u = 0; u < U; ++u) issue(u, qb[u]);
+  for (int64_t i0 = 0; i0 < mine; i0 += U) {
 #pragma unroll
-    for (int c = 0; c < kD; ++c) {
-      const float qc = q[c];
-      const float* sr = stp + c * kPadCols;
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < mine) {
+        const int64_t tile = sub + (i0 + u) * S;
 #pragma unroll
-      for (int j4 = 0; j4 < 9; ++j4) {
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(sr + 4 * j4);
+        for (int h = 0; h < 4; ++h) {
+          const f32x4 x = __builtin_bit_cast(f32x4, qb[u][h]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * j4 + e <= kD) num[4 * j4 + e] = __builtin_fmaf(qc, s4[e], num[4 * j4 + e]);
+          for (int e = 0; e < 4; ++e) qt[(lq * 4 + e) * kF32QPitch + lt + 8 * h] = x[e];
+        }
+        issue(i0 + u + U, qb[u]);
+        wave_lds_order();
+        float av[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) av[i] = qt[(2 * i + tk) * kF32QPitch + col];
+        wave_lds_order();
+        f32x16 d = (f32x16)0;
+        float den = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = fmap_f32<Fm>(av[i]);
+          den = __builtin_fmaf(a, ks[i], den);
+          d = __builtin_amdgcn_mfma_f32_32x32x2f32(a, kv[i], d, 0, 0, 0);
+        }
+        den += __shfl_xor(den, 32);
+        if (l < 32) rv[col] = 1.0f / (den + eps);
+        wave_lds_order();
+        // d lane l, register r: token 8 (r / 4) + 4 (l / 32) + r % 4, channel l % 32
+        f32x4 r4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          r4[g] = *reinterpret_cast<const f32x4*>(rv + 8 * g + 4 * tk);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ot[(8 * (r >> 2) + 4 * tk + (r & 3)) * kF32OPitch + col] = d[r] * r4[r >> 2][r & 3];
+        wave_lds_order();
+        const int64_t n0 = n_lo + tile * kF32Tile + lt;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const u32x4 o = *reinterpret_cast<const u32x4*>(ot + (lt + 8 * h) * kF32OPitch + lq * 4);
+          if (n0 + 8 * h < n_hi) st16(Out + obase + (n0 + 8 * h) * orow + lq * 4, o);
+        }
+        wave_lds_order();
       }
-    }
-    const float rinv = 1.0f / (num[kD] + eps);
-    float* op = Out + obase + n * orow;
-#pragma unroll
-    for (int c4 = 0; c4 < kD / 4; ++c4) {
-      f32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = num[4 * c4 + e] * rinv;
-      st16(op + 4 * c4, __builtin_bit_cast(u32x4, o));
     }
   }
 }
@@ -887,7 +969,7 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
     float* __restrict__ state, unsigned long long* __restrict__ ctl, unsigned long long epoch,
     int64_t N, int64_t H, int64_t ld, int64_t pairs, int64_t units, int64_t chunk,
     int64_t nchunks, int64_t BH) {
-  __shared__ float slot[2 * S][2 * kTile * kD];
+  __shared__ alignas(16) float slot[2 * S][2 * kF32TileFloats];
   __shared__ float xchg[(S > 1 ? S - 1 : 1) * 2 * 17 * kWave];
   const BlockCoords bc = block_coords(pairs, units, H);
   const int64_t n_lo = bc.p * chunk;
@@ -1010,6 +1092,7 @@ __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ state, float* __restrict__ Out,
     float eps, int64_t N, int64_t H, int64_t ld, int64_t pairs, int64_t units, int64_t chunk) {
   __shared__ float stp[2][kD * kPadCols];
+  __shared__ alignas(16) float wl[2 * S][kF32ApplyLds];
   const BlockCoords bc = block_coords(pairs, units, H);
   if (bc.active && bc.sub == 0) stage_state_padded(stp[bc.hh], state + (bc.b * H + bc.h) * kSF);
   __syncthreads();
@@ -1017,7 +1100,7 @@ __global__ __launch_bounds__(128 * S) void apply_f32_kernel(
   const int64_t n_lo = bc.p * chunk;
   const int64_t n_hi = n_lo + chunk < N ? n_lo + chunk : N;
   apply_f32_wave<Fm>(Q, Out, stp[bc.hh], eps, ld, bc.b * N * ld + bc.h * kD, H * kD,
-                     (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S);
+                     (bc.b * N * H + bc.h) * kD, n_lo, n_hi, bc.sub, S, wl[threadIdx.x >> 6]);
 }
 
 // One block per (b, head pair) over all N tokens: reduce into registers,
@@ -1049,7 +1132,7 @@ template <int S, int U>
 __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ Out, float eps, int64_t N, int64_t H, int64_t pairs) {
-  __shared__ float slot[2 * S][2 * kTile * kD];
+  __shared__ alignas(16) float slot[2 * S][2 * kF32TileFloats];
   __shared__ float xchg[(S > 1 ? S - 1 : 1) * 2 * 17 * kWave];
   __shared__ float st[2][kSF];
   __shared__ float stp[2][kD * kPadCols];
@@ -1066,7 +1149,8 @@ __global__ __launch_bounds__(128 * S) void fused_f32_kernel(
   if (bc.active && bc.sub == 0) stage_state_padded(stp[bc.hh], st[bc.hh]);
   __syncthreads();
   if (!bc.active) return;
-  apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, base, H * kD, base, 0, N, bc.sub, S);
+  apply_f32_wave(Q, Out, stp[bc.hh], eps, H * kD, base, H * kD, base, 0, N, bc.sub, S,
+                 slot[threadIdx.x >> 6]);
 }
 
 // ------------------------------------------------------------ bf16 backward
@@ -1611,7 +1695,13 @@ constexpr int kBwkvS = SANA_BWKV_S, kBwkvU = SANA_BWKV_U;
 constexpr int64_t kXcds = 8;
 int64_t apply_xcds(const Plan& p) { return p.units >= kXcds ? kXcds : 1; }
 int64_t xcd_grid(int64_t items, int64_t X) { return X * ((items + X - 1) / X); }
-constexpr int kF32S = 2, kF32U = 2;
+#ifndef SANA_F32_S
+#define SANA_F32_S 4
+#endif
+#ifndef SANA_F32_U
+#define SANA_F32_U 2
+#endif
+constexpr int kF32S = SANA_F32_S, kF32U = SANA_F32_U;
 
 // Runs f(std::integral_constant<int, Fm>) for the feature map fmap.
 template <class F>
