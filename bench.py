@@ -3,7 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--op fwd|bwd|block_causal|qkv] [--block L] [--fmap relu|elu1|cos]
-                    [--layout contiguous|packed]
+                    [--layout contiguous|packed] [--dtype bf16|f32]
 
 A step is one full forward pass (the state reduction over token ranges into
 per-block partials, then the apply, which sums them) - or, with --op bwd, one
@@ -56,6 +56,9 @@ def parse():
                          "forward (default workload: the 16-frame video, one block per frame)")
     ap.add_argument("--fmap", default="relu", choices=["relu", "elu1", "cos"],
                     help="feature map of the forward (other than relu: the split kernels)")
+    ap.add_argument("--dtype", default=None, choices=["bf16", "f32"],
+                    help="forward: run the workload's shape and recipe in this dtype "
+                         "(default: the workload's own)")
     ap.add_argument("--layout", default="contiguous", choices=["contiguous", "packed"],
                     help="forward inputs as three [B][N][H][d] tensors, or read in place "
                          "from one packed [B][N][3][H][d] projection output (strided entry)")
@@ -733,6 +736,9 @@ def main():
         R.lib()
         return run_qkv(args, w)
     variant = {"auto": R.VARIANT_AUTO, "split": R.VARIANT_SPLIT, "fused": R.VARIANT_FUSED}[args.variant]
+    if args.dtype and args.dtype != w.dtype:
+        import dataclasses
+        w = dataclasses.replace(w, dtype=args.dtype)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.lib()
     log(args, f"workload {wname} {w.shape} {w.dtype}: generating inputs")
@@ -812,8 +818,8 @@ def main():
     dominant = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dominant]
     achieved = alg_bytes[dominant] / (dom_ms * 1e-3) / 1e9
-    traffic = (measured_traffic(dominant, wname)
-               if args.fmap == "relu" and args.layout == "contiguous" else None)
+    traffic = (measured_traffic(dominant, wname) if args.fmap == "relu" and
+               args.layout == "contiguous" and w.dtype == W.WORKLOADS[wname].dtype else None)
     path_gbps = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = w.B * w.N / (ms_per_step * 1e-3)
 
