@@ -96,14 +96,29 @@ __device__ __forceinline__ void widen_bf16x8(u32x4 w, float (&x)[8]) {
   }
 }
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x to ~2^-17 relative).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to two bf16 (round to nearest even), as one packed conversion.
+__device__ __forceinline__ unsigned int cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x to ~2^-17 relative),
+// a pair at a time: one packed conversion each for hi and lo, hi widened back
+// exactly (a bf16 is the top half of a binary32).
 __device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, w;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const __bf16 h = (__bf16)x[m];
-    hi[m] = h;
-    lo[m] = (__bf16)(x[m] - (float)h);
+  for (int e = 0; e < 4; ++e) {
+    h[e] = cvt_pk_bf16(x[2 * e], x[2 * e + 1]);
+    const float h0 = __builtin_bit_cast(float, h[e] << 16);
+    const float h1 = __builtin_bit_cast(float, h[e] & 0xFFFF0000u);
+    w[e] = cvt_pk_bf16(x[2 * e] - h0, x[2 * e + 1] - h1);
   }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, w);
 }
 
 // Feature maps phi, element by element in fp32 (the values of sana_fmap_t):
@@ -1317,9 +1332,9 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       const int po = tile_off(col, hh * 4 + g);
       const u32x4 qraw = *reinterpret_cast<const u32x4*>(w.q + po);
       const u32x4 graw = *reinterpret_cast<const u32x4*>(w.g + po);
-      float pq[8], gf[8], u[8];
-      widen_bf16x8(relu_bf16x8(qraw), pq);
-      widen_bf16x8(graw, gf);
+      float pq[8], u[8];
+      const u32x4 rq = relu_bf16x8(qraw);
+      widen_bf16x8(rq, pq);
       row_product<false>(ro[hh], __builtin_bit_cast(bf16x8, graw), (bf16x8)0, u);  // u = S g
       float dp = 0.0f, p = 0.0f;
 #pragma unroll
@@ -1330,12 +1345,20 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       const float rinv = __builtin_amdgcn_rcpf(token_sum(dp) + eps);  // 1 ulp
       p = token_sum(p);
       const float dden = valid ? -p * rinv * rinv : 0.0f;
-      // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the ReLU gate
-      const s16x8 qs = __builtin_bit_cast(s16x8, qraw);
-      bf16x8 dq;
+      // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the
+      // ReLU gate on the packed pair: each 16-bit half of rq is ReLU(q)'s bits,
+      // 0 where q <= 0 and 0x0001..0x7FFF above, so adding 0x7FFF to each half
+      // (no carry crosses: at most 0xFFFE) sets its top bit exactly where
+      // q > 0, and an arithmetic shift spreads that bit over the half
+      u32x4 dqw;
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-        dq[m] = qs[m] > 0 ? (__bf16)(u[m] * rinv + ro[hh].last[m] * dden) : (__bf16)0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const unsigned int v = cvt_pk_bf16(u[2 * e] * rinv + ro[hh].last[2 * e] * dden,
+                                           u[2 * e + 1] * rinv + ro[hh].last[2 * e + 1] * dden);
+        const s16x2 top = __builtin_bit_cast(s16x2, rq[e] + 0x7FFF7FFFu);
+        dqw[e] = v & __builtin_bit_cast(unsigned int, top >> 15);
+      }
+      const bf16x8 dq = __builtin_bit_cast(bf16x8, dqw);
       // the token reduction: 1 / den and dden rows to LDS, the operands
       // gathered transposed (k = the lane's 8 tokens, channel l%32)
       if (g == 0) {
