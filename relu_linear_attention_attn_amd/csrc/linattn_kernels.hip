@@ -105,6 +105,16 @@ __device__ __forceinline__ unsigned int cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// The ReLU gate on a packed bf16 pair: v kept in each half where the same
+// half of relu (max(x, 0) of x's bits as signed 16-bit values) is nonzero,
+// i.e. x > 0, and zeroed elsewhere. relu's halves are 0 or 0x0001..0x7FFF, so
+// adding 0x7FFF to each (no carry crosses: at most 0xFFFE) sets a half's top
+// bit exactly where x > 0, and an arithmetic shift spreads it over the half.
+__device__ __forceinline__ unsigned int relu_gate_pk(unsigned int v, unsigned int relu) {
+  const s16x2 top = __builtin_bit_cast(s16x2, relu + 0x7FFF7FFFu);
+  return v & __builtin_bit_cast(unsigned int, top >> 15);
+}
+
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x to ~2^-17 relative),
 // a pair at a time: one packed conversion each for hi and lo, hi widened back
 // exactly (a bf16 is the top half of a binary32).
@@ -1345,19 +1355,13 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       const float rinv = __builtin_amdgcn_rcpf(token_sum(dp) + eps);  // 1 ulp
       p = token_sum(p);
       const float dden = valid ? -p * rinv * rinv : 0.0f;
-      // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the
-      // ReLU gate on the packed pair: each 16-bit half of rq is ReLU(q)'s bits,
-      // 0 where q <= 0 and 0x0001..0x7FFF above, so adding 0x7FFF to each half
-      // (no carry crosses: at most 0xFFFE) sets its top bit exactly where
-      // q > 0, and an arithmetic shift spreads that bit over the half
+      // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the ReLU gate
       u32x4 dqw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned int v = cvt_pk_bf16(u[2 * e] * rinv + ro[hh].last[2 * e] * dden,
-                                           u[2 * e + 1] * rinv + ro[hh].last[2 * e + 1] * dden);
-        const s16x2 top = __builtin_bit_cast(s16x2, rq[e] + 0x7FFF7FFFu);
-        dqw[e] = v & __builtin_bit_cast(unsigned int, top >> 15);
-      }
+      for (int e = 0; e < 4; ++e)
+        dqw[e] = relu_gate_pk(cvt_pk_bf16(u[2 * e] * rinv + ro[hh].last[2 * e] * dden,
+                                          u[2 * e + 1] * rinv + ro[hh].last[2 * e + 1] * dden),
+                              rq[e]);
       const bf16x8 dq = __builtin_bit_cast(bf16x8, dqw);
       // the token reduction: 1 / den and dden rows to LDS, the operands
       // gathered transposed (k = the lane's 8 tokens, channel l%32)
@@ -1492,17 +1496,19 @@ __device__ __forceinline__ void grad_kv_pair_wave(const unsigned short* __restri
       const u32x4 kraw = *reinterpret_cast<const u32x4*>(slot + po);
       const u32x4 vraw = *reinterpret_cast<const u32x4*>(slot + kTileBytes + po);
       float y[8], x[8];
+      const u32x4 rk = relu_bf16x8(kraw);
       row_product<false>(ro[hh], __builtin_bit_cast(bf16x8, vraw), (bf16x8)0, y);
-      col_product(ao[hh], __builtin_bit_cast(bf16x8, relu_bf16x8(kraw)), x);
-      const s16x8 kq = __builtin_bit_cast(s16x8, kraw);
-      bf16x8 dk, dv;
+      col_product(ao[hh], __builtin_bit_cast(bf16x8, rk), x);
+      u32x4 dk, dv;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        dk[m] = kq[m] > 0 ? (__bf16)(y[m] + ro[hh].last[m]) : (__bf16)0.0f;
-        dv[m] = (__bf16)x[m];
+      for (int e = 0; e < 4; ++e) {
+        dk[e] = relu_gate_pk(cvt_pk_bf16(y[2 * e] + ro[hh].last[2 * e],
+                                         y[2 * e + 1] + ro[hh].last[2 * e + 1]),
+                             rk[e]);
+        dv[e] = cvt_pk_bf16(x[2 * e], x[2 * e + 1]);
       }
-      *reinterpret_cast<bf16x8*>(slot + po) = dk;
-      *reinterpret_cast<bf16x8*>(slot + kTileBytes + po) = dv;
+      *reinterpret_cast<u32x4*>(slot + po) = dk;
+      *reinterpret_cast<u32x4*>(slot + kTileBytes + po) = dv;
     }
     wave_lds_order();
   };
