@@ -498,7 +498,7 @@ sana_status_t plan_qkv(int64_t B, int64_t N, int64_t C, int64_t H, int64_t d, Qk
   return SANA_OK;
 }
 
-constexpr int64_t kQkvGroupM = 4;  // M tiles per group of the projection's block order
+constexpr int64_t kQkvGroupM = 8;  // token tiles per group of the projection's tile order
 
 sana_status_t qkv_forward(const void* x, const void* w, void* q, void* out, int64_t B, int64_t N,
                           int64_t C, int64_t H, int64_t d, float eps, void* workspace,

@@ -3,29 +3,32 @@
 // The Sana review's deployment section folds linear attention's ReLU(K)^T V
 // product into the QKV projection layer. Here one bf16 MFMA GEMM computes
 // [q | k | v] = x W^T (x: [B][N][C] token features, W: [3D][C], the [out][in]
-// layout of a linear layer; D = H d). Blocks whose output columns are Q write
-// Q (bf16) to memory; blocks whose columns are one head pair's K and V never
+// layout of a linear layer; D = H d). Tiles whose output columns are Q write
+// Q (bf16) to memory; tiles whose columns are two head pairs' K and V never
 // store them: they round the tile to bf16 (what an unfused bf16 projection
-// would store), form the pair's state ReLU(K)^T [V | 1] over the tile's 256
-// tokens on MFMA, and write it as one partial state. The apply of the forward
-// pass then sums a head pair's partials and computes the output from Q.
+// would store), form each pair's state ReLU(K)^T [V | 1] over the tile's 256
+// tokens on MFMA, and write it as one partial state per pair. The apply of
+// the forward pass then sums a head pair's partials and computes the output
+// from Q.
 //
-// Tiles: 256 tokens x 128 output columns x 32 input channels per step, four
-// waves per block and two blocks per CU, wave w owning tokens 64w .. 64w + 63
-// of the tile (2 x 4 MFMA 32x32x16 bf16 tiles). Both operand tiles have the
-// input channels contiguous (x rows and W rows), so lane l of an MFMA reads
-// row l % 32 and 8 consecutive channels: one 16-byte LDS read from a tile
-// stored as 64-byte rows whose 16-byte pieces are XOR-swizzled by the row.
-// Each step's pieces are loaded into registers two steps ahead (two register
-// sets) and stored to the other of two LDS stages between the two halves of
-// the current step's MFMAs; one barrier per step.
+// Tiles: 256 tokens x 256 output columns, one block of four waves per CU,
+// one wave per SIMD, each owning a 128 x 128 quarter (4 x 4 MFMA 32x32x16
+// bf16 tiles, accumulators in AGPRs: 0.5 fragment reads per MFMA). Operands
+// come in 64-channel stages: a stage holds 128 bytes of every x and W row of
+// the tile, i.e. one whole 128-byte line per row, loaded by buffer loads
+// straight to LDS with 8 lanes per line. Whole lines are the point: loads of
+// 64-byte half lines (32 channels per row and step) return data at about
+// half the rate per CU (64 against 124..140 bytes per ns measured, with
+// registers or LDS as the destination), which had held every 32-channel
+// design near 1000 TFLOP/s. Two stages (128 KB); the next stage's 16 loads
+// per wave are issued among the first 16 MFMAs of the current one.
 //
-// Measured on the 4096px 1.6B block (x [2, 16384, 2240]): about 1000
-// TFLOP/s, 40% of the bf16 MFMA peak; the same loop with its MFMAs alone
-// runs at 1620 TFLOP/s, and the fragment reads from LDS (12 per 16 MFMAs)
-// account for most of the difference. Loading the stages with buffer loads
-// straight to LDS (three stages, no register staging) measured the same.
+// Epilogues from registers: Q tiles multiply W x^T, so each lane holds 4
+// consecutive output columns of one token (8-byte stores); K | V tiles form
+// the state from the accumulators directly (see there).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "linattn_internal.h"
 
@@ -41,27 +44,63 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kSC = kStateCols;    // 33
 constexpr int kSF = kStateFloats;  // 1056
-constexpr int kBM = 256, kBN = 128, kBK = 32;
+constexpr int kBM = 256, kBN = 256;         // tile: tokens x output columns
 constexpr int kThreads = 256;
-constexpr int kRow = kBK * 2;              // bytes per operand tile row (32 channels)
-constexpr int kATile = kBM * kRow;         // 16 KB
-constexpr int kBTile = kBN * kRow;         // 8 KB
-constexpr int kStage = kATile + kBTile;    // 24 KB
-constexpr int kKVPitch = kBM * 2 + 16;     // bytes per feature row of the transposed K|V tile
-constexpr int kXchg = kBN * kKVPitch;      // exchange area after the K|V tile
-// LDS: two operand stages during the loop; the epilogue reuses it for the
-// transposed K|V tile and the wave exchange (the larger need, 74.5 KB), so
-// two blocks fit a CU's 160 KB.
-constexpr int kLds = kXchg + 2 * 17 * kWave * 4;
-static_assert(2 * kStage <= kLds && kBM * kBN * 2 <= kLds, "stages and Q tile fit");
-// dword 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle)
+constexpr int kPair = 64;                   // channels per stage
+constexpr int kPRow = kPair * 2;            // 128 bytes per row and stage
+constexpr int kPA = kBM * kPRow;            // 32 KB of x rows
+constexpr int kPStage = kPA + kBN * kPRow;  // 64 KB
+constexpr int kLds = 2 * kPStage;           // the K | V epilogue reuses stage 0
+// dword 3 of a raw buffer resource on gfx950 (32-bit data format, no
+// swizzle): a load past num_records returns 0
 constexpr int kRsrcFlags = 0x00020000;
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), other counters not waited
 
-// Offset of 16-byte piece c (0..3) of row r in a tile of 64-byte rows: the
-// piece index is XORed with (r / 4) % 4, so the 16 rows an MFMA fragment
-// read touches at once (four 64-byte rows per 256-byte bank sweep) fall on
-// distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return (r << 6) + ((c ^ ((r >> 2) & 3)) << 4); }
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The four dwords of a raw buffer resource over `bytes` bytes at p, made
+// wave-uniform (a load past `bytes` returns 0).
+__device__ __forceinline__ i32x4 buffer_words(const void* p, int bytes) {
+  const unsigned long long ad = reinterpret_cast<unsigned long long>(p);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(ad & 0xFFFFFFFFu));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int>((ad >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = kRsrcFlags;
+  return r;
+}
+
+// One 16-byte buffer load per lane straight to LDS: lane l's bytes land at
+// LDS address m0 + 16 l. Written as inline assembly so that the compiler,
+// which cannot tell which LDS bytes such a load writes, does not wait for
+// every one in flight before each LDS read; the kernel waits (s_waitcnt
+// vmcnt) for the ones it needs. Nothing lands in a register. (M0 is reserved
+// to the compiler, which warns when an asm statement clobbers it; this
+// file's code uses M0 nowhere else.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, int voffset, int soffset, int m0) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(m0)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt operand for "at most n vector memory operations of this wave in
+// flight" (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt at
+// their maxima, i.e. not waited for).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Stage layout: row r (x rows 0..255, then W rows 256..511) at 128 r; its
+// 16-byte piece j (channels 8 j .. 8 j + 7 of the stage) in slot
+// j ^ ((r >> 1) & 7), so the 16 consecutive rows an MFMA fragment read takes
+// at one piece fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int pslot(int r, int j) { return (r << 7) + ((j ^ ((r >> 1) & 7)) << 4); }
 
 struct QkvArgs {
   const unsigned short* x;  // [B][N][C]
@@ -71,22 +110,26 @@ struct QkvArgs {
   int64_t N, C, H, D, pairs;
   int64_t J;      // 256-token tiles per batch item, ceil(N / 256)
   int64_t MT;     // B * J
-  int64_t nq;     // Q column tiles, ceil(D / 128)
-  int64_t NT;     // nq + pairs
-  int64_t GM;     // M tiles per group of the block order
+  int64_t nq;     // Q column tiles, ceil(D / 256)
+  int64_t NT;     // nq + ceil(pairs / 2)
+  int64_t GM;     // M tiles per group of the tile order
   int64_t items;  // MT * NT
 };
 
-__global__ __launch_bounds__(kThreads, 2) void qkv_state_kernel(QkvArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void qkv_state_kernel(QkvArgs a) {
   __shared__ alignas(16) unsigned char lds[kLds];
   const int tid = threadIdx.x;
   const int l = tid & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv & 1;   // tokens 128 wm .. +127 of the tile
+  const int wn = wv >> 1;  // columns 128 wn .. +127 of the tile
 
-  // Work item of this block: the items are cut into 8 contiguous runs, one
-  // per XCD (blocks are dealt to the XCDs round robin), and ordered in groups
-  // of GM M-tiles with the M-tile fastest, so the blocks an XCD runs at once
-  // share a few x tiles and a few W tiles in its L2.
+  // Tile of this block: the items are cut into 8 contiguous runs, one per
+  // XCD (blocks are dealt to the XCDs round robin), and ordered in groups of
+  // GM token tiles with the token tile fastest, so the blocks an XCD runs at
+  // once share a few x tiles and a few W tiles in its L2. Item (mt, nt):
+  // token tile mt, column tile nt (Q columns 256 nt .., or K | V of head
+  // pairs p0 and p0 + 1).
   constexpr int64_t X = 8;
   const int64_t per = (a.items + X - 1) / X;
   const int64_t item = (blockIdx.x % X) * per + blockIdx.x / X;
@@ -99,266 +142,276 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_state_kernel(QkvArgs a) {
   const int64_t b = mt / a.J, j = mt - b * a.J;
   const int64_t n0 = j * kBM;
   const bool is_q = nt < a.nq;
-  const int64_t p = nt - a.nq;  // head pair of a K|V tile
+  const int64_t p0 = 2 * (nt - a.nq);
 
-  // Operand tiles come in through buffer loads, whose range check returns 0
-  // for bytes past a resource's size: the x resource spans the tile's valid
-  // tokens, so tokens past N read 0; the W tile is two resources of 64 rows
-  // (Q: columns 128 nt .. +63 and +64 .. +127; K | V: the pair's 64 k rows
-  // and its 64 v rows), each sized to its rows below D, so columns past D
-  // (the end of Q, the missing second head of an odd pair) read 0. Offsets
-  // are 32-bit within a resource (the host bounds 256 C * 2 bytes).
   const int64_t rows_a = a.N - n0 < kBM ? a.N - n0 : kBM;
-  const __amdgpu_buffer_rsrc_t ra_src = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<unsigned short*>(a.x + (b * a.N + n0) * a.C), 0,
-      static_cast<int>(rows_a * a.C * 2), kRsrcFlags);
-  int64_t w0, w1;  // first W row of each 64-row half of the tile
-  if (is_q) {
-    w0 = nt * kBN;
-    w1 = w0 + 64;
-  } else {
-    w0 = a.D + 64 * p;
-    w1 = 2 * a.D + 64 * p;
-  }
-  const int64_t f0 = is_q ? nt * kBN : 64 * p;  // feature of the first row of each half
+  const i32x4 ra_src = buffer_words(a.x + (b * a.N + n0) * a.C, static_cast<int>(rows_a * a.C * 2));
+  // The B tile of a Q item is W rows 256 nt .. +255; of a K | V item,
+  // [k(p0) | v(p0) | k(p0 + 1) | v(p0 + 1)], 64 rows each. Wave wv loads B
+  // rows 64 wv .. +63 through a resource that ends at D (the end of Q, a
+  // missing head of an odd last pair, a missing last pair), so those rows
+  // read 0; the x resource ends at the tile's last valid token.
   auto half_rows = [&](int64_t f) { return a.D - f <= 0 ? 0 : (a.D - f < 64 ? a.D - f : 64); };
-  const int64_t rows_w0 = half_rows(f0), rows_w1 = half_rows(is_q ? f0 + 64 : f0);
-  const __amdgpu_buffer_rsrc_t rw_src[2] = {
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(a.w + w0 * a.C), 0,
-                                        static_cast<int>(rows_w0 * a.C * 2), kRsrcFlags),
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(a.w + w1 * a.C), 0,
-                                        static_cast<int>(rows_w1 * a.C * 2), kRsrcFlags)};
-
-  // Global loads of one step: x tile 4 pieces per thread (rows lr + 64 i),
-  // W tile 2 (row lr of each 64-row half), never predicated. Two register
-  // sets: step j's pieces go to set j % 2 and are issued two steps before
-  // they are stored to LDS, so they have two steps of multiplies to land.
-  // Channels past C (a ragged last step) read the next row's; they are
-  // overwritten with zeros in LDS after the store.
-  const int lr = tid >> 2, lc = tid & 3;
-  const int off_a = (lr * static_cast<int>(a.C) + 8 * lc) * 2;
-  const int row_a = 64 * static_cast<int>(a.C) * 2;   // bytes between a thread's x rows
-  u32x4 ra0[4], rb0[2], ra1[4], rb1[2];
-  // A step inside C passes its channel offset as the scalar offset, so the
-  // per-lane offsets are loop-invariant registers; the ragged last step adds
-  // it to the lane offsets, which the range check covers.
-  int vo_a[4];
+  i32x4 rw_src;
+  {
+    const int qi = wv;
+    int64_t w0, f;
+    if (is_q) {
+      w0 = nt * kBN + 64 * qi;
+      f = w0;
+    } else {
+      const int64_t p = p0 + (qi >> 1);
+      w0 = ((qi & 1) ? 2 * a.D : a.D) + 64 * p;
+      f = 64 * p;
+    }
+    const int64_t rows = half_rows(f);
+    rw_src = buffer_words(a.w + (rows > 0 ? w0 : 0) * a.C, static_cast<int>(rows * a.C * 2));
+  }
+  // Stage loads straight to LDS: per wave 8 instructions for x rows
+  // 64 wv + 8 i .. +7 and 8 for B rows 64 wv + 8 i .. +7; lane l lands in
+  // slot l % 8 of row l / 8 and so fetches piece (l % 8) ^ ((row >> 1) & 7)
+  // of that row: 8 whole 128-byte lines per instruction. Offsets are 32-bit
+  // within a resource (the host bounds 256 C * 2 bytes).
+  const int row_c = static_cast<int>(a.C) * 2;
+  const int lrow = l >> 3, lsl = l & 7;
+  int vo_a[8], vo_b[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vo_a[i] = off_a + i * row_a;
-  auto load_full = [&](int k0, u32x4 (&ra)[4], u32x4 (&rb)[2]) {
-    const int kb = k0 * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo_a[i], kb, 0));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      rb[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw_src[i], off_a, kb, 0));
+  for (int i = 0; i < 8; ++i) {
+    const int ra = 64 * wv + 8 * i + lrow;   // x row in the tile
+    const int rb = 8 * i + lrow;             // row in this wave's W quarter
+    const int rbt = 64 * wv + rb;            // row in the B tile
+    vo_a[i] = ra * row_c + ((lsl ^ ((ra >> 1) & 7)) << 4);
+    vo_b[i] = rb * row_c + ((lsl ^ ((rbt >> 1) & 7)) << 4);
+  }
+  const int lbase = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(reinterpret_cast<unsigned long long>((lds_ptr)lds)));
+  // load i (0..15) of stage q into LDS stage q % 2: x rows (i < 8), else B
+  // rows. Inside C the channel offset goes in the scalar offset; a ragged
+  // stage adds it to the lane offsets, which the range check covers.
+  auto dma_one = [&](int q, int i) {
+    const bool inside = q < a.C / kPair;
+    const int kb = q * kPRow;
+    const int so = inside ? kb : 0, vk = inside ? 0 : kb;
+    const int m0 = lbase + (q & 1) * kPStage + (i < 8 ? 0 : kPA) + (64 * wv + 8 * (i & 7)) * kPRow;
+    load_lds16(i < 8 ? ra_src : rw_src, (i < 8 ? vo_a[i & 7] : vo_b[i & 7]) + vk, so, m0);
   };
-  auto load = [&](int k0, u32x4 (&ra)[4], u32x4 (&rb)[2]) {
-    const int kb = k0 * 2;
+  auto dma_pair = [&](int q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo_a[i] + kb, 0, 0));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      rb[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw_src[i], off_a + kb, 0, 0));
+    for (int i = 0; i < 16; ++i) dma_one(q, i);
   };
-  auto store_full = [&](int s, const u32x4 (&ra)[4], const u32x4 (&rb)[2]) {
-    unsigned char* A = lds + s * kStage;
-    unsigned char* Bt = A + kATile;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(A + swz(lr + 64 * i, lc)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = rb[i];
-  };
-  auto store = [&](int s, int k0, const u32x4 (&ra)[4], const u32x4 (&rb)[2]) {
-    unsigned char* A = lds + s * kStage;
-    unsigned char* Bt = A + kATile;
-    store_full(s, ra, rb);
-    if (k0 + kBK > a.C && k0 + 8 * lc >= a.C) {  // a ragged step: this thread's pieces past C
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(A + swz(lr + 64 * i, lc)) = (u32x4)0;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(Bt + swz(lr + 64 * i, lc)) = (u32x4)0;
+  // a ragged stage, once landed: its pieces at channels >= C (the next row's
+  // data) are zeroed
+  auto zero_tail = [&](int q) {
+    unsigned char* A = lds + (q & 1) * kPStage;
+    for (int idx = tid; idx < (kBM + kBN) * 8; idx += kThreads) {
+      const int r = idx >> 3, j = idx & 7;
+      if (q * kPair + 8 * j >= a.C)
+        *reinterpret_cast<u32x4*>(A + pslot(r, j)) = (u32x4)0;  // rows >= kBM: the B tile
     }
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = (f32x16)0;
-  // One step's multiplies. The fragments of sub-step kk + 1 are read from
-  // LDS before the MFMAs of sub-step kk are issued, so their latency hides
-  // behind those MFMAs.
-  // One step's multiplies: both 16-channel sub-steps' fragments are read
-  // from stage s first, then the MFMAs of sub-step 0, then `between` (the
-  // main loop stores the next stage there, overlapping the MFMAs), then
-  // those of sub-step 1.
-  auto compute_with = [&](int s, auto&& between) {
-    const unsigned char* A = lds + s * kStage;
-    const unsigned char* Bt = A + kATile;
-    bf16x8 af[2][2], bfr[2][4];
+  // One stage: four 16-channel sub-steps; sub-step kk + 1's fragments are
+  // read while sub-step kk's 16 MFMAs run (one read per two MFMAs). Lane l
+  // of an MFMA reads row l % 32, piece 2 kk + l / 32 (8 channels). Swap:
+  // D = W x^T (Q tiles), else x W^T. Pre: stage q + 1's loads go out among
+  // sub-step 0's MFMAs.
+  auto compute_pair = [&](int q, auto swap, auto pre) {
+    constexpr bool Pre = decltype(pre)::value;
+    constexpr bool Swap = decltype(swap)::value;
+    const unsigned char* A = lds + (q & 1) * kPStage;
+    const unsigned char* Bt = A + kPA;
+    bf16x8 af[2][4], bfr[2][4];
+    auto frags = [&](int kk, int buf) {
+      const int j = 2 * kk + (l >> 5);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = 2 * kk + (l >> 5);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[kk][mi] = *reinterpret_cast<const bf16x8*>(A + swz(64 * wv + 32 * mi + (l & 31), c));
+      for (int mi = 0; mi < 4; ++mi)
+        af[buf][mi] = *reinterpret_cast<const bf16x8*>(A + pslot(128 * wm + 32 * mi + (l & 31), j));
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        bfr[kk][ni] = *reinterpret_cast<const bf16x8*>(Bt + swz(32 * ni + (l & 31), c));
-    }
-    auto mfmas = [&](int kk) {
+        bfr[buf][ni] = *reinterpret_cast<const bf16x8*>(Bt + pslot(128 * wn + 32 * ni + (l & 31), j));
+    };
+    auto mm = [&](int buf) {
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][mi], bfr[kk][ni],
-                                                                acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = Swap ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][ni], af[buf][mi],
+                                                                       acc[mi][ni], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][mi], bfr[buf][ni],
+                                                                       acc[mi][ni], 0, 0, 0);
     };
-    mfmas(0);
+    auto frag1 = [&](int kk, int buf, int r) {  // read r (0..7) of frags(kk, buf)
+      const int jp = 2 * kk + (l >> 5);
+      if (r < 4)
+        af[buf][r] = *reinterpret_cast<const bf16x8*>(A + pslot(128 * wm + 32 * r + (l & 31), jp));
+      else
+        bfr[buf][r - 4] =
+            *reinterpret_cast<const bf16x8*>(Bt + pslot(128 * wn + 32 * (r - 4) + (l & 31), jp));
+    };
+    frags(0, 0);
+    // sub-step 0, pinned: MFMA idx, then (even idx) one of sub-step 1's
+    // fragment reads, then (with the prefetch) load idx of pair q + 1
     __builtin_amdgcn_sched_barrier(0);
-    between();
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-  };
-  auto compute = [&](int s) { compute_with(s, [] {}); };
-
-  // Steps of kBK channels (the last one ragged when C % kBK != 0). Step j
-  // multiplies stage j % 2 while step j + 2's pieces load into the register
-  // set step j's used; at its end step j + 1's set is stored to the other
-  // stage. The loop is unrolled by two so the sets stay fixed registers.
-  const int nk = static_cast<int>((a.C + kBK - 1) / kBK);
-  load(0, ra0, rb0);
-  if (nk > 1) load(kBK, ra1, rb1);
-  store(0, 0, ra0, rb0);
-  __syncthreads();
-  // Main loop: steps whose loads (two ahead) and stores are whole steps
-  // inside C, with nothing conditional, so the waits before the stores can
-  // count exactly the loads issued after them. Then the last steps with the
-  // general loads and stores.
-  const int nfull = static_cast<int>(a.C / kBK);
-  auto step_fast = [&](int kt, u32x4 (&ra_free)[4], u32x4 (&rb_free)[2],
-                       const u32x4 (&ra_next)[4], const u32x4 (&rb_next)[2]) {
-    load_full((kt + 2) * kBK, ra_free, rb_free);
-    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the multiplies
-    // step kt + 1's pieces (loaded a step ago) are stored to the other stage
-    // between the two halves of the multiplies
-    compute_with(kt & 1, [&] { store_full((kt & 1) ^ 1, ra_next, rb_next); });
-    __syncthreads();
-  };
-  auto step = [&](int kt, u32x4 (&ra_free)[4], u32x4 (&rb_free)[2], const u32x4 (&ra_next)[4],
-                  const u32x4 (&rb_next)[2]) {
-    const int s = kt & 1;
-    if (kt + 2 < nk) load((kt + 2) * kBK, ra_free, rb_free);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) store(s ^ 1, (kt + 1) * kBK, ra_next, rb_next);
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 3 < nfull; kt += 2) {
-    step_fast(kt, ra0, rb0, ra1, rb1);
-    step_fast(kt + 1, ra1, rb1, ra0, rb0);
-  }
-  for (; kt < nk; kt += 2) {
-    step(kt, ra0, rb0, ra1, rb1);
-    if (kt + 1 < nk) step(kt + 1, ra1, rb1, ra0, rb0);
-  }
-
-  // acc[mi][ni] lane l, register r: token 64 wv + 32 mi + 8 (r / 4) + 4 (l / 32)
-  // + r % 4, tile column 32 ni + l % 32.
-  if (is_q) {
-    // Q: bf16 to LDS token-major (256-byte rows, 16-byte pieces swizzled by
-    // the token), then whole 16-byte pieces to memory
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+    for (int idx = 0; idx < 16; ++idx) {
+      const int mi = idx >> 2, ni = idx & 3;
+      acc[mi][ni] = Swap ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[0][ni], af[0][mi],
+                                                                   acc[mi][ni], 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][mi], bfr[0][ni],
+                                                                   acc[mi][ni], 0, 0, 0);
+      if ((idx & 1) == 0) frag1(1, 1, idx >> 1);
+      if (Pre) dma_one(q + 1, idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) frags(kk + 1, (kk + 1) & 1);
+      mm(kk & 1);
+      if (kk < 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // a barrier that waits for this wave's LDS operations only (loads to LDS
+  // in flight are waited for by count)
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Stages of 64 channels (the last one ragged when C % 64 != 0).
+  const int np = static_cast<int>((a.C + kPair - 1) / kPair);
+  const int npfull = static_cast<int>(a.C / kPair);
+  dma_pair(0);
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  barrier();
+  if (npfull < 1) {
+    zero_tail(0);
+    barrier();
+  }
+  // Stage q is multiplied while stage q + 1 loads into the other LDS stage;
+  // then this wave waits for its loads, and one barrier frees stage q and
+  // publishes everyone's stage q + 1.
+  auto main_loop = [&](auto swap) {
+    for (int q = 0; q + 1 < np; ++q) {
+      compute_pair(q, swap, std::true_type{});
+      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+      barrier();
+      if (q + 1 >= npfull) {
+        zero_tail(q + 1);
+        barrier();
+      }
+    }
+    compute_pair(np - 1, swap, std::false_type{});
+    barrier();
+  };
+  if (is_q)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
+
+  // Q blocks multiplied W x^T: acc[mi][ni] lane l, register r = 4 g + e holds
+  // token 128 wm + 32 mi + l % 32, tile column 128 wn + 32 ni + 8 g + 4 (l / 32)
+  // + e, so each lane stores 4 consecutive columns (8 bytes) per (mi, ni, g).
+  if (is_q) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int64_t t = n0 + 128 * wm + 32 * mi + (l & 31);
+      if (t >= a.N) continue;
+      unsigned short* row = a.q + (b * a.N + t) * a.D;
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 64 * wv + 32 * mi + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-          const int f = 32 * ni + (l & 31);
-          *reinterpret_cast<__bf16*>(lds + t * 256 + (((f >> 3) ^ (t & 15)) << 4) + 2 * (f & 7)) =
-              (__bf16)acc[mi][ni][r];
+        for (int g = 0; g < 4; ++g) {
+          const int64_t f = nt * kBN + 128 * wn + 32 * ni + 8 * g + 4 * (l >> 5);
+          if (f < a.D) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[mi][ni][4 * g + e];
+            *reinterpret_cast<bf16x4*>(row + f) = v;
+          }
         }
-    __syncthreads();
-#pragma unroll 4
-    for (int i = 0; i < kBM * 16 / kThreads; ++i) {
-      const int idx = tid + kThreads * i;
-      const int t = idx >> 4, c = idx & 15;
-      const int64_t f0 = nt * kBN + 8 * c;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + t * 256 + ((c ^ (t & 15)) << 4));
-      if (n0 + t < a.N && f0 < a.D)
-        *reinterpret_cast<u32x4*>(a.q + (b * a.N + n0 + t) * a.D + f0) = v;
     }
     return;
   }
 
-  // K | V: bf16 to LDS transposed, [tile column][token] (4 tokens, 8 bytes,
-  // per write); tokens past N are written as 0, so they add nothing
+  // K | V blocks (x W^T): acc[mi][ni] lane l, register r holds token
+  // 128 wm + 32 mi + 8 (r / 4) + 4 (l / 32) + r % 4 and tile column
+  // 128 wn + 32 ni + l % 32; columns 0..63 of the wave are k of heads 0 and 1
+  // of pair p0 + wn, 64..127 their v. The state ReLU(K)^T V of head hh over
+  // the wave's 128 tokens comes straight from these registers: lane l holds
+  // k channel l % 32 (an MFMA A row) and v channel l % 32 (a B column) at the
+  // same tokens, so registers 0..7 of both (tokens 0..15 of the 32-token
+  // tile, 8 per lane half) are one 32x32x16 MFMA's operands and registers
+  // 8..15 (tokens 16..31) the next. The tile is rounded to bf16 first, as a
+  // bf16 projection would store it. Tokens past N hold 0 (their x rows read
+  // 0), so they add nothing.
+  f32x16 st[2] = {(f32x16)0, (f32x16)0};
+  float ks[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int f = 32 * ni + (l & 31);
-        const int t = 64 * wv + 32 * mi + 8 * g + 4 * (l >> 5);
-        bf16x4 v;
+      for (int half = 0; half < 2; ++half) {
+        s16x8 kv;
+        bf16x8 vv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = n0 + t + e < a.N ? (__bf16)acc[mi][ni][4 * g + e] : (__bf16)0.0f;
-        *reinterpret_cast<bf16x4*>(lds + f * kKVPitch + 2 * t) = v;
+        for (int e = 0; e < 8; ++e) {
+          kv[e] = __builtin_bit_cast(short, (__bf16)acc[mi][hh][8 * half + e]);
+          vv[e] = (__bf16)acc[mi][2 + hh][8 * half + e];
+        }
+        kv = __builtin_elementwise_max(kv, (s16x8)0);  // ReLU on bf16 bit patterns
+        st[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), vv,
+                                                         st[hh], 0, 0, 0);
+        const u32x4 u = __builtin_bit_cast(u32x4, kv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // ksum: exact widening of bf16
+          ks[hh] += __builtin_bit_cast(float, u[e] << 16);
+          ks[hh] += __builtin_bit_cast(float, u[e] & 0xFFFF0000u);
+        }
       }
-  __syncthreads();
-  // The pair's state over the tile's tokens: wave w takes head w % 2 and
-  // tokens 128 (w / 2) .. +127; S = ReLU(K)^T V on MFMA 32x32x16 (lane l:
-  // row = K channel l % 32, column = V channel l % 32, 8 tokens 8 (l / 32)..),
-  // ksum of ReLU(K) on the VALU (exact widening of bf16).
-  const int hh = wv & 1, th = wv >> 1;
-  f32x16 st = (f32x16)0;
-  float ks = 0.0f;
+  // the two token halves (waves wm = 0, 1 of a column half) are summed
+  // through LDS (stage 0, free since the last barrier)
+  float* xch = reinterpret_cast<float*>(lds) + wn * 2 * 17 * kWave;
+  if (wm == 1) {
 #pragma unroll
-  for (int s = 0; s < kBM / 2 / 16; ++s) {
-    const int t0 = 128 * th + 16 * s + 8 * (l >> 5);
-    s16x8 kv = *reinterpret_cast<const s16x8*>(lds + (32 * hh + (l & 31)) * kKVPitch + 2 * t0);
-    const bf16x8 vv =
-        *reinterpret_cast<const bf16x8*>(lds + (64 + 32 * hh + (l & 31)) * kKVPitch + 2 * t0);
-    kv = __builtin_elementwise_max(kv, (s16x8)0);  // ReLU on bf16 bit patterns
-    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), vv, st, 0, 0, 0);
-    const u32x4 u = __builtin_bit_cast(u32x4, kv);
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ks += __builtin_bit_cast(float, u[e] << 16);
-      ks += __builtin_bit_cast(float, u[e] & 0xFFFF0000u);
+      for (int r = 0; r < 16; ++r) xch[(hh * 17 + r) * kWave + l] = st[hh][r];
+      xch[(hh * 17 + 16) * kWave + l] = ks[hh];
     }
   }
-  float* xch = reinterpret_cast<float*>(lds + kXchg) + hh * 17 * kWave;
-  if (th == 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xch[r * kWave + l] = st[r];
-    xch[16 * kWave + l] = ks;
-  }
   __syncthreads();
-  if (th == 0) {
+  const int64_t p = p0 + wn;
+  if (wm == 0 && p < a.pairs) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] += xch[r * kWave + l];
-    ks += xch[16 * kWave + l];
-    ks += __shfl_xor(ks, 32);  // lanes l and l ^ 32 hold one channel's two token halves
-    float* dst = a.partials + ((b * a.pairs + p) * a.J + j) * 2 * kSF + hh * kSF;
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      dst[i * kSC + (l & 31)] = st[r];
+      for (int r = 0; r < 16; ++r) st[hh][r] += xch[(hh * 17 + r) * kWave + l];
+      float kq = ks[hh] + xch[(hh * 17 + 16) * kWave + l];
+      kq += __shfl_xor(kq, 32);  // lanes l and l ^ 32 hold one channel's two token halves
+      float* dst = a.partials + ((b * a.pairs + p) * a.J + j) * 2 * kSF + hh * kSF;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        dst[i * kSC + (l & 31)] = st[hh][r];
+      }
+      if (l < 32) dst[l * kSC + kHeadDim] = kq;
     }
-    if (l < 32) dst[l * kSC + kHeadDim] = ks;
   }
 }
 
@@ -381,7 +434,7 @@ hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partia
   a.J = qkv_m_tiles(N);
   a.MT = B * a.J;
   a.nq = (a.D + kBN - 1) / kBN;
-  a.NT = a.nq + a.pairs;
+  a.NT = a.nq + (a.pairs + 1) / 2;
   a.GM = GM;
   a.items = a.MT * a.NT;
   const int64_t grid = 8 * ((a.items + 7) / 8);
@@ -391,7 +444,7 @@ hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partia
 
 int64_t qkv_grid_blocks(int64_t B, int64_t N, int64_t H) {
   const int64_t D = H * kHeadDim;
-  const int64_t items = B * qkv_m_tiles(N) * ((D + kBN - 1) / kBN + (H + 1) / 2);
+  const int64_t items = B * qkv_m_tiles(N) * ((D + kBN - 1) / kBN + ((H + 1) / 2 + 1) / 2);
   return 8 * ((items + 7) / 8);
 }
 
