@@ -79,6 +79,35 @@ def test_qkv_matches_oracle(B, N, C, H):
     assert_close(decode(out, "bf16"), oref, "bf16", f"qkv B={B} N={N} C={C} H={H}")
 
 
+RAGGED_C = [8 * r for r in range(1, 8)] + [128 + 8 * r for r in range(8)]
+
+
+@pytest.mark.parametrize("C", RAGGED_C)
+def test_qkv_every_channel_residue(C):
+    """C over every residue mod 64 (the projection's channel stage), in one
+    stage and in three, with a ragged token tile and an odd head count:
+    against the oracle, and bit for bit equal to the same inputs with x and W
+    padded by zero channels to whole stages (the products of zero channels
+    add +0 to every fp32 sum, so the zeroed tail of a ragged stage must act
+    exactly like absent channels)."""
+    B, N, H = 1, 300, 5
+    print(f"\n[case] qkv channel residue C={C}", flush=True)
+    w, x, q, out = _run(B, N, C, H, seed=1700 + C)
+    qref, oref = QK.qkv_attention_from_inputs(x["x"], x["w"], H, w.eps)
+    _check_q(q, qref, _terms(x["x"], x["w"]), C, f"C={C}")
+    assert_close(decode(out, "bf16"), oref, "bf16", f"qkv C={C}")
+    Cp = -(-C // 64) * 64
+    if Cp != C:
+        xp = np.zeros(x["x"].shape[:-1] + (Cp,), dtype=np.uint16)
+        xp[..., :C] = x["x"]
+        wp = np.zeros(x["w"].shape[:-1] + (Cp,), dtype=np.uint16)
+        wp[..., :C] = x["w"]
+        qp, outp = R.forward_qkv(_dev(xp), _dev(wp), H, eps=w.eps)
+        torch().cuda.synchronize()
+        assert np.array_equal(q, to_host(qp, "bf16")), f"C={C}: q differs from the padded run"
+        assert np.array_equal(out, to_host(outp, "bf16")), f"C={C}: out differs from the padded run"
+
+
 def test_qkv_latent_4096px_sampled_heads():
     """The 1.6B block at 4096px: x [2, 16384, 2240], 70 heads; heads 0, 33
     and 69 compared in full (the oracle projects only their rows)."""
