@@ -16,8 +16,9 @@ constexpr int kStateFloats = kHeadDim * kStateCols;   // 1056 floats = 4224 byte
 constexpr int kTile = 16;                             // tokens per wave iteration
 constexpr int kHeadsPerBlock = 2;                     // a head pair shares 128-byte lines (bf16)
 
-// Work split of one call. The bf16 reduction runs blocks over balanced
-// ranges of the flattened (head-pair unit, tile) index; the fp32 reduction
+// Work split of one call. The bf16 reduction runs a (head-pair unit, token
+// chunk) grid when one round of it fills the device, else blocks over
+// balanced ranges of the flattened (unit, tile) index; the fp32 reduction
 // and both applies run (unit, token chunk) grids. The block and chunk counts
 // depend on the device (CU count and kernel occupancy); the workspace is
 // sized for the largest counts any device can pick.
@@ -30,6 +31,9 @@ struct Plan {
   int64_t tiles;          // 16-token tiles per unit, ceil(N / 16)
   // bf16 reduction: blocks and tiles per block (ranges of the flattened index)
   int64_t red_blocks, red_q;
+  // bf16 reduction on a (unit, chunk) grid instead: red_cb chunks of red_cq
+  // tiles per unit, one partial slot per chunk (red_cb = 0: balanced ranges)
+  int64_t red_cb, red_cq;
   int64_t slots;          // partial slots per unit the workspace holds
   // token chunks (fp32 reduction; apply of both dtypes)
   int64_t red_chunk;      // tokens per reduction chunk (multiple of kTile)
@@ -45,6 +49,11 @@ struct Plan {
   size_t ctl_bytes;       // workspace bytes for the per-unit control words
   size_t workspace_bytes; // total
 };
+
+// The slot rule of the bf16 reduction's partials: -chunks per unit on a
+// (unit, chunk) grid, else the tiles per balanced range (each unit's slot
+// count follows from it, see the kernels' slot_count).
+inline int64_t red_rule(const Plan& p) { return p.red_cb > 0 ? -p.red_cb : p.red_q; }
 
 // Device-independent part of the plan: sizes and the workspace layout.
 Plan make_plan(int64_t B, int64_t N, int64_t H);
@@ -81,9 +90,10 @@ int64_t qkv_m_tiles(int64_t N);
 int64_t qkv_grid_blocks(int64_t B, int64_t N, int64_t H);
 hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partials, int64_t B,
                             int64_t N, int64_t C, int64_t H, int64_t GM, hipStream_t stream);
-// Backward (bf16). bwd_q runs on the reduction's grid: it sums the partials of
-// launch_reduce(fold = false) for the state, writes dq and writes [dS | dz]
-// partials on the same slots; bwd_kv sums those and writes dk and dv.
+// Backward (bf16). bwd_q runs on balanced ranges: it sums the partials of
+// launch_reduce(fold = false) for the state (slots by red_rule), writes dq
+// and writes [dS | dz] partials on the balanced ranges' slots; bwd_kv sums
+// those and writes dk and dv.
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
                         const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream);
 hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,

@@ -953,6 +953,35 @@ __device__ __forceinline__ SlotRange slot_range(int64_t unit, int64_t T, int64_t
   return {first, ((unit + 1) * T - 1) / Qb - first + 1};
 }
 
+// Partial slots a unit's state is split into, by the rule `Qr` of the grid
+// that wrote them: Qr > 0, balanced ranges of Qr tiles (slot_range); Qr < 0,
+// a (unit, chunk) grid of -Qr chunks per unit, one slot per chunk; Qr = 0, a
+// single folded state.
+__device__ __forceinline__ int64_t slot_count(int64_t unit, int64_t T, int64_t Qr) {
+  return Qr > 0 ? slot_range(unit, T, Qr).count : (Qr < 0 ? -Qr : 1);
+}
+
+// XCD-grouped (unit, chunk) items. The hardware deals blocks to the XCDs
+// round robin (block g to XCD g % X on MI355X, X = 8), and each XCD has its
+// own L2. The units * C items, unit-major, are cut into X contiguous runs of
+// `per` = ceil(units * C / X) items; block g takes item g / X of run g % X.
+// Every XCD then gets the same number of blocks, and a unit's chunk blocks
+// share one L2 (or two, where a run boundary splits the unit), which fetches
+// the unit's partials about once instead of once per block. The grid is
+// X * per blocks; the few past the last item exit. X = 1 keeps the plain
+// order; the mapping is a bijection either way, only locality depends on X.
+struct Item {
+  int64_t unit, chunk;
+  bool valid;
+};
+__device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
+  const int64_t items = units * C;
+  const int64_t per = (items + X - 1) / X;
+  const int64_t item = (blockIdx.x % X) * per + blockIdx.x / X;
+  const int64_t unit = item / C;
+  return {unit, item - unit * C, item < items};
+}
+
 // State reduction over one block's range. For each unit it touches, the
 // block folds its waves' sums and writes them as partial number
 // (g - first block of the unit) of that unit. With Fold, the last of the
@@ -965,12 +994,23 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
     float* __restrict__ partials, float* __restrict__ state, unsigned long long* __restrict__ ctl,
     unsigned long long epoch, int64_t N, int64_t H, int64_t ld, int64_t pairs, int64_t T,
-    int64_t Qb, int64_t F, int64_t slots) {
+    int64_t Qb, int64_t F, int64_t slots, int64_t C, int64_t X) {
   __shared__ RedLds<S> lds;
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = blockIdx.x;
-  const int64_t f_lo = g * Qb;
-  const int64_t f_hi = f_lo + Qb < F ? f_lo + Qb : F;
+  // C > 0: (unit, chunk) items of Qb tiles, C = ceil(T / Qb) chunks per unit,
+  // in XCD runs (xcd_item); the chunk is the slot. C = 0: balanced ranges.
+  int64_t f_lo, f_hi, chunk = 0;
+  if (C > 0) {
+    const Item it = xcd_item(F / T, C, X);
+    if (!it.valid) return;  // the whole block
+    chunk = it.chunk;
+    f_lo = it.unit * T + it.chunk * Qb;
+    f_hi = f_lo + Qb < (it.unit + 1) * T ? f_lo + Qb : (it.unit + 1) * T;
+  } else {
+    f_lo = g * Qb;
+    f_hi = f_lo + Qb < F ? f_lo + Qb : F;
+  }
   for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
     const int64_t base = sg.b * N * ld + sg.h * kD;
@@ -978,12 +1018,20 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     float ks[2] = {0.0f, 0.0f};
     reduce_pair_wave<U, Fm>(K, V, ld, base, sg.n_lo, sg.n_hi, sub, S, sg.two, lds.slot[sub],
                             acc, ks);
-    const SlotRange sr = slot_range(unit, T, Qb);
-    float* part = partials + ((unit * slots) + (g - sr.first)) * 2 * kSF;
+    int64_t slot, count;
+    if (C > 0) {
+      slot = chunk;
+      count = C;
+    } else {
+      const SlotRange sr = slot_range(unit, T, Qb);
+      slot = g - sr.first;
+      count = sr.count;
+    }
+    float* part = partials + ((unit * slots) + slot) * 2 * kSF;
     block_sum_state<S, Fold>(acc, ks, lds.xchg, sub, part, sg.two);
-    if (Fold && arrive_last(ctl + unit, epoch, sr.count))
+    if (Fold && arrive_last(ctl + unit, epoch, count))
       fold_partials(partials + unit * slots * 2 * kSF, 2 * kSF, state + (sg.b * H + sg.h) * kSF,
-                    (sg.two ? 2 : 1) * kSF, sr.count);
+                    (sg.two ? 2 : 1) * kSF, count);
     __syncthreads();  // the LDS is reused by the next segment
   }
 }
@@ -1049,34 +1097,14 @@ __device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, i
   if (threadIdx.x + blockDim.x < n4) stage[threadIdx.x + blockDim.x] = a1;
 }
 
-// XCD-grouped (unit, chunk) items. The hardware deals blocks to the XCDs
-// round robin (block g to XCD g % X on MI355X, X = 8), and each XCD has its
-// own L2. The units * C items, unit-major, are cut into X contiguous runs of
-// `per` = ceil(units * C / X) items; block g takes item g / X of run g % X.
-// Every XCD then gets the same number of blocks, and a unit's chunk blocks
-// share one L2 (or two, where a run boundary splits the unit), which fetches
-// the unit's partials about once instead of once per block. The grid is
-// X * per blocks; the few past the last item exit. X = 1 keeps the plain
-// order; the mapping is a bijection either way, only locality depends on X.
-struct Item {
-  int64_t unit, chunk;
-  bool valid;
-};
-__device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
-  const int64_t items = units * C;
-  const int64_t per = (items + X - 1) / X;
-  const int64_t item = (blockIdx.x % X) * per + blockIdx.x / X;
-  const int64_t unit = item / C;
-  return {unit, item - unit * C, item < items};
-}
 
 // Apply, one block per (unit, token chunk of Qa tiles), C chunks per unit,
 // grouped by XCD (xcd_item).
 // The state of a unit is the sum of `count`
 // consecutive [2][d][d+1] slots at src + b * sb + p * sp (+ j * 2 * kSF),
-// count from slot_range(unit, T, Qr) when Qr > 0 (the partials of the
-// reduction, summed here in ascending slot order, as fold_partials does), -Qr
-// when Qr < 0 (a fixed number of slots per unit), else 1 (a folded state).
+// count = slot_count(unit, T, Qr): the partials of the reduction (balanced
+// ranges or a (unit, chunk) grid), summed here in ascending slot order, as
+// fold_partials does; a fixed number of slots per unit; or 1, a folded state.
 // The block sums them once into LDS; each wave then builds
 // its MFMA operands from there. q has token stride ld (as k and v in
 // reduce_bf16_kernel); the output is contiguous [B][N][H][d].
@@ -1096,7 +1124,7 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
   const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
   {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
-    const int64_t count = Qr > 0 ? slot_range(unit, T, Qr).count : (Qr < 0 ? -Qr : 1);
+    const int64_t count = slot_count(unit, T, Qr);
     const f32x4* st = reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp);
     const int n4 = (sg.two ? 2 : 1) * kSF / 4;
     auto make_ops = [&](ApplyOperands (&op)[2]) {
@@ -1585,17 +1613,17 @@ struct StateOps {
   }
 };
 
-// bwd_q over one block's range of the flattened (unit, tile) index (the
-// forward reduction's grid): the forward state of a unit is the sum of the
-// reduction's partials fwd_parts (same grid, so the same slots), and the
-// block writes its [dS | dz] partial of each unit it touches to grad_parts
-// (partial g - first, like the reduction).
+// bwd_q over one block's range of the flattened (unit, tile) index
+// (balanced ranges of Qb tiles): the forward state of a unit is the sum of
+// the reduction's partials fwd_parts (slots by rule Qf, see slot_count), and
+// the block writes its [dS | dz] partial of each unit it touches to
+// grad_parts (partial g - first, like the balanced reduction).
 template <int S, int U>
 __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ G,
     unsigned short* __restrict__ dQ, const float* __restrict__ fwd_parts,
     float* __restrict__ grad_parts, float eps, int64_t N, int64_t H, int64_t pairs, int64_t T,
-    int64_t Qb, int64_t F, int64_t slots) {
+    int64_t Qb, int64_t F, int64_t slots, int64_t Qf) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
   union alignas(16) Lds {
     BwdQWaveLds wave[S];
@@ -1611,7 +1639,7 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
     const SlotRange sr = slot_range(unit, T, Qb);
     const StateOps ops{reinterpret_cast<const f32x4*>(fwd_parts + unit * slots * 2 * kSF),
-                       sr.count, sg.two, stage};
+                       slot_count(unit, T, Qf), sg.two, stage};
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
     grad_q_pair_wave<U>(Q, G, dQ, ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
@@ -1643,7 +1671,7 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
   const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
   const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
   const StateOps ops{reinterpret_cast<const f32x4*>(grad_parts + unit * slots * 2 * kSF),
-                     slot_range(unit, T, Qr).count, sg.two, stage};
+                     slot_count(unit, T, Qr), sg.two, stage};
   grad_kv_pair_wave<U>(K, V, dK, dV, ops, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi,
                        sub, S, sg.two, tiles[sub]);
 }
@@ -1656,7 +1684,7 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
 // apply, this kernel turns block states into inclusive prefix sums over the
 // F blocks of each batch item. Unit u = (b * F + f) * pairs + p of that plan
 // has the state sum_{j < count} src[b' * sb + p * sp + j * 2 * kSF + e]
-// (b' = b * F + f; count from slot_range(u, T, Qr) when Qr > 0, else 1).
+// (b' = b * F + f; count = slot_count(u, T, Qr), 1 for a folded state).
 // Thread (b, p, e) walks f = 0 .. F-1, adds block f's element e (slots in
 // ascending order) to its running sum and writes the sum to
 // dst[(b' * H + h) * kSF + e % kSF], the [B * F][H][d][d+1] layout the apply
@@ -1677,7 +1705,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_block_states_kernel(
   float run = 0.0f;
   for (int64_t f = 0; f < F; ++f) {
     const int64_t b2 = b * F + f;
-    const int64_t count = Qr > 0 ? slot_range(b2 * pairs + p, T, Qr).count : 1;
+    const int64_t count = slot_count(b2 * pairs + p, T, Qr);
     const float* x = src + b2 * sb + p * sp + e;
     float sum = x[0];
     for (int64_t j = 1; j < count; ++j) sum += x[j * 2 * kSF];
@@ -1756,10 +1784,14 @@ hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, con
     if (dtype == 1) {
       auto* kernel = fold ? reduce_bf16_kernel<kRedS, kRedU, true, kFmapRelu>
                           : reduce_bf16_kernel<kRedS, kRedU, false, Fm>;
-      hipLaunchKernelGGL(kernel, dim3((unsigned)p.red_blocks), dim3(64 * kRedS), 0, stream,
+      const bool chunked = p.red_cb > 0;
+      const int64_t X = apply_xcds(p);
+      const int64_t blocks = chunked ? xcd_grid(p.units * p.red_cb, X) : p.red_blocks;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * kRedS), 0, stream,
                          static_cast<const unsigned short*>(k),
                          static_cast<const unsigned short*>(v), partials, state, ctl, epoch, p.N,
-                         p.H, p.ld, p.pairs, p.tiles, p.red_q, p.units * p.tiles, p.slots);
+                         p.H, p.ld, p.pairs, p.tiles, chunked ? p.red_cq : p.red_q,
+                         p.units * p.tiles, p.slots, chunked ? p.red_cb : int64_t(0), X);
     } else {
       hipLaunchKernelGGL((reduce_f32_kernel<kF32S, kF32U, Fm>),
                          dim3((unsigned)(p.units * p.red_chunks)), dim3(128 * kF32S), 0, stream,
@@ -1840,7 +1872,7 @@ hipError_t launch_apply_partials(const Plan& p, const void* q, const float* part
     hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>),
                        dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
                        kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
-                       p.pairs * sp, sp, p.red_q, static_cast<unsigned short*>(out), eps, p.N, p.H,
+                       p.pairs * sp, sp, red_rule(p), static_cast<unsigned short*>(out), eps, p.N, p.H,
                        p.ld, p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
     return hipGetLastError();
   });
@@ -1864,7 +1896,7 @@ hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
                      dim3(64 * kBwqS), 0, stream, static_cast<const unsigned short*>(q),
                      static_cast<const unsigned short*>(g), static_cast<unsigned short*>(dq),
                      fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles, p.red_q,
-                     p.units * p.tiles, p.slots);
+                     p.units * p.tiles, p.slots, red_rule(p));
   return hipGetLastError();
 }
 
@@ -1888,7 +1920,7 @@ hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* 
   const int64_t sp = bf16 ? p.slots * 2 * kSF : int64_t(2 * kSF);
   hipLaunchKernelGGL(scan_block_states_kernel, dim3((unsigned)(B * p.pairs * kScanBlocksPerPair)),
                      dim3(kScanThreads), 0, stream, bf16 ? partials : state, sb, sp,
-                     bf16 ? p.red_q : int64_t(0), p.tiles, prefix, F, p.H, p.pairs);
+                     bf16 ? red_rule(p) : int64_t(0), p.tiles, prefix, F, p.H, p.pairs);
   return hipGetLastError();
 }
 
