@@ -35,13 +35,6 @@ import numpy as np
 from .linattn import phi, to_f64
 
 
-def block_of(n: int, L: int) -> np.ndarray:
-    """Block index of each of n tokens for blocks of L tokens."""
-    if L < 1:
-        raise ValueError("block length must be >= 1")
-    return np.arange(n) // L
-
-
 def block_states(k: np.ndarray, v: np.ndarray, L: int) -> np.ndarray:
     """Per-block augmented states phi(K_c)^T [V_c | 1] of one head:
     [blocks, d, d+1]."""

@@ -85,6 +85,64 @@ def _quadratic_loops(q, k, v, eps):
     return out
 
 
+def _exact_rational_out(q, k, v, eps, b, h, i, c):
+    """out[b, i, h, c] of the unreordered definition in exact rational arithmetic."""
+    relu = lambda x: max(Fraction(x), Fraction(0))  # noqa: E731
+    N, d = q.shape[1], q.shape[3]
+    w = [sum(relu(q[b, i, h, e]) * relu(k[b, j, h, e]) for e in range(d)) for j in range(N)]
+    return sum(w[j] * Fraction(v[b, j, h, c]) for j in range(N)) / (sum(w) + Fraction(eps))
+
+
+def pin_quadratic_exact_rational():
+    """The explicit n x n form (oracle.linattn.quadratic_fp64) against exact
+    rational arithmetic on dyadic inputs; the shapes have n >= 2 and q != k, so
+    a transposed weight matrix or a row sum over the key axis changes values."""
+    rng = np.random.default_rng(11)
+    for (B, N, H, d) in [(1, 2, 1, 3), (2, 3, 2, 4), (1, 5, 3, 5), (1, 7, 1, 8)]:
+        q, k, v = (rng.integers(-16, 17, size=(B, N, H, d)) / 8.0 for _ in range(3))
+        eps = 0.25
+        got = L.quadratic_fp64(q, k, v, eps)
+        for b in range(B):
+            for h in range(H):
+                for i in range(N):
+                    for c in range(d):
+                        exact = float(_exact_rational_out(q, k, v, eps, b, h, i, c))
+                        if abs(got[b, i, h, c] - exact) > 1e-14 * max(1.0, abs(exact)):
+                            return (f"quadratic form mismatch at {(b, i, h, c)}: "
+                                    f"{got[b, i, h, c]} vs {exact}")
+    return None
+
+
+def pin_quadratic_matches_loops():
+    """quadratic_fp64 against the n x n weights built by a loop over key tokens
+    (_quadratic_loops), on the tiny fp32 workload and random shapes; with a
+    single key token it reduces to v s / (s + eps); dead query rows give 0."""
+    w = W.WORKLOADS["tiny_f32"]
+    x = {t: W.generate_tensor(w, t).astype(np.float64) for t in "qkv"}
+    cases = [(x["q"], x["k"], x["v"], w.eps)]
+    rng = np.random.default_rng(13)
+    for n in (1, 2, 3, 17, 64):
+        cases.append(tuple(_rand((2, n, 3, 32), rng) for _ in range(3)) + (1e-3,))
+    for q, k, v, eps in cases:
+        a = L.quadratic_fp64(q, k, v, eps)
+        b = _quadratic_loops(q, k, v, eps)
+        if not np.all(np.isfinite(a)) or _rel(a, b) > 1e-12:
+            return f"quadratic form vs loop form rel error {_rel(a, b):.3g} at n={q.shape[1]}"
+    d = 32
+    q = np.full((1, 1, 1, d), -1.0)
+    k = np.full((1, 1, 1, d), -1.0)
+    q[0, 0, 0, 3], k[0, 0, 0, 3] = 0.5, 1.0   # s = 0.5 = eps: out = v / 2
+    v = _rand((1, 1, 1, d))
+    if not np.allclose(L.quadratic_fp64(q, k, v, 0.5), v / 2, rtol=1e-15, atol=0):
+        return "quadratic form: N = 1 closed form v s / (s + eps) violated"
+    q, k, v = (_rand((1, 20, 2, 32)) for _ in range(3))
+    q[:, ::4] = -np.abs(q[:, ::4])
+    got = L.quadratic_fp64(q, k, v, 1e-6)
+    if np.any(got[:, ::4] != 0) or np.any(np.all(got[:, 1::4] == 0, axis=-1)):
+        return "quadratic form: dead query rows not exactly zero (or live rows zero)"
+    return None
+
+
 def pin_single_token():
     """N = 1: out = v * s / (s + eps), s = phi(q).phi(k). Chosen with s = eps so
     that the eps placement matters: out = v / 2."""
@@ -250,7 +308,8 @@ def pin_eps_zero_dead_row():
 
 
 PINS = [
-    pin_exact_rational, pin_quadratic_form, pin_single_token, pin_constant_inputs,
+    pin_exact_rational, pin_quadratic_form, pin_quadratic_exact_rational,
+    pin_quadratic_matches_loops, pin_single_token, pin_constant_inputs,
     pin_one_hot_query, pin_convex_bound, pin_positive_scaling, pin_dead_query_rows,
     pin_dead_key_tokens, pin_permutation, pin_linearity_in_v, pin_independence,
     pin_eps_zero_dead_row,
@@ -327,6 +386,26 @@ def _mut_forward(kind):
     return linattn_fp64
 
 
+def _mut_quadratic(kind):
+    def quadratic_fp64(q, k, v, eps):
+        B, N, H, d = q.shape
+        out = np.empty((B, N, H, d))
+        for b in range(B):
+            for h in range(H):
+                pk = k[b, :, h, :] if kind == "quad_k_no_relu" else L.phi(k[b, :, h, :])
+                w = L.phi(q[b, :, h, :]) @ pk.T
+                if kind == "quad_w_transposed":
+                    w = w.T
+                r = w.sum(axis=0) if kind == "quad_rowsum_axis0" else w.sum(axis=1)
+                den = r if kind == "quad_eps_dropped" else r + eps
+                num = w @ v[b, :, h, :]
+                if kind == "quad_v_from_q":
+                    num = w @ q[b, :, h, :]
+                out[b, :, h, :] = num / den[:, None]
+        return out
+    return quadratic_fp64
+
+
 MUTANTS = {
     "phi_identity": ("phi", lambda x: np.asarray(x, dtype=np.float64)),
     "phi_abs": ("phi", np.abs),
@@ -346,6 +425,11 @@ MUTANTS = {
     "wrong_head": ("linattn_fp64", _mut_forward("wrong_head")),
     "batch_mixed": ("linattn_fp64", _mut_forward("batch_mixed")),
     "q_k_swapped": ("linattn_fp64", _mut_forward("q_k_swapped")),
+    "quad_eps_dropped": ("quadratic_fp64", _mut_quadratic("quad_eps_dropped")),
+    "quad_w_transposed": ("quadratic_fp64", _mut_quadratic("quad_w_transposed")),
+    "quad_rowsum_axis0": ("quadratic_fp64", _mut_quadratic("quad_rowsum_axis0")),
+    "quad_k_no_relu": ("quadratic_fp64", _mut_quadratic("quad_k_no_relu")),
+    "quad_v_from_q": ("quadratic_fp64", _mut_quadratic("quad_v_from_q")),
 }
 
 

@@ -22,6 +22,32 @@ def _rel(a, b):
     return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
 
 
+def pin_masked_form_exact():
+    """The masked n x n form itself (masked_quadratic_fp64, the reference of
+    the next pin) against exact rational arithmetic on dyadic inputs with a
+    non-symmetric 0/1 mask: out_i = sum_n m_in w_in v_n / (sum_n m_in w_in + eps)."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(21)
+    B, N, H, d = 1, 6, 2, 4
+    q, k, v = (rng.integers(-16, 17, size=(B, N, H, d)) / 8.0 for _ in range(3))
+    mask = (rng.random((N, N)) < 0.6).astype(np.float64)
+    mask[0] = 0.0          # a query that sees nothing: out = 0
+    eps = 0.25
+    got = BC.masked_quadratic_fp64(q, k, v, mask, eps)
+    relu = lambda x: max(Fraction(x), Fraction(0))  # noqa: E731
+    for h in range(H):
+        for i in range(N):
+            w = [int(mask[i, j]) * sum(relu(q[0, i, h, e]) * relu(k[0, j, h, e]) for e in range(d))
+                 for j in range(N)]
+            for c in range(d):
+                exact = float(sum(w[j] * Fraction(v[0, j, h, c]) for j in range(N))
+                              / (sum(w) + Fraction(eps)))
+                if abs(got[0, i, h, c] - exact) > 1e-14 * max(1.0, abs(exact)):
+                    return f"masked form mismatch at {(i, h, c)}: {got[0, i, h, c]} vs {exact}"
+    return None
+
+
 def pin_masked_quadratic():
     """Against the explicit masked n x n form, including a ragged last block."""
     eps = 1e-3
@@ -82,14 +108,31 @@ def pin_causality():
     return None
 
 
-PINS = [pin_masked_quadratic, pin_one_block_is_noncausal, pin_token_causal,
-        pin_first_block_alone, pin_causality]
+PINS = [pin_masked_form_exact, pin_masked_quadratic, pin_one_block_is_noncausal,
+        pin_token_causal, pin_first_block_alone, pin_causality]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
 def test_pin_holds(pin):
     msg = pin()
     assert msg is None, msg
+
+
+def _mut_masked(kind):
+    def masked_quadratic_fp64(q, k, v, mask, eps):
+        B, N, H, d = q.shape
+        out = np.empty((B, N, H, d))
+        for b in range(B):
+            for h in range(H):
+                w = L.phi(q[b, :, h]) @ L.phi(k[b, :, h]).T
+                m = mask.T if kind == "mask_transposed" else mask
+                w = w if kind == "mask_ignored" else w * m
+                r = w.sum(axis=1)
+                if kind == "den_unmasked":
+                    r = (L.phi(q[b, :, h]) @ L.phi(k[b, :, h]).T).sum(axis=1)
+                out[b, :, h] = (w @ v[b, :, h]) / (r + eps)[:, None]
+        return out
+    return masked_quadratic_fp64
 
 
 def _mut_prefix(kind):
@@ -149,6 +192,9 @@ MUTANTS = {
     "no_ones_column": ("block_states", _mut_block_states("no_ones")),
     "previous_block_state": ("apply_prefix", _mut_apply("previous_block")),
     "whole_sequence_state": ("apply_prefix", _mut_apply("last_prefix")),
+    "mask_transposed": ("masked_quadratic_fp64", _mut_masked("mask_transposed")),
+    "mask_ignored": ("masked_quadratic_fp64", _mut_masked("mask_ignored")),
+    "den_unmasked": ("masked_quadratic_fp64", _mut_masked("den_unmasked")),
 }
 
 
