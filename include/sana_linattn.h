@@ -32,7 +32,9 @@
  * Ownership. Every pointer is a device pointer owned by the caller (q, k, v,
  * out, state, workspace). The library allocates no device memory and keeps no
  * per-call state. q, k and v are only read. out must not overlap q, k, v, the
- * state or the workspace.
+ * state or the workspace, and a workspace must not overlap any tensor of the
+ * call, inputs included (its partial results are written while other blocks
+ * still read the inputs); a detected overlap returns SANA_ERR_INVALID_ARG.
  *
  * Streams. Every call enqueues its kernels on `stream` (NULL = the default
  * stream) and returns without synchronising. Results are defined once the
@@ -110,7 +112,7 @@ typedef enum {
  * argument error (same checks as the forward call).
  */
 sana_status_t sana_linattn_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
-                                          int dtype, size_t* bytes);
+                                          sana_dtype_t dtype, size_t* bytes);
 
 /*
  * The forward pass: out = phi(Q)(phi(K)^T [V|1]) split into numerator and
@@ -123,7 +125,7 @@ sana_status_t sana_linattn_workspace_size(int64_t B, int64_t N, int64_t H, int64
  */
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out,
                                int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                               int dtype, void* workspace, size_t workspace_bytes,
+                               sana_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
 /*
@@ -133,7 +135,7 @@ sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void
  */
 sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void* v, void* out,
                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                       int dtype, int variant, void* workspace,
+                                       sana_dtype_t dtype, sana_variant_t variant, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -150,7 +152,7 @@ sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void*
  */
 sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void* v, void* out,
                                         int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                        int dtype, int variant, void* workspace,
+                                        sana_dtype_t dtype, sana_variant_t variant, void* workspace,
                                         size_t workspace_bytes, hipEvent_t* events,
                                         int n_events, int* n_kernels, hipStream_t stream);
 
@@ -169,7 +171,7 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
  */
 sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v, void* out,
                                     int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                    int dtype, int fmap, void* workspace, size_t workspace_bytes,
+                                    sana_dtype_t dtype, sana_fmap_t fmap, void* workspace, size_t workspace_bytes,
                                     hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
@@ -192,7 +194,7 @@ sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v,
  */
 sana_status_t sana_linattn_fwd_strided(const void* q, const void* k, const void* v, int64_t ld,
                                        void* out, int64_t B, int64_t N, int64_t H, int64_t d,
-                                       float eps, int dtype, int fmap, void* workspace,
+                                       float eps, sana_dtype_t dtype, sana_fmap_t fmap, void* workspace,
                                        size_t workspace_bytes, hipEvent_t* events, int n_events,
                                        hipStream_t stream);
 
@@ -242,7 +244,7 @@ sana_status_t sana_linattn_qkv_fwd(const void* x, const void* w_qkv, void* q, vo
  * token ranges sum to the state of their union.
  */
 sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state,
-                                    int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
+                                    int64_t B, int64_t N, int64_t H, int64_t d, sana_dtype_t dtype,
                                     void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
@@ -254,12 +256,11 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state,
  */
 sana_status_t sana_linattn_apply(const void* q, const float* state, void* out,
                                  int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                 int dtype, hipStream_t stream);
+                                 sana_dtype_t dtype, hipStream_t stream);
 
 /* Bytes of one [B][H][d][d+1] fp32 state (0 and SANA_ERR_* on bad arguments). */
 sana_status_t sana_linattn_state_size(int64_t B, int64_t H, int64_t d, size_t* bytes);
 
-/* Static, human-readable name of a status code ("unknown status" otherwise). */
 /*
  * Backward pass (bf16 only). Given g = dL/dout for the forward pass with the
  * same q, k, v and eps, writes dq = dL/dq, dk = dL/dk, dv = dL/dv, per (b, h):
@@ -286,10 +287,10 @@ sana_status_t sana_linattn_state_size(int64_t B, int64_t H, int64_t d, size_t* b
  * any HIP call; three kernels are enqueued on `stream`.
  */
 sana_status_t sana_linattn_bwd_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
-                                              int dtype, size_t* bytes);
+                                              sana_dtype_t dtype, size_t* bytes);
 sana_status_t sana_linattn_bwd(const void* q, const void* k, const void* v, const void* dout,
                                void* dq, void* dk, void* dv, int64_t B, int64_t N, int64_t H,
-                               int64_t d, float eps, int dtype, void* workspace,
+                               int64_t d, float eps, sana_dtype_t dtype, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -301,7 +302,7 @@ sana_status_t sana_linattn_bwd(const void* q, const void* k, const void* v, cons
 sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void* v,
                                         const void* dout, void* dq, void* dk, void* dv,
                                         int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                        int dtype, void* workspace, size_t workspace_bytes,
+                                        sana_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                         hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
@@ -325,11 +326,11 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
  * (fixed order: results are bitwise repeatable), the apply.
  */
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,
-                                                      int64_t d, int64_t block, int dtype,
+                                                      int64_t d, int64_t block, sana_dtype_t dtype,
                                                       size_t* bytes);
 sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const void* v,
                                             void* out, int64_t B, int64_t N, int64_t H,
-                                            int64_t d, int64_t block, float eps, int dtype,
+                                            int64_t d, int64_t block, float eps, sana_dtype_t dtype,
                                             void* workspace, size_t workspace_bytes,
                                             hipStream_t stream);
 /* The same, recording events[0] before and events[1..3] after its three
@@ -337,11 +338,13 @@ sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const 
 sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* k, const void* v,
                                                      void* out, int64_t B, int64_t N, int64_t H,
                                                      int64_t d, int64_t block, float eps,
-                                                     int dtype, void* workspace,
+                                                     sana_dtype_t dtype, void* workspace,
                                                      size_t workspace_bytes, hipEvent_t* events,
                                                      int n_events, hipStream_t stream);
 
-const char* sana_linattn_strerror(int status);
+/* Static, human-readable name of a status code ("unknown status" for a value
+ * outside sana_status_t). Never NULL; the string is owned by the library. */
+const char* sana_linattn_strerror(sana_status_t status);
 
 /* SANA_LINATTN_VERSION of the built library. */
 int sana_linattn_version(void);

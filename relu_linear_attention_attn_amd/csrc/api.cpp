@@ -12,6 +12,8 @@
 #include <cstring>
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <random>
 #include <mutex>
 
 #include "linattn_internal.h"
@@ -215,32 +217,17 @@ void fit_plan_to_device(Plan& p, int dtype) {
     const int64_t want = cdiv(waves, p.units * block_waves(KernelKind::kReduce, dtype));
     int64_t rc = clamp64(std::min(want, std::max<int64_t>(1, rcap / p.units)), 1,
                          p.red_chunks_max);
-#ifdef SANA_TUNING
-    if (const char* e = getenv("SANA_F32_RED_CHUNKS")) rc = clamp64(atoll(e), 1, p.red_chunks_max);
-#endif
     p.red_chunk = chunk_tokens(p.N, rc);
     p.red_chunks = cdiv(p.N, p.red_chunk);
   }
   // apply and backward k/v pass: (unit, chunk) grids, each for its kernel's
   // occupancy
   int64_t ac = grid_chunks(p.units, p.N, acap);
-#ifdef SANA_TUNING
-  if (const char* e = getenv("SANA_APP_CHUNKS")) ac = std::max<int64_t>(1, atoll(e));
-#endif
   p.app_chunk = chunk_tokens(p.N, ac);
   p.app_chunks = cdiv(p.N, p.app_chunk);
   int64_t bc = grid_chunks(p.units, p.N, static_cast<int64_t>(c.cus) * c.occ_bwd_kv);
-#ifdef SANA_TUNING
-  if (const char* e = getenv("SANA_BKV_CHUNKS")) bc = std::max<int64_t>(1, atoll(e));
-#endif
   p.bkv_chunk = chunk_tokens(p.N, bc);
   p.bkv_chunks = cdiv(p.N, p.bkv_chunk);
-#ifdef SANA_TUNING
-  if (getenv("SANA_PRINT_PLAN"))
-    fprintf(stderr, "plan cus %d occ red %d app %d | red blocks %lld q %lld | app chunks %lld chunk %lld\n",
-            c.cus, c.occ[0][dt], c.occ[1][dt], (long long)p.red_blocks, (long long)p.red_q,
-            (long long)p.app_chunks, (long long)p.app_chunk);
-#endif
 }
 
 namespace {
@@ -275,8 +262,16 @@ int resolve_variant(const Plan& p, int variant) {
 int kernels_of(int variant) { return variant == SANA_VARIANT_SPLIT ? 2 : 1; }
 
 // A fresh tag per call for the per-pair control words (48 bits; never 0).
+// The count starts at a per-process random value, so a control word left in
+// a reused workspace by another process or another copy of the library is
+// unlikely to carry the tag of a call here.
 unsigned long long next_epoch() {
-  static std::atomic<unsigned long long> counter{0};
+  static std::atomic<unsigned long long> counter{[] {
+    std::random_device rd;
+    return (static_cast<unsigned long long>(rd()) << 32) ^ rd() ^
+           static_cast<unsigned long long>(
+               std::chrono::steady_clock::now().time_since_epoch().count());
+  }()};
   unsigned long long e;
   do {
     e = (counter.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
@@ -304,7 +299,7 @@ using sana::Plan;
 
 extern "C" {
 
-sana_status_t sana_linattn_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
+sana_status_t sana_linattn_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d, sana_dtype_t dtype,
                                           size_t* bytes) {
   if (!bytes) return SANA_ERR_INVALID_ARG;
   *bytes = 0;
@@ -383,7 +378,13 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
       overlaps(out, tb, v, in_bytes))
     return SANA_ERR_INVALID_ARG;
   if ((s = check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
-  if (overlaps(out, tb, workspace, p.workspace_bytes)) return SANA_ERR_INVALID_ARG;
+  // the reduction writes partials while other blocks still read k and v, and
+  // the apply writes out: the workspace may alias no tensor
+  if (overlaps(out, tb, workspace, p.workspace_bytes) ||
+      overlaps(workspace, p.workspace_bytes, q, in_bytes) ||
+      overlaps(workspace, p.workspace_bytes, k, in_bytes) ||
+      overlaps(workspace, p.workspace_bytes, v, in_bytes))
+    return SANA_ERR_INVALID_ARG;
 
   // every check passed: from here on HIP is called
   (void)hipGetLastError();  // clear an unrelated earlier error
@@ -457,7 +458,8 @@ sana_status_t block_causal(const void* q, const void* k, const void* v, void* ou
     return SANA_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < bc.workspace_bytes) return SANA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
-  if (overlaps(out, tb, workspace, bc.workspace_bytes)) return SANA_ERR_INVALID_ARG;
+  for (const void* t : {static_cast<const void*>(out), q, k, v})
+    if (overlaps(t, tb, workspace, bc.workspace_bytes)) return SANA_ERR_INVALID_ARG;
 
   (void)hipGetLastError();
   Plan fp = bc.p;
@@ -539,16 +541,15 @@ sana_status_t qkv_forward(const void* x, const void* w, void* q, void* out, int6
   if (!workspace || workspace_bytes < qp.workspace_bytes) return SANA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
   if (overlaps(workspace, qp.workspace_bytes, q, tb) ||
-      overlaps(workspace, qp.workspace_bytes, out, tb))
+      overlaps(workspace, qp.workspace_bytes, out, tb) ||
+      overlaps(workspace, qp.workspace_bytes, x, qp.x_bytes) ||
+      overlaps(workspace, qp.workspace_bytes, w, qp.w_bytes))
     return SANA_ERR_INVALID_ARG;
 
   (void)hipGetLastError();
   Plan fp = qp.p;
   fit_plan_to_device(fp, SANA_DTYPE_BF16);
   int64_t gm = kQkvGroupM;
-#ifdef SANA_TUNING
-  if (const char* e = getenv("SANA_QKV_GM")) gm = std::max<int64_t>(1, atoll(e));
-#endif
   float* partials = static_cast<float*>(workspace);
   auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
   if (!mark(0)) return SANA_ERR_HIP;
@@ -591,7 +592,10 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
   const size_t wb = bwd_workspace_bytes(p);
   if (!workspace || workspace_bytes < wb) return SANA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
-  // an output may overlap nothing else (inputs may alias each other)
+  // an output may overlap nothing else (inputs may alias each other), and the
+  // workspace no tensor
+  for (const void* x : in)
+    if (overlaps(workspace, wb, x, tb)) return SANA_ERR_INVALID_ARG;
   for (int i = 0; i < 3; ++i) {
     for (const void* x : in)
       if (overlaps(outs[i], tb, x, tb)) return SANA_ERR_INVALID_ARG;
@@ -625,7 +629,7 @@ extern "C" {
 
 sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void* v, void* out,
                                        int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                       int dtype, int variant, void* workspace,
+                                       sana_dtype_t dtype, sana_variant_t variant, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream) {
   return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, variant, workspace, workspace_bytes,
                        nullptr, 0, nullptr, stream);
@@ -633,7 +637,7 @@ sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void*
 
 sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void* v, void* out,
                                         int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                        int dtype, int variant, void* workspace,
+                                        sana_dtype_t dtype, sana_variant_t variant, void* workspace,
                                         size_t workspace_bytes, hipEvent_t* events,
                                         int n_events, int* n_kernels, hipStream_t stream) {
   if (!events) {
@@ -651,7 +655,7 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
 
 sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v, void* out,
                                     int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                    int dtype, int fmap, void* workspace, size_t workspace_bytes,
+                                    sana_dtype_t dtype, sana_fmap_t fmap, void* workspace, size_t workspace_bytes,
                                     hipEvent_t* events, int n_events, hipStream_t stream) {
   return sana::forward(q, k, v, out, B, N, H, d, eps, dtype, SANA_VARIANT_SPLIT, workspace,
                        workspace_bytes, events, n_events, nullptr, stream, fmap);
@@ -659,7 +663,7 @@ sana_status_t sana_linattn_fwd_fmap(const void* q, const void* k, const void* v,
 
 sana_status_t sana_linattn_fwd_strided(const void* q, const void* k, const void* v, int64_t ld,
                                        void* out, int64_t B, int64_t N, int64_t H, int64_t d,
-                                       float eps, int dtype, int fmap, void* workspace,
+                                       float eps, sana_dtype_t dtype, sana_fmap_t fmap, void* workspace,
                                        size_t workspace_bytes, hipEvent_t* events, int n_events,
                                        hipStream_t stream) {
   if (ld < 1) return SANA_ERR_INVALID_ARG;
@@ -668,14 +672,14 @@ sana_status_t sana_linattn_fwd_strided(const void* q, const void* k, const void*
 }
 
 sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
-                               int64_t N, int64_t H, int64_t d, float eps, int dtype,
+                               int64_t N, int64_t H, int64_t d, float eps, sana_dtype_t dtype,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return sana_linattn_fwd_variant(q, k, v, out, B, N, H, d, eps, dtype, SANA_VARIANT_AUTO,
                                   workspace, workspace_bytes, stream);
 }
 
 sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, int64_t B,
-                                    int64_t N, int64_t H, int64_t d, int dtype, void* workspace,
+                                    int64_t N, int64_t H, int64_t d, sana_dtype_t dtype, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
   size_t tb = 0;
   sana_status_t s = sana::check_shape(B, N, H, d, dtype, &tb);
@@ -687,7 +691,9 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, 
   if ((s = sana::check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
   const size_t sb = static_cast<size_t>(B * H) * sana::kStateFloats * 4;
   if (sana::overlaps(state, sb, k, tb) || sana::overlaps(state, sb, v, tb) ||
-      sana::overlaps(state, sb, workspace, p.workspace_bytes))
+      sana::overlaps(state, sb, workspace, p.workspace_bytes) ||
+      sana::overlaps(workspace, p.workspace_bytes, k, tb) ||
+      sana::overlaps(workspace, p.workspace_bytes, v, tb))
     return SANA_ERR_INVALID_ARG;
   (void)hipGetLastError();
   Plan fp = p;
@@ -698,7 +704,7 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, 
 }
 
 sana_status_t sana_linattn_apply(const void* q, const float* state, void* out, int64_t B,
-                                 int64_t N, int64_t H, int64_t d, float eps, int dtype,
+                                 int64_t N, int64_t H, int64_t d, float eps, sana_dtype_t dtype,
                                  hipStream_t stream) {
   size_t tb = 0;
   sana_status_t s = sana::check_shape(B, N, H, d, dtype, &tb);
@@ -717,7 +723,7 @@ sana_status_t sana_linattn_apply(const void* q, const float* state, void* out, i
 }
 
 sana_status_t sana_linattn_bwd_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
-                                              int dtype, size_t* bytes) {
+                                              sana_dtype_t dtype, size_t* bytes) {
   if (!bytes) return SANA_ERR_INVALID_ARG;
   *bytes = 0;
   const sana_status_t s = sana::check_shape(B, N, H, d, dtype, nullptr);
@@ -729,7 +735,7 @@ sana_status_t sana_linattn_bwd_workspace_size(int64_t B, int64_t N, int64_t H, i
 
 sana_status_t sana_linattn_bwd(const void* q, const void* k, const void* v, const void* dout,
                                void* dq, void* dk, void* dv, int64_t B, int64_t N, int64_t H,
-                               int64_t d, float eps, int dtype, void* workspace,
+                               int64_t d, float eps, sana_dtype_t dtype, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
   return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
                         workspace_bytes, nullptr, 0, stream);
@@ -738,7 +744,7 @@ sana_status_t sana_linattn_bwd(const void* q, const void* k, const void* v, cons
 sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void* v,
                                         const void* dout, void* dq, void* dk, void* dv,
                                         int64_t B, int64_t N, int64_t H, int64_t d, float eps,
-                                        int dtype, void* workspace, size_t workspace_bytes,
+                                        sana_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                         hipEvent_t* events, int n_events, hipStream_t stream) {
   if (!events) return SANA_ERR_INVALID_ARG;
   return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
@@ -746,7 +752,7 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
 }
 
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,
-                                                      int64_t d, int64_t block, int dtype,
+                                                      int64_t d, int64_t block, sana_dtype_t dtype,
                                                       size_t* bytes) {
   if (!bytes) return SANA_ERR_INVALID_ARG;
   *bytes = 0;
@@ -759,7 +765,7 @@ sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int
 
 sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const void* v,
                                             void* out, int64_t B, int64_t N, int64_t H,
-                                            int64_t d, int64_t block, float eps, int dtype,
+                                            int64_t d, int64_t block, float eps, sana_dtype_t dtype,
                                             void* workspace, size_t workspace_bytes,
                                             hipStream_t stream) {
   return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
@@ -769,7 +775,7 @@ sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const 
 sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* k, const void* v,
                                                      void* out, int64_t B, int64_t N, int64_t H,
                                                      int64_t d, int64_t block, float eps,
-                                                     int dtype, void* workspace,
+                                                     sana_dtype_t dtype, void* workspace,
                                                      size_t workspace_bytes, hipEvent_t* events,
                                                      int n_events, hipStream_t stream) {
   if (!events) return SANA_ERR_INVALID_ARG;
@@ -796,7 +802,7 @@ sana_status_t sana_linattn_qkv_fwd(const void* x, const void* w_qkv, void* q, vo
                            events, n_events, stream);
 }
 
-const char* sana_linattn_strerror(int status) {
+const char* sana_linattn_strerror(sana_status_t status) {
   switch (status) {
     case SANA_OK: return "success";
     case SANA_ERR_INVALID_ARG: return "invalid argument";

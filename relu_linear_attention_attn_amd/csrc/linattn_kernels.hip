@@ -31,8 +31,9 @@
 //           8 consecutive output channels of one token: one 16-byte store.
 //           The denominator comes from a third tile whose A rows all equal
 //           ksum, so it lands in the same lane and register as its numerator.
-// fp32 path: plain VALU FMA kernels with the same work split (exact fp32
-// products, for the fp32 contract; not the throughput path).
+// fp32 path: the same two halves on fp32 MFMA (v_mfma_f32_32x32x2f32: exact
+// fp32 products and fp32 sums, for the fp32 contract) over 32-token tiles of
+// one head.
 
 #include <hip/hip_runtime.h>
 
@@ -706,10 +707,7 @@ __device__ __forceinline__ void stage_state_padded(float* dst, const float* st) 
 // over the banks), then the output tile [token][channel] (pitch 36 floats,
 // 16-byte rows for the line reads), and 1 / den per token.
 constexpr int kF32QPitch = 33, kF32OPitch = 36;
-#ifndef SANA_F32_APP_U
-#define SANA_F32_APP_U 2
-#endif
-constexpr int kF32ApplyU = SANA_F32_APP_U;  // tiles in flight per wave
+constexpr int kF32ApplyU = 2;  // tiles in flight per wave
 constexpr int kF32ApplyLds = kF32Tile * kF32OPitch + kF32Tile;  // floats per wave
 
 // Applies one head's state to the tiles sub, sub + S, ... of 32 tokens of
@@ -1714,30 +1712,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_block_states_kernel(
   }
 }
 
-#ifndef SANA_RED_S
-#define SANA_RED_S 8
-#endif
-#ifndef SANA_RED_U
-#define SANA_RED_U 2
-#endif
-#ifndef SANA_APP_S
-#define SANA_APP_S 8
-#endif
-#ifndef SANA_APP_U
-#define SANA_APP_U 2
-#endif
-#ifndef SANA_BWQ_U
-#define SANA_BWQ_U 1
-#endif
-#ifndef SANA_BWKV_U
-#define SANA_BWKV_U 1
-#endif
-#ifndef SANA_BWKV_S
-#define SANA_BWKV_S 8
-#endif
 // token sub-streams per head (S) and tiles in flight per wave (U)
-constexpr int kRedS = SANA_RED_S, kRedU = SANA_RED_U;
-constexpr int kAppS = SANA_APP_S, kAppU = SANA_APP_U;
+constexpr int kRedS = 8, kRedU = 2;
+constexpr int kAppS = 8, kAppU = 2;
 // Dynamic LDS the bf16 apply requests on top of its own (about 25 KB), only
 // to hold it to one block (8 waves) per CU: with inputs that are not in the
 // Infinity Cache, 8 streaming waves per CU move this read + write mix faster
@@ -1745,20 +1722,14 @@ constexpr int kAppS = SANA_APP_S, kAppU = SANA_APP_U;
 // fewer concurrent streams contend for HBM rows.
 constexpr unsigned kApplyLdsPad = 64 << 10;
 constexpr int kFusS = 8, kFusU = 2;
-constexpr int kBwqS = 8, kBwqU = SANA_BWQ_U;
-constexpr int kBwkvS = SANA_BWKV_S, kBwkvU = SANA_BWKV_U;
+constexpr int kBwqS = 8, kBwqU = 1;
+constexpr int kBwkvS = 8, kBwkvU = 1;
 // XCDs of MI355X (the round-robin width of block dispatch). Fewer units than
 // that: plain order (a unit's chunks are spread over the XCDs anyway).
 constexpr int64_t kXcds = 8;
 int64_t apply_xcds(const Plan& p) { return p.units >= kXcds ? kXcds : 1; }
 int64_t xcd_grid(int64_t items, int64_t X) { return X * ((items + X - 1) / X); }
-#ifndef SANA_F32_S
-#define SANA_F32_S 4
-#endif
-#ifndef SANA_F32_U
-#define SANA_F32_U 2
-#endif
-constexpr int kF32S = SANA_F32_S, kF32U = SANA_F32_U;
+constexpr int kF32S = 4, kF32U = 2;
 
 // Runs f(std::integral_constant<int, Fm>) for the feature map fmap.
 template <class F>

@@ -359,3 +359,31 @@ def test_fwd_strided_rejects_invalid_arguments(L):
     assert f(ws=P_O) == INVALID
     two = (ctypes.c_void_p * 2)(1, 2)
     assert f(ev=two, nev=2) == INVALID
+
+
+def test_workspace_may_alias_no_tensor(L):
+    """The reduction writes partials while other blocks still read k and v,
+    so every entry point with a workspace rejects one that overlaps any of
+    its tensors (inputs included) with SANA_ERR_INVALID_ARG."""
+    need = ws_size(L, 1, 64, 2)[1]
+    for ws in (P_Q, P_K + 256, P_V):
+        assert fwd(L, ws=ws, wsb=need) == INVALID, ws
+        assert L.sana_linattn_fwd_fmap(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 1e-6, BF16, 1, ws,
+                                       need, None, 0, None) == INVALID, ws
+    for ws in (P_K, P_V + 256):
+        assert L.sana_linattn_kv_state(P_K, P_V, P_O, 1, 64, 2, 32, BF16, ws, need,
+                                       None) == INVALID, ws
+    bneed = bws(L, 1, 64, 2)[1]
+    for ws in (P_Q, P_K, P_V, P_G):
+        assert bwd(L, ws=ws, wsb=bneed) == INVALID, ws
+    cneed = bcws(L, 1, 64, 2, 16)[1]
+    for ws in (P_Q, P_K, P_V):
+        assert L.sana_linattn_fwd_block_causal(P_Q, P_K, P_V, P_O, 1, 64, 2, 32, 16, 1e-6, BF16,
+                                               ws, cneed, None) == INVALID, ws
+    qneed = qkv_ws(L, 1, 64, 64, 2)[1]
+    for ws in (P_Q, P_K + 4096):   # x at P_Q (8 KB), w at P_K (24 KB)
+        assert L.sana_linattn_qkv_fwd(P_Q, P_K, P_V, P_O, 1, 64, 64, 2, 32, 1e-6, ws, qneed,
+                                      None, 0, None) == INVALID, ws
+    # strided inputs: the workspace may not fall inside the span of a strided q
+    assert L.sana_linattn_fwd_strided(P_Q, P_K, P_V, 192, P_O, 1, 64, 2, 32, 1e-6, BF16, 0,
+                                      P_Q + 8192, need, None, 0, None) == INVALID
