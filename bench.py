@@ -238,102 +238,101 @@ def copy_ceiling(device, mib: int = 1024, reps: int = 10):
     return {"gbps": best[name], "kernel": name, "mib": mib, "all_gbps": best}
 
 
-def _blas_threads() -> int:
+def host_cores() -> int:
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def _blas_info():
+    """(BLAS library NumPy calls, its thread count)."""
     try:
         from threadpoolctl import threadpool_info
 
-        return max([p.get("num_threads", 1) for p in threadpool_info()
-                    if p.get("user_api") == "blas"] or [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            return blas[0].get("internal_api", "blas"), max(p.get("num_threads", 1) for p in blas)
     except Exception:
-        return 1
+        pass
+    return "unknown", 1
+
+
+def timed_oracle(w, budget_s: float, decode, compute, what: str):
+    """The oracle on whole (b, h) heads of workload w, cycling through them
+    until `budget_s` seconds of its float64 compute are spent, with BLAS
+    limited to the host's cores. decode(b, h) turns the head's input bits
+    into float64 arrays (timed apart); compute(arrays) runs the oracle on
+    them. Returns the cpu_baseline record: compute-only tokens/s (token-heads
+    per compute second / H), the core count, BLAS threads and decode time."""
+    cores = host_cores()
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        limiter = None
+    blas, blas_threads = _blas_info()
+    done, decode_s, compute_s = 0, 0.0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    while compute_s < budget_s:
+        b, h = heads[done % len(heads)]
+        ta = time.perf_counter()
+        arrays = decode(b, h)
+        tb = time.perf_counter()
+        compute(arrays)
+        tc = time.perf_counter()
+        decode_s += tb - ta
+        compute_s += tc - tb
+        done += 1
+    if limiter is not None:
+        limiter.unregister()
+    return {
+        "value": done * w.N / compute_s / w.H,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} (b, h) heads of {w.name} ({len(heads)} per full pass) x all {w.N} "
+                  f"tokens each, {what}, float64 NumPy; tokens/s = token-heads per second of "
+                  f"oracle compute / H (bf16 decode timed apart)",
+        "compute_s": compute_s,
+        "decode_s": decode_s,
+        "blas": blas,
+        "blas_threads": blas_threads,
+    }
 
 
 def cpu_baseline(w, inputs, budget_s: float, fmap: str = "relu"):
-    """Time the CPU oracle on whole heads of the workload until the budget is
-    spent; report token-heads/s converted to tokens/s (all H heads of a
-    token)."""
-    import numpy as np
+    """The forward oracle (oracle/linattn.py, or the feature-map oracle) on
+    whole heads of the workload."""
     import oracle.linattn as L
     import oracle.linattn_feature_maps as FM
 
-    threads = _blas_threads()
-    # whole passes over the workload's (b, h) heads until the budget is spent
-    done = 0
-    passes = 0
-    t0 = time.perf_counter()
-    decode_s = 0.0
-    while True:
-        for b in range(w.B):
-            for h in range(w.H):
-                ta = time.perf_counter()
-                k = L.to_f64(inputs["k"][b, :, h, :], w.dtype)
-                v = L.to_f64(inputs["v"][b, :, h, :], w.dtype)
-                q = L.to_f64(inputs["q"][b, :, h, :], w.dtype)
-                tb = time.perf_counter()
-                if fmap == "relu":
-                    kv, ks = L.kv_state(k, v)
-                    L.apply_state(q, kv, ks, w.eps)
-                else:
-                    kv, ks = FM.state_head(k, v, fmap)
-                    FM.apply_head(q, kv, ks, w.eps, fmap)
-                decode_s += tb - ta
-                done += 1
-                if time.perf_counter() - t0 >= budget_s:
-                    break
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        passes += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    wall = time.perf_counter() - t0
-    token_heads = done * w.N
-    return {
-        "value": token_heads / wall / w.H,
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{done} (b, h) head passes ({w.B * w.H} heads per full pass, "
-                  f"{passes} pass(es)) x all {w.N} tokens of {w.name}, float64 NumPy "
-                  f"({wall:.1f} s wall incl. {decode_s:.1f} s bf16 decode); tokens/s = "
-                  f"token-heads/s / H",
-        "seconds": wall,
-    }
+    def decode(b, h):
+        return tuple(L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkv")
+
+    def compute(a):
+        q, k, v = a
+        if fmap == "relu":
+            kv, ks = L.kv_state(k, v)
+            L.apply_state(q, kv, ks, w.eps)
+        else:
+            kv, ks = FM.state_head(k, v, fmap)
+            FM.apply_head(q, kv, ks, w.eps, fmap)
+
+    return timed_oracle(w, budget_s, decode, compute, f"forward ({fmap})")
 
 
 def cpu_baseline_bwd(w, inputs, budget_s: float):
-    """The backward oracle on whole heads of the workload until the budget is
-    spent; token-heads/s converted to tokens/s (all H heads of a token)."""
+    """The backward oracle (oracle/linattn_bwd.py) on whole heads."""
     import oracle.linattn as L
     import oracle.linattn_bwd as LB
 
-    threads = _blas_threads()
-    done, passes, decode_s = 0, 0, 0.0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        for b in range(w.B):
-            for h in range(w.H):
-                ta = time.perf_counter()
-                q, k, v, g = (L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkvg")
-                decode_s += time.perf_counter() - ta
-                LB.backward_head(q, k, v, g, w.eps)
-                done += 1
-                if time.perf_counter() - t0 >= budget_s:
-                    break
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        passes += 1
-    wall = time.perf_counter() - t0
-    return {
-        "value": done * w.N / wall / w.H,
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{done} (b, h) head backward passes ({w.B * w.H} heads per full pass, "
-                  f"{passes} pass(es)) x all {w.N} tokens of {w.name}, float64 NumPy "
-                  f"({wall:.1f} s wall incl. {decode_s:.1f} s bf16 decode); tokens/s = "
-                  f"token-heads/s / H",
-        "seconds": wall,
-    }
+    def decode(b, h):
+        return tuple(L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkvg")
+
+    return timed_oracle(w, budget_s, decode, lambda a: LB.backward_head(*a, w.eps), "backward")
 
 
 def run_bwd(args, w):
@@ -423,36 +422,16 @@ def run_bwd(args, w):
 
 
 def cpu_baseline_block_causal(w, inputs, block: int, budget_s: float):
-    """The block-causal oracle on whole heads until the budget is spent."""
+    """The block-causal oracle (oracle/linattn_block_causal.py) on whole heads."""
     import oracle.linattn as L
     import oracle.linattn_block_causal as BC
 
-    threads = _blas_threads()
-    done, decode_s = 0, 0.0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        for b in range(w.B):
-            for h in range(w.H):
-                ta = time.perf_counter()
-                q, k, v = (L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkv")
-                decode_s += time.perf_counter() - ta
-                BC.block_causal_head(q, k, v, block, w.eps)
-                done += 1
-                if time.perf_counter() - t0 >= budget_s:
-                    break
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    wall = time.perf_counter() - t0
-    return {
-        "value": done * w.N / wall / w.H,
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{done} (b, h) head passes of {w.B * w.H} x all {w.N} tokens of {w.name}, "
-                  f"blocks of {block}, float64 NumPy ({wall:.1f} s wall incl. {decode_s:.1f} s "
-                  f"bf16 decode); tokens/s = token-heads/s / H",
-        "seconds": wall,
-    }
+    def decode(b, h):
+        return tuple(L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkv")
+
+    return timed_oracle(w, budget_s, decode,
+                        lambda a: BC.block_causal_head(*a, block, w.eps),
+                        f"block-causal forward, blocks of {block}")
 
 
 def run_block_causal(args, w):
@@ -668,30 +647,53 @@ def run_qkv(args, w, C: int = 2240):
 
 
 def cpu_baseline_qkv(w, inputs, C: int, budget_s: float):
-    """The oracle (float64 projection of one head's q, k, v rows, rounding,
-    attention) over whole heads until the budget is spent."""
+    """The QKV oracle (oracle/linattn_qkv.py: float64 projection of one head's
+    q, k, v rows, bf16 rounding, attention) over whole heads, all B x N tokens
+    each, until `budget_s` seconds of its compute are spent; x is decoded once
+    and every decode is timed apart."""
     import numpy as np
+    import oracle.linattn as L
     import oracle.linattn_qkv as QK
 
-    threads = _blas_threads()
-    D = w.D
-    done = 0
+    cores = host_cores()
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:
+        limiter = None
+    blas, blas_threads = _blas_info()
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+    x64 = L.bf16_bits_to_f64(inputs["x"])
+    decode_s = time.perf_counter() - t0
+    D = w.D
+    done, compute_s = 0, 0.0
+    while compute_s < budget_s:
         h = done % w.H
         rows = np.concatenate([np.arange(h * w.d, h * w.d + w.d) + i * D for i in range(3)])
-        QK.qkv_attention_from_inputs(inputs["x"], inputs["w"][rows], 1, w.eps, w.d)
+        ta = time.perf_counter()
+        w64 = L.bf16_bits_to_f64(inputs["w"][rows])
+        tb = time.perf_counter()
+        QK.qkv_attention_fp64(x64, w64, 1, w.eps, w.d)
+        tc = time.perf_counter()
+        decode_s += tb - ta
+        compute_s += tc - tb
         done += 1
-    wall = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     return {
-        "value": done * w.B * w.N / wall / w.H,
+        "value": done * w.B * w.N / compute_s / w.H,
         "unit": "tokens/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{done} heads (all {w.B} x {w.N} tokens each: float64 projection of the "
-                  f"head's q, k, v rows from C={C}, bf16 rounding, attention) of {w.name}; "
-                  f"tokens/s = token-heads/s / H",
-        "seconds": wall,
+        "sample": f"{done} heads of {w.name} (all {w.B} x {w.N} tokens each: float64 "
+                  f"projection of the head's q, k, v rows from C={C}, bf16 rounding, "
+                  f"attention); tokens/s = token-heads per second of oracle compute / H "
+                  f"(bf16 decode timed apart)",
+        "compute_s": compute_s,
+        "decode_s": decode_s,
+        "blas": blas,
+        "blas_threads": blas_threads,
     }
 
 
@@ -816,7 +818,39 @@ def main():
                   for j, n in enumerate(names)}
     alg_bytes = {"reduce": 2 * elem, "apply": 2 * elem, "fused": 4 * elem}
     dominant = max(per_kernel, key=per_kernel.get)
+
+    # The dominant kernel's average launch duration without per-launch event
+    # records (each event between kernels adds a few microseconds to the
+    # kernel it brackets): `steps` launches back to back on the launch
+    # stream, one event pair around the region, inputs cycled as above.
+    # The fused variant's step is its one kernel. The split forward's apply is
+    # launched alone from a folded state (sana_linattn_apply: the same apply
+    # kernel and grid; its prologue sums one state slot instead of the
+    # reduction's per-chunk partials).
+    duration_source = "per-kernel events in the step (include event cost)"
     dom_ms = per_kernel[dominant]
+    if nk == 1:
+        dom_ms, duration_source = ms_per_step, "the step (one kernel), back to back"
+    elif dominant == "apply" and args.fmap == "relu" and args.layout == "contiguous":
+        state = R.kv_state(sets[0]["k"], sets[0]["v"])
+
+        def apply_only(i):
+            d = sets[i % n_sets]
+            R.apply(d["q"], state, eps=w.eps, out=d["out"])
+
+        for i in range(args.warmup):
+            apply_only(i)
+        log(args, f"timing {args.steps} apply launches back to back")
+        e0, e1 = make_events(2)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            apply_only(i)
+        e1.record(stream)
+        e1.synchronize()
+        dom_ms = e0.elapsed_time(e1) / args.steps
+        duration_source = ("apply launched back to back from a folded state, one event pair "
+                           "around the region")
     achieved = alg_bytes[dominant] / (dom_ms * 1e-3) / 1e9
     traffic = (measured_traffic(dominant, wname) if args.fmap == "relu" and
                args.layout == "contiguous" and w.dtype == W.WORKLOADS[wname].dtype else None)
@@ -843,13 +877,15 @@ def main():
                    "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
-        "kernel_ms": per_kernel,
+        "kernel_ms_events_bracketed": per_kernel,
         "ms_per_step_with_kernel_events": ms_events,
         "ms_per_step_one_input_set": ms_one_set,
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic},
+                     "traffic": traffic, "kernel_ms": dom_ms,
+                     "kernel_ms_source": duration_source,
+                     "algorithmic_bytes_per_launch": alg_bytes[dominant]},
     }
     if args.copy_mib == 0:
         # achievable-bandwidth reference, outside every timed region (not in
