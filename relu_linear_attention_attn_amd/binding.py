@@ -77,6 +77,16 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with "
                 "`python relu_linear_attention_attn_amd/csrc/build.py` (hipcc, gfx950)")
+        # torch first: its HIP runtime is then already in the process when the
+        # library asks for libamdhip64.so.7 and the library binds to that one.
+        # Loaded the other way round, torch pulls in a second copy of the HIP
+        # and HSA runtimes (its libraries name the runtime differently), and the
+        # library's runtime neither sees torch's streams and memory nor can
+        # use the device reliably (hipGetDevice fails).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         L.sana_linattn_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
                                                   ctypes.POINTER(_sz)]

@@ -387,3 +387,20 @@ def test_workspace_may_alias_no_tensor(L):
     # strided inputs: the workspace may not fall inside the span of a strided q
     assert L.sana_linattn_fwd_strided(P_Q, P_K, P_V, 192, P_O, 1, 64, 2, 32, 1e-6, BF16, 0,
                                       P_Q + 8192, need, None, 0, None) == INVALID
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library through the binding leaves one HIP runtime and one
+    HSA runtime in the process (torch's), even when nothing imported torch
+    before: two copies cannot share streams or memory, and the library's copy
+    fails its first device query."""
+    pytest.importorskip("torch")
+    code = ("import relu_linear_attention_attn_amd as R; R.lib(); import torch; "
+            "m = open('/proc/self/maps').read().splitlines(); "
+            "print(sorted({l.split()[-1] for l in m if 'libamdhip64' in l or 'hsa-runtime64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert sum("libamdhip64" in p for p in libs) == 1, libs
+    assert sum("hsa-runtime64" in p for p in libs) == 1, libs
