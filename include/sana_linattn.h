@@ -129,6 +129,26 @@ sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void
                                hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * pass of sana_linattn_fwd - same arguments, checks and result bits - with
+ * its workspace in a static device array of SANA_LINATTN_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends. The call
+ * allocates nothing. A shape whose workspace (sana_linattn_workspace_size)
+ * exceeds SANA_LINATTN_SCRATCH_BYTES returns SANA_ERR_WORKSPACE before any
+ * HIP call. Every call on one GPU shares that GPU's array, and the array
+ * keeps the last call's contents (the kernels need none of it cleared):
+ * calls on one GPU that may run at the same time (different streams not
+ * ordered against each other, or different host threads) race, so the
+ * caller must order them. The first call on a device looks up the array's
+ * device address there (SANA_ERR_HIP if that fails).
+ */
+#define SANA_LINATTN_SCRATCH_BYTES ((size_t)64 << 20)
+sana_status_t sana_linattn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                       int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                       sana_dtype_t dtype, hipStream_t stream);
+
+/*
  * Same as sana_linattn_fwd with an explicit kernel variant (sana_variant_t).
  * Every variant computes the same function; results of one variant are
  * bitwise repeatable for the same inputs and shape on the same device.

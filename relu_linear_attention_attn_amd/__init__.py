@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     forward,
     forward_block_causal,
     forward_fmap,
+    forward_noalloc,
     forward_profiled,
     forward_qkv,
     forward_strided,

@@ -48,6 +48,7 @@ EXPORTS = (
     "sana_linattn_fwd_strided",
     "sana_linattn_qkv_workspace_size",
     "sana_linattn_qkv_fwd",
+    "sana_linattn_fwd_noalloc",
     "sana_linattn_strerror",
     "sana_linattn_version",
 )
@@ -93,6 +94,9 @@ def lib() -> ctypes.CDLL:
         L.sana_linattn_state_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_sz)]
         L.sana_linattn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, ctypes.c_int, _vp, _sz, _vp]
+        L.sana_linattn_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                               ctypes.c_float, ctypes.c_int, _vp]
+        L.sana_linattn_fwd_noalloc.restype = ctypes.c_int
         L.sana_linattn_fwd_variant.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                                ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
                                                _sz, _vp]
@@ -246,6 +250,25 @@ def forward(q, k, v, eps: float = 1e-6, heads: Optional[int] = None, out=None,
                                           workspace.numel() * workspace.element_size(),
                                           _stream(q)),
            "sana_linattn_fwd_variant")
+    return out
+
+
+SCRATCH_BYTES = 64 << 20   # SANA_LINATTN_SCRATCH_BYTES
+
+
+def forward_noalloc(q, k, v, out, eps: float = 1e-6, heads: Optional[int] = None):
+    """forward() through sana_linattn_fwd_noalloc: the library's static device
+    scratch serves as the workspace, so the call allocates nothing (out is the
+    caller's). Calls on one GPU share that scratch: order them on one stream."""
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q)
+    _check_tensor(v, "v", q)
+    _check_tensor(out, "out", q)
+    _check(lib().sana_linattn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), B, N, H, d, float(eps),
+                                          _dtype_code(q), _stream(q)),
+           "sana_linattn_fwd_noalloc")
     return out
 
 

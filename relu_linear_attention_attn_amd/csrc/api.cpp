@@ -343,11 +343,13 @@ size_t strided_span(int64_t B, int64_t N, int64_t H, int64_t d, int64_t ld, int6
 // recorded before the first kernel and after each kernel. Feature maps
 // other than ReLU, and q, k, v with a token stride ld other than H d, run
 // the split kernels only (ld = 0 means H d).
+// ws_source (may be NULL) supplies the workspace once every host check has
+// passed, in place of workspace / workspace_bytes.
 sana_status_t forward(const void* q, const void* k, const void* v, void* out, int64_t B,
                       int64_t N, int64_t H, int64_t d, float eps, int dtype, int variant,
                       void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
                       int* n_kernels, hipStream_t stream, int fmap = SANA_FMAP_RELU,
-                      int64_t ld = 0) {
+                      int64_t ld = 0, WorkspaceSource ws_source = nullptr) {
   size_t tb = 0;
   sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
   if (s != SANA_OK) return s;
@@ -377,6 +379,7 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   if (overlaps(out, tb, q, in_bytes) || overlaps(out, tb, k, in_bytes) ||
       overlaps(out, tb, v, in_bytes))
     return SANA_ERR_INVALID_ARG;
+  if (ws_source && ws_source(&workspace, &workspace_bytes) != hipSuccess) return SANA_ERR_HIP;
   if ((s = check_workspace(p, workspace, workspace_bytes)) != SANA_OK) return s;
   // the reduction writes partials while other blocks still read k and v, and
   // the apply writes out: the workspace may alias no tensor
@@ -623,6 +626,14 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
 }
 
 }  // namespace
+
+sana_status_t forward_from_source(const void* q, const void* k, const void* v, void* out,
+                                  int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                  int dtype, WorkspaceSource ws_source, hipStream_t stream) {
+  return forward(q, k, v, out, B, N, H, d, eps, dtype, SANA_VARIANT_AUTO, nullptr, 0, nullptr, 0,
+                 nullptr, stream, SANA_FMAP_RELU, 0, ws_source);
+}
+
 }  // namespace sana
 
 extern "C" {

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libsana_linattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "linattn_kernels.hip", "qkv_kernels.hip"]
+SOURCES = ["api.cpp", "linattn_kernels.hip", "qkv_kernels.hip", "noalloc.hip"]
 
 # Packed fp32 VALU ops are disabled for every device pass.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "sana_linattn.h"
+
 namespace sana {
 
 constexpr int kHeadDim = 32;                          // d
@@ -54,6 +56,15 @@ struct Plan {
 // (unit, chunk) grid, else the tiles per balanced range (each unit's slot
 // count follows from it, see the kernels' slot_count).
 inline int64_t red_rule(const Plan& p) { return p.red_cb > 0 ? -p.red_cb : p.red_q; }
+
+// Supplies a workspace (device pointer and bytes) to the forward pass; asked
+// only after every host check of the call has passed.
+typedef hipError_t (*WorkspaceSource)(void** workspace, size_t* bytes);
+
+// sana_linattn_fwd with its workspace taken from `ws_source` (api.cpp).
+sana_status_t forward_from_source(const void* q, const void* k, const void* v, void* out,
+                                  int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                  int dtype, WorkspaceSource ws_source, hipStream_t stream);
 
 // Device-independent part of the plan: sizes and the workspace layout.
 Plan make_plan(int64_t B, int64_t N, int64_t H);
