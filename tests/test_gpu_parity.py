@@ -188,18 +188,27 @@ def test_repeat_calls_are_bitwise_identical(name):
             assert np.array_equal(a, b), vname
 
 
-def test_scaling_k_by_two_changes_at_most_one_ulp():
-    """phi(2k) = 2 phi(k) and doubling is exact in bf16 and fp32, so the state
-    doubles exactly; the output moves only through eps, i.e. by at most one
-    bf16 rounding step."""
-    w = W.WORKLOADS["sana06_1024px"]
+def _ordered(u):
+    """bf16 bits as sign-magnitude integers: adjacent bf16 values differ by 1."""
+    u = u.astype(np.int32)
+    return np.where(u & 0x8000, -(u & 0x7FFF), u)
+
+
+@pytest.mark.parametrize("name", ["sana06_1024px", "latent_4096px"])
+@pytest.mark.parametrize("scaled", ["k", "q"])
+def test_scaling_by_two_changes_at_most_one_ulp(name, scaled):
+    """phi(2x) = 2 phi(x) and doubling is exact in bf16 and fp32. Doubling K
+    doubles the state exactly; doubling Q doubles both the numerator and the
+    denominator's dot product exactly. Either way the output moves only
+    through eps, i.e. by at most one bf16 rounding step, in every variant."""
+    w = W.WORKLOADS[name]
     x, dev = _inputs(w)
-    a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps), "bf16").astype(np.int32)
-    b = to_host(R.forward(dev["q"], dev["k"] * 2, dev["v"], eps=w.eps), "bf16").astype(np.int32)
-    # compare as sign-magnitude integers: adjacent bf16 values differ by 1
-    def ordered(u):
-        return np.where(u & 0x8000, -(u & 0x7FFF), u)
-    assert np.max(np.abs(ordered(a) - ordered(b))) <= 1
+    two = dict(dev)
+    two[scaled] = dev[scaled] * 2
+    for vname, var in VARIANTS.items():
+        a = to_host(R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var), "bf16")
+        b = to_host(R.forward(two["q"], two["k"], two["v"], eps=w.eps, variant=var), "bf16")
+        assert np.max(np.abs(_ordered(a) - _ordered(b))) <= 1, vname
 
 
 def test_convex_combination_bound():
@@ -227,6 +236,27 @@ def test_output_canaries_untouched():
         t.cuda.synchronize()
         host = buf.cpu().numpy()
         assert np.all(host[:pad] == 12345) and np.all(host[pad + n:] == 12345), vname
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_workspace_canaries_untouched(dtype):
+    """The forward pass and the state reduction write only inside the
+    workspace they are given: the bytes just before and after it keep their
+    values (the workspace is the exact queried size)."""
+    t = torch()
+    w = W.custom("ws_canary", 2, 3000, 5, dtype=dtype, seed=6)
+    x, dev = _inputs(w)
+    dt = R.DTYPE_BF16 if dtype == "bf16" else R.DTYPE_F32
+    size = R.workspace_size(w.B, w.N, w.H, dtype=dt)
+    pad = 4096
+    buf = t.full((size + 2 * pad,), 0xA5, dtype=t.uint8, device="cuda")
+    ws = buf[pad:pad + size]
+    for vname, var in VARIANTS.items():
+        R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps, variant=var, workspace=ws)
+    R.kv_state(dev["k"], dev["v"], workspace=ws)
+    t.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:pad] == 0xA5) and np.all(host[pad + size:] == 0xA5)
 
 
 def test_heads_given_as_flat_width():
@@ -294,14 +324,29 @@ def test_errors_enqueue_nothing():
     assert bool((out == 3.0).all())
 
 
-# --------------------------------------------- 1M tokens, sampled outputs
+# ------------------------------------------------------------ 1M tokens
+
+def _chunk_edges(N: int, units: int, cus: int = 256):
+    """Token offsets where the split kernels' chunks start on this shape, by
+    the library's rule for a (head pair, chunk) grid on `cus` one-block-per-CU
+    slots: c = slots // units chunks (one round that fills at least 3/4 of the
+    slots), each a whole number of 16-token tiles, an even count made odd."""
+    c = max(1, cus // units)
+    assert 4 * units * c >= 3 * cus, "shape outside the one-round rule"
+    tiles = -(-(-(-N // c)) // 16)
+    if tiles > 1 and tiles % 2 == 0:
+        tiles += 1
+    chunk = 16 * tiles
+    return list(range(chunk, N, chunk)), chunk
 
 
 @pytest.mark.timeout(900)
-def test_video_1m_tokens_sampled():
-    """B=1, N=1,048,576, H=36, t(4) heavy-tailed Q and K: the full state is
-    checked against the oracle's, and outputs on sampled token rows (plus the
-    first and last rows and chunk edges) element by element."""
+def test_video_1m_tokens():
+    """B=1, N=1,048,576, H=36, t(4) heavy-tailed Q and K: heads 0 and 35 (the
+    first and last) compared with the oracle on all 1,048,576 rows, element
+    by element; every head on sampled rows that include the first and last
+    rows and both sides of every chunk boundary of the reduction and the
+    apply; and the whole state against the oracle's."""
     w = W.WORKLOADS["video_1m_tokens"]
     x, dev = {}, {}
     for t in "qkv":
@@ -312,15 +357,23 @@ def test_video_1m_tokens_sampled():
     out = R.forward(dev["q"], dev["k"], dev["v"], eps=w.eps)
     st = R.kv_state(dev["k"], dev["v"])
     torch().cuda.synchronize()
-    rng = np.random.default_rng(2024)
-    rows = np.unique(np.concatenate([rng.choice(w.N, 4096, replace=False),
-                                     [0, 1, 15, 16, 17, w.N - 17, w.N - 1],
-                                     np.arange(0, w.N, 18432)[:64]]))
-    got = decode(to_host(out[0, rows], "bf16"), "bf16")
-    print("[case] oracle state over 1M tokens", flush=True)
+    edges, chunk = _chunk_edges(w.N, w.B * ((w.H + 1) // 2))
+    assert chunk == 74928 and len(edges) == 13   # 14 chunks on 256 CUs
+    print(f"[case] chunk {chunk} tokens, {len(edges) + 1} chunks", flush=True)
     ref_state = L.state_from_inputs(x["k"], x["v"], "bf16")
     _, srel, _ = metrics(st.cpu().numpy().astype(np.float64), ref_state)
     print(f"state rel-L2 {srel:.3e}", flush=True)
     assert srel < 1e-4
+    for h in (0, w.H - 1):
+        print(f"[case] head {h}: all {w.N} rows", flush=True)
+        got = decode(to_host(out[0, :, h], "bf16"), "bf16")
+        ref = L.apply_state(decode(x["q"][0, :, h], "bf16"), ref_state[0, h, :, :w.d],
+                            ref_state[0, h, :, w.d], w.eps)
+        assert_close(got, ref, "bf16", f"video_1m_tokens head {h}, all rows")
+    rng = np.random.default_rng(2024)
+    rows = np.unique(np.concatenate([rng.choice(w.N, 4096, replace=False),
+                                     [0, 1, 15, 16, 17, w.N - 17, w.N - 1],
+                                     *[[e - 1, e, e + 1] for e in edges]]))
+    got = decode(to_host(out[0, rows], "bf16"), "bf16")
     ref = L.apply_rows(decode(x["q"][0, rows], "bf16"), ref_state[0], w.eps)
-    assert_close(got, ref, "bf16", "video_1m_tokens sampled rows")
+    assert_close(got, ref, "bf16", "video_1m_tokens sampled rows, every head")
