@@ -324,15 +324,19 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
 // Where a launch must leave one folded state (the fp32 reduction, and the
 // bf16 one behind sana_linattn_kv_state), the partials of a head pair are
 // folded into it by the last block to finish that pair, in ascending chunk
-// order, so the result does not depend on which block finishes last. The hand-off between blocks (which may
-// sit on different XCDs, each with its own L2) avoids device-wide fences,
-// whose L2 write-back per block would cost more than the whole reduction:
-//   * partials are written with device-coherent stores (relaxed atomic
-//     stores at agent scope, which write through the L2),
-//   * each wave waits until its stores have completed, then the block bumps
-//     the pair's control word with a device-scope atomic,
-//   * the block that brings the count to the number of chunks reads the
-//     partials back with device-coherent loads.
+// order, so the result does not depend on which block finishes last. The
+// hand-off between blocks (which may sit on different XCDs, each with its
+// own L2) is a release/acquire pair at agent scope on the pair's control
+// word:
+//   * partials are written with agent-scope (device-coherent) stores, and
+//     each wave waits until its stores have completed before the block
+//     barrier, so every store of the block precedes thread 0's update;
+//   * thread 0 counts the block in with a compare-and-swap that is a release
+//     (the block's partials become visible device-wide before the new count
+//     can be seen) and an acquire (if it is the last block, the other
+//     blocks' partials, released before their counts, are visible to it);
+//   * the last block reads the partials back with agent-scope loads after
+//     the block barrier that follows thread 0's acquire.
 // The control word holds (call epoch << 16 | finished blocks). A word left by
 // an earlier call, or garbage, carries another epoch and restarts the count,
 // so the workspace needs no clearing between calls.
@@ -343,7 +347,7 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 __device__ __forceinline__ bool arrive_last(unsigned long long* ctl, unsigned long long epoch,
                                             int64_t nchunks) {
   __shared__ int last;
-  // wait until this wave's coherent partial stores have completed
+  // wait until this wave's partial stores have completed
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -351,7 +355,7 @@ __device__ __forceinline__ bool arrive_last(unsigned long long* ctl, unsigned lo
     unsigned long long nxt;
     while (true) {
       nxt = (cur >> 16) == epoch ? cur + 1 : ((epoch << 16) | 1ull);
-      if (__hip_atomic_compare_exchange_strong(ctl, &cur, nxt, __ATOMIC_RELAXED,
+      if (__hip_atomic_compare_exchange_strong(ctl, &cur, nxt, __ATOMIC_ACQ_REL,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
         break;
     }
