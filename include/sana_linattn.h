@@ -84,7 +84,10 @@ typedef enum {
 } sana_status_t;
 
 typedef enum {
-  SANA_VARIANT_AUTO = 0,   /* FUSED up to N = 1024, SPLIT beyond */
+  SANA_VARIANT_AUTO = 0,   /* by shape and device: SPLIT for N > 1024; for N <= 1024,
+                              FUSED when the call is tiny (B * ceil(H/2) * N <= 4096) or
+                              has at least as many head pairs as co-resident fused blocks
+                              (one per CU on MI355X), SPLIT otherwise */
   SANA_VARIANT_SPLIT = 1,  /* two launches: split-N state reduction into per-block partials,
                               then the apply, which sums a head pair's partials in fixed
                               order (bf16); fp32 folds them at the end of the reduction */
@@ -164,9 +167,9 @@ sana_status_t sana_linattn_fwd_variant(const void* q, const void* k, const void*
  * hipEventElapsedTime(events[i-1], events[i]) is the duration of kernel i.
  * The kernels, in order: SPLIT - the state reduction over token ranges,
  * then the apply (which, in bf16, also sums the reduction's partials); FUSED -
- * its single kernel. *n_kernels (if not NULL) receives that count (2 or 1)
- * whenever the shape, dtype and variant are valid, even when the call fails
- * otherwise. The events are created by the caller (hipEventCreate);
+ * its single kernel; AUTO - those of the variant it picks. *n_kernels (if not
+ * NULL) receives that count (2 or 1) whenever the shape, dtype and variant
+ * are valid, even when the call fails otherwise. The events are created by the caller (hipEventCreate);
  * n_events must be at least *n_kernels + 1, else SANA_ERR_INVALID_ARG.
  * Computes exactly what sana_linattn_fwd_variant computes.
  */

@@ -116,6 +116,8 @@ Plan make_plan(int64_t B, int64_t N, int64_t H) {
   p.red_chunks = cdiv(N, p.red_chunk);
   p.app_chunk = cdiv(N, kTile) * kTile;
   p.app_chunks = 1;
+  p.app_q = 0;
+  p.app_blocks = 0;
   const size_t bh = static_cast<size_t>(B * H);
   const size_t f32_partials = static_cast<size_t>(p.red_chunks_max) * bh * kStateFloats * 4;
   const size_t bf16_partials =
@@ -134,6 +136,7 @@ struct DeviceCaps {
   int cus = 0;
   int occ[2][2] = {{1, 1}, {1, 1}};  // [kernel: reduce, apply][dtype]
   int occ_bwd_kv = 1;                // backward k/v pass (bf16)
+  int occ_fused[2] = {1, 1};         // fused kernel [dtype]
 };
 
 const DeviceCaps& device_caps() {
@@ -152,6 +155,7 @@ const DeviceCaps& device_caps() {
       c.occ[1][dt] = occupancy_blocks_per_cu(KernelKind::kApply, dt);
     }
     c.occ_bwd_kv = occupancy_blocks_per_cu(KernelKind::kBwdKV, 1);
+    for (int dt = 0; dt < 2; ++dt) c.occ_fused[dt] = occupancy_blocks_per_cu(KernelKind::kFused, dt);
     caps[dev] = c;
   });
   return caps[dev];
@@ -225,6 +229,17 @@ void fit_plan_to_device(Plan& p, int dtype) {
   int64_t ac = grid_chunks(p.units, p.N, acap);
   p.app_chunk = chunk_tokens(p.N, ac);
   p.app_chunks = cdiv(p.N, p.app_chunk);
+  // more head pairs than co-resident apply blocks: the (unit, chunk) grid
+  // would need several rounds, the last one part empty; balanced ranges over
+  // one round keep every CU streaming to the end (bf16)
+  if (dt == 1 && p.units > acap) {
+    const int64_t F = p.units * p.tiles;
+    const int64_t g = std::max<int64_t>(
+        1, std::min(std::min<int64_t>(acap, kMaxRangeBlocks),
+                    F / (block_waves(KernelKind::kApply, dt) * kMinTilesPerWave)));
+    p.app_q = cdiv(F, g);
+    p.app_blocks = cdiv(F, p.app_q);
+  }
   int64_t bc = grid_chunks(p.units, p.N, static_cast<int64_t>(c.cus) * c.occ_bwd_kv);
   p.bkv_chunk = chunk_tokens(p.N, bc);
   p.bkv_chunks = cdiv(p.N, p.bkv_chunk);
@@ -251,12 +266,28 @@ bool valid_variant(int variant) {
          variant == SANA_VARIANT_FUSED;
 }
 
-// The kernel arrangement a call runs: AUTO takes the fused kernel for short
-// sequences (one block per head pair fills the device poorly once N grows,
-// but saves the second launch while N is small) and the split pair beyond.
-int resolve_variant(const Plan& p, int variant) {
+// The kernel arrangement a call runs. AUTO, for sequences up to kFusedMaxN
+// tokens (beyond, the split pair):
+//  * the fused kernel when the whole call is tiny (launch-bound: one launch
+//    beats two), or when there are at least as many head-pair units as
+//    co-resident fused blocks;
+//  * the split pair when there are fewer (most CUs would idle under the
+//    one-block-per-unit fused grid; measured on 2 x 1024 x 36: 14.7 against
+//    15.7 us). Running the fused kernel over whole rounds of units and the
+//    split pair over the rest measured slower on 16 x 1024 x 70 (63.9
+//    against 61.1 us): the short last fused round costs less than two more
+//    launches over its units.
+// Queries the device (CU count, occupancy) once per device.
+constexpr int64_t kTinyUnitTokens = 4096;  // units x N at or below which one launch wins
+
+int resolve_variant(const Plan& p, int dtype, int variant) {
   if (variant != SANA_VARIANT_AUTO) return variant;
-  return p.N <= kFusedMaxN ? SANA_VARIANT_FUSED : SANA_VARIANT_SPLIT;
+  if (p.N > kFusedMaxN) return SANA_VARIANT_SPLIT;
+  if (p.units * p.N <= kTinyUnitTokens) return SANA_VARIANT_FUSED;
+  const DeviceCaps& c = device_caps();
+  const int64_t slots =
+      static_cast<int64_t>(c.cus) * c.occ_fused[dtype == SANA_DTYPE_BF16 ? 1 : 0];
+  return p.units < slots ? SANA_VARIANT_SPLIT : SANA_VARIANT_FUSED;
 }
 
 int kernels_of(int variant) { return variant == SANA_VARIANT_SPLIT ? 2 : 1; }
@@ -365,7 +396,7 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   if (split_only) variant = SANA_VARIANT_SPLIT;
   Plan p = make_plan(B, N, H);
   p.ld = ld;
-  const int run = resolve_variant(p, variant);
+  const int run = resolve_variant(p, dtype, variant);
   const int nk = kernels_of(run);
   if (n_kernels) *n_kernels = nk;
   if (events) {
@@ -656,7 +687,8 @@ sana_status_t sana_linattn_fwd_profiled(const void* q, const void* k, const void
       // still report the kernel count when the arguments allow it
       size_t tb = 0;
       if (sana::check_shape(B, N, H, d, dtype, &tb) == SANA_OK && sana::valid_variant(variant))
-        *n_kernels = sana::kernels_of(sana::resolve_variant(sana::make_plan(B, N, H), variant));
+        *n_kernels =
+            sana::kernels_of(sana::resolve_variant(sana::make_plan(B, N, H), dtype, variant));
     }
     return SANA_ERR_INVALID_ARG;
   }

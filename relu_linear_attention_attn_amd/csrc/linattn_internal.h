@@ -43,6 +43,9 @@ struct Plan {
   int64_t red_chunks_max; // chunks the workspace is sized for
   int64_t app_chunk;      // tokens per apply chunk (multiple of kTile)
   int64_t app_chunks;
+  // bf16 apply on balanced ranges instead: app_blocks blocks of app_q tiles
+  // of the flattened (unit, tile) index (app_q = 0: the (unit, chunk) grid)
+  int64_t app_q, app_blocks;
   int64_t bkv_chunk;      // backward k/v pass (bf16): tokens per chunk, chunks per unit
   int64_t bkv_chunks;
   size_t partial_bytes;   // workspace bytes for partials (either dtype)
@@ -71,7 +74,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H);
 // Fills the chunk counts for the current device (makes HIP queries once per device).
 void fit_plan_to_device(Plan& p, int dtype);
 
-enum class KernelKind { kReduce, kApply, kBwdQ, kBwdKV };
+enum class KernelKind { kReduce, kApply, kBwdQ, kBwdKV, kFused };
 int occupancy_blocks_per_cu(KernelKind kind, int dtype);
 int block_waves(KernelKind kind, int dtype);  // waves per block
 

@@ -836,11 +836,11 @@ struct PairCoords {
   bool two;  // the pair's second head exists
 };
 
-__device__ __forceinline__ PairCoords pair_coords(int64_t pairs, int64_t units, int64_t H) {
+// Block g of a one-block-per-unit grid.
+__device__ __forceinline__ PairCoords pair_coords(int64_t pairs, int64_t H) {
   PairCoords c;
-  const int64_t bid = blockIdx.x;
-  const int64_t unit = bid % units;
-  c.p = bid / units;
+  const int64_t unit = blockIdx.x;
+  c.p = 0;
   c.b = unit / pairs;
   c.h = 2 * (unit % pairs);
   c.sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1101,7 +1101,7 @@ __device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, i
 
 
 // Apply, one block per (unit, token chunk of Qa tiles), C chunks per unit,
-// grouped by XCD (xcd_item).
+// grouped by XCD (xcd_item), or balanced ranges (C = 0).
 // The state of a unit is the sum of `count`
 // consecutive [2][d][d+1] slots at src + b * sb + p * sp (+ j * 2 * kSF),
 // count = slot_count(unit, T, Qr): the partials of the reduction (balanced
@@ -1119,12 +1119,20 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
   __shared__ alignas(16) unsigned char slots[S][kTileBytes];
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Item it = xcd_item(units, C, X);
-  if (!it.valid) return;  // the whole block
-  const int64_t unit = it.unit;
-  const int64_t f_lo = unit * T + it.chunk * Qa;
-  const int64_t f_hi = f_lo + Qa < (unit + 1) * T ? f_lo + Qa : (unit + 1) * T;
-  {
+  // C > 0: one (unit, chunk) item of Qa tiles per block, in XCD runs.
+  // C = 0: balanced ranges of Qa tiles of the flattened (unit, tile) index;
+  // a block that straddles units applies each in turn.
+  int64_t f_lo, f_hi;
+  if (C > 0) {
+    const Item it = xcd_item(units, C, X);
+    if (!it.valid) return;  // the whole block
+    f_lo = it.unit * T + it.chunk * Qa;
+    f_hi = f_lo + Qa < (it.unit + 1) * T ? f_lo + Qa : (it.unit + 1) * T;
+  } else {
+    f_lo = static_cast<int64_t>(blockIdx.x) * Qa;
+    f_hi = f_lo + Qa < units * T ? f_lo + Qa : units * T;
+  }
+  for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
     const int64_t count = slot_count(unit, T, Qr);
     const f32x4* st = reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp);
@@ -1139,6 +1147,7 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     apply_pair_wave<U, Fm>(Q, Out, make_ops, eps, ld, sg.b * N * ld + sg.h * kD, H * kD,
                            (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi, sub, S, sg.two,
                            slots[sub]);
+    __syncthreads();  // every wave has its operands before `stage` is refilled
   }
 }
 
@@ -1167,7 +1176,7 @@ __global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
     int64_t N, int64_t H, int64_t pairs) {
   __shared__ RedLds<S> lds;
   __shared__ float st[2][kSF];
-  const PairCoords pc = pair_coords(pairs, (int64_t)gridDim.x, H);
+  const PairCoords pc = pair_coords(pairs, H);
   const int64_t base = (pc.b * N * H + pc.h) * kD;
   f32x16 acc[2] = {(f32x16)0, (f32x16)0};
   float ks[2] = {0.0f, 0.0f};
@@ -1782,6 +1791,7 @@ int block_waves(KernelKind kind, int dtype) {
   switch (kind) {
     case KernelKind::kBwdQ: return kBwqS;
     case KernelKind::kBwdKV: return kBwkvS;
+    case KernelKind::kFused: return dtype == 1 ? kFusS : 2 * kF32S;
     default: break;
   }
   if (dtype != 1) return 2 * kF32S;
@@ -1812,8 +1822,25 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_kv_bf16_kernel<kBwkvS, kBwkvU>,
                                                        64 * kBwkvS, 0);
       break;
+    case KernelKind::kFused:
+      e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &n, fused_bf16_kernel<kFusS, kFusU>, 64 * kFusS, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                           &n, fused_f32_kernel<kF32S, kF32U>, 128 * kF32S, 0);
+      break;
   }
   return e == hipSuccess && n > 0 ? n : 1;
+}
+
+// The bf16 apply's grid: (unit, chunk) items in XCD runs, or balanced ranges
+// of app_q tiles when the plan says so (app_q > 0).
+struct ApplyGrid {
+  int64_t blocks, C, Qa, X;
+};
+ApplyGrid apply_grid(const Plan& p) {
+  if (p.app_q > 0) return {p.app_blocks, 0, p.app_q, 1};
+  const int64_t X = apply_xcds(p);
+  return {xcd_grid(p.units * p.app_chunks, X), p.app_chunks, p.app_chunk / kTile, X};
 }
 
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state, void* out,
@@ -1821,13 +1848,12 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
   return with_fmap(fmap, [&](auto fm) {
     constexpr int Fm = decltype(fm)::value;
     if (dtype == 1) {
-      const int64_t X = apply_xcds(p);
-      hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>),
-                         dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
-                         kApplyLdsPad, stream, static_cast<const unsigned short*>(q), state,
-                         p.H * kSF, int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out),
-                         eps, p.N, p.H, p.ld, p.pairs, p.units, p.tiles, p.app_chunks,
-                         p.app_chunk / kTile, X);
+      const ApplyGrid ag = apply_grid(p);
+      hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>), dim3((unsigned)ag.blocks),
+                         dim3(64 * kAppS), kApplyLdsPad, stream,
+                         static_cast<const unsigned short*>(q), state, p.H * kSF,
+                         int64_t(2 * kSF), int64_t(0), static_cast<unsigned short*>(out), eps, p.N,
+                         p.H, p.ld, p.pairs, p.units, p.tiles, ag.C, ag.Qa, ag.X);
     } else {
       hipLaunchKernelGGL((apply_f32_kernel<kF32S, Fm>), dim3((unsigned)(p.units * p.app_chunks)),
                          dim3(128 * kF32S), 0, stream, static_cast<const float*>(q), state,
@@ -1841,14 +1867,14 @@ hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* st
 hipError_t launch_apply_partials(const Plan& p, const void* q, const float* partials, void* out,
                                  float eps, hipStream_t stream, int fmap) {
   const int64_t sp = p.slots * 2 * kSF;
-  const int64_t X = apply_xcds(p);
+  const ApplyGrid ag = apply_grid(p);
   return with_fmap(fmap, [&](auto fm) {
     constexpr int Fm = decltype(fm)::value;
-    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>),
-                       dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
-                       kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
-                       p.pairs * sp, sp, red_rule(p), static_cast<unsigned short*>(out), eps, p.N, p.H,
-                       p.ld, p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+    hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, Fm>), dim3((unsigned)ag.blocks),
+                       dim3(64 * kAppS), kApplyLdsPad, stream,
+                       static_cast<const unsigned short*>(q), partials, p.pairs * sp, sp,
+                       red_rule(p), static_cast<unsigned short*>(out), eps, p.N, p.H, p.ld,
+                       p.pairs, p.units, p.tiles, ag.C, ag.Qa, ag.X);
     return hipGetLastError();
   });
 }
@@ -1856,12 +1882,11 @@ hipError_t launch_apply_partials(const Plan& p, const void* q, const float* part
 hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partials, int64_t count,
                               void* out, float eps, hipStream_t stream) {
   const int64_t sp = count * 2 * kSF;
-  const int64_t X = apply_xcds(p);
-  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, kFmapRelu>),
-                     dim3((unsigned)xcd_grid(p.units * p.app_chunks, X)), dim3(64 * kAppS),
-                     kApplyLdsPad, stream, static_cast<const unsigned short*>(q), partials,
-                     p.pairs * sp, sp, -count, static_cast<unsigned short*>(out), eps, p.N, p.H,
-                     p.ld, p.pairs, p.units, p.tiles, p.app_chunks, p.app_chunk / kTile, X);
+  const ApplyGrid ag = apply_grid(p);
+  hipLaunchKernelGGL((apply_bf16_kernel<kAppS, kAppU, kFmapRelu>), dim3((unsigned)ag.blocks),
+                     dim3(64 * kAppS), kApplyLdsPad, stream, static_cast<const unsigned short*>(q),
+                     partials, p.pairs * sp, sp, -count, static_cast<unsigned short*>(out), eps,
+                     p.N, p.H, p.ld, p.pairs, p.units, p.tiles, ag.C, ag.Qa, ag.X);
   return hipGetLastError();
 }
 

@@ -96,6 +96,27 @@ def test_ragged_shapes(B, N, H, dtype):
         assert_close(_run(w, dev, var), ref, dtype, f"B={B} N={N} H={H} {dtype} {vname}")
 
 
+# --------------------------------------------- AUTO's choice by shape
+
+
+def test_auto_variant_by_shape():
+    """AUTO runs the split pair for N > 1024 and for few head pairs at
+    N <= 1024, the fused kernel for a tiny call and for at least one head pair
+    per CU (256 on MI355X); each result matches the oracle."""
+    t = torch()
+    for (B, N, H, want) in ((2, 1024, 36, 2), (1, 64, 2, 1), (1, 2048, 4, 2),
+                            (16, 1024, 70, 1), (9, 1000, 57, 1), (2, 700, 251, 2)):
+        w = W.custom(f"arr_{B}_{N}_{H}", B, N, H, seed=7 + H)
+        print(f"\n[case] AUTO B={B} N={N} H={H}", flush=True)
+        x, dev = _inputs(w)
+        events = [t.cuda.Event(enable_timing=True) for _ in range(3)]
+        out, nk = R.forward_profiled(dev["q"], dev["k"], dev["v"], events, eps=w.eps)
+        t.cuda.synchronize()
+        assert nk == want, (B, N, H, nk)
+        assert_close(decode(to_host(out, "bf16"), "bf16"), _oracle(w, x), "bf16",
+                     f"AUTO B={B} N={N} H={H}")
+
+
 # ------------------------------------------------------ state and apply halves
 
 
