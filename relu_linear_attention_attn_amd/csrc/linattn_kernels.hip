@@ -484,14 +484,17 @@ __device__ __forceinline__ u32x4 apply_head(const ApplyOperands& op, u32x4 qpiec
 // Applies the pair's two heads to the tiles sub, sub + S, ... of [n_lo, n_hi).
 // `two` as for reduce_pair_wave: with one head, the second half-line is read
 // from the first head (inside the tensor), computed and never stored.
-// make_ops(op) fills the two heads' operands; it runs after the first U tiles'
-// loads are issued, so whatever it waits for (the state's loads, a block
-// barrier: every wave of the block calls it) overlaps those loads.
+// pre_ops() runs first and returns what make_ops(op, pre) needs loaded
+// ahead (the first state slots); make_ops fills the two heads' operands
+// after the first U tiles' loads are issued, so whatever it waits for (the
+// state's loads, a block barrier: every wave of the block calls it) overlaps
+// those loads, and the state's loads, issued before them, do not wait
+// behind them.
 // row / base locate q as in reduce_pair_wave; orow / obase locate the output.
-template <int U, int Fm = kFmapRelu, class MakeOps>
+template <int U, int Fm = kFmapRelu, class PreOps, class MakeOps>
 __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict__ Q,
                                                 unsigned short* __restrict__ Out,
-                                                MakeOps&& make_ops, float eps,
+                                                PreOps&& pre_ops, MakeOps&& make_ops, float eps,
                                                 int64_t row, int64_t base, int64_t orow,
                                                 int64_t obase, int64_t n_lo, int64_t n_hi,
                                                 int sub, int S, bool two,
@@ -516,10 +519,11 @@ __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict
       qd[h2] = ld16_stream(Q + base + (n < n_hi ? n : n_lo) * row + 8 * jl);
     }
   };
+  const auto pre = pre_ops();
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u, qb[u]);
   ApplyOperands op[2];
-  make_ops(op);
+  make_ops(op, pre);
 
   // stage the tile's lines, compute both heads in place in the tile, and read
   // the output lines back; `full` says the whole tile is inside the range
@@ -1093,13 +1097,40 @@ __global__ __launch_bounds__(128 * S) void reduce_f32_kernel(
 // unconditional (indices clamped to valid slots and elements) and a batch's
 // loads are all issued before any is added. The caller synchronises before
 // reading stage.
+// The first kFirstSlots slots of such a sum, loaded ahead (indices clamped
+// to valid slots and elements), so a caller can issue them before its other
+// loads: a wave's loads complete in issue order, so the sum then waits for
+// these alone.
+constexpr int kFirstSlots = 4;
+struct SlotPrefetch {
+  f32x4 x0[kFirstSlots], x1[kFirstSlots];
+};
+__device__ __forceinline__ SlotPrefetch prefetch_slots(const f32x4* __restrict__ st,
+                                                       int64_t count, int n4) {
+  const int e0 = threadIdx.x < n4 ? threadIdx.x : n4 - 1;
+  const int e1 = threadIdx.x + blockDim.x < n4 ? threadIdx.x + blockDim.x : n4 - 1;
+  SlotPrefetch pf;
+#pragma unroll
+  for (int u = 0; u < kFirstSlots; ++u) {
+    const int64_t j = u < count ? u : count - 1;
+    pf.x0[u] = st[j * (2 * kSF / 4) + e0];
+    pf.x1[u] = st[j * (2 * kSF / 4) + e1];
+  }
+  return pf;
+}
+
 __device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, int64_t count,
-                                                 int n4, f32x4* stage) {
+                                                 int n4, f32x4* stage, const SlotPrefetch& pf) {
   constexpr int kBatch = 8;
   const int e0 = threadIdx.x < n4 ? threadIdx.x : n4 - 1;
   const int e1 = threadIdx.x + blockDim.x < n4 ? threadIdx.x + blockDim.x : n4 - 1;
-  f32x4 a0 = (f32x4)0, a1 = (f32x4)0;
-  for (int64_t j0 = 0; j0 < count; j0 += kBatch) {
+  f32x4 a0 = pf.x0[0], a1 = pf.x1[0];
+#pragma unroll
+  for (int u = 1; u < kFirstSlots; ++u) {
+    a0 = u < count ? a0 + pf.x0[u] : a0;
+    a1 = u < count ? a1 + pf.x1[u] : a1;
+  }
+  for (int64_t j0 = kFirstSlots; j0 < count; j0 += kBatch) {
     f32x4 x0[kBatch], x1[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -1109,13 +1140,17 @@ __device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, i
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const bool first = j0 + u == 0, take = j0 + u < count;
-      a0 = first ? x0[u] : (take ? a0 + x0[u] : a0);
-      a1 = first ? x1[u] : (take ? a1 + x1[u] : a1);
+      const bool take = j0 + u < count;
+      a0 = take ? a0 + x0[u] : a0;
+      a1 = take ? a1 + x1[u] : a1;
     }
   }
   if (threadIdx.x < n4) stage[threadIdx.x] = a0;
   if (threadIdx.x + blockDim.x < n4) stage[threadIdx.x + blockDim.x] = a1;
+}
+__device__ __forceinline__ void sum_slots_to_lds(const f32x4* __restrict__ st, int64_t count,
+                                                 int n4, f32x4* stage) {
+  sum_slots_to_lds(st, count, n4, stage, prefetch_slots(st, count, n4));
 }
 
 
@@ -1156,14 +1191,15 @@ __global__ __launch_bounds__(64 * S) void apply_bf16_kernel(
     const int64_t count = slot_count(unit, T, Qr);
     const f32x4* st = reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp);
     const int n4 = (sg.two ? 2 : 1) * kSF / 4;
-    auto make_ops = [&](ApplyOperands (&op)[2]) {
-      sum_slots_to_lds(st, count, n4, stage);
+    auto pre_ops = [&] { return prefetch_slots(st, count, n4); };
+    auto make_ops = [&](ApplyOperands (&op)[2], const SlotPrefetch& pf) {
+      sum_slots_to_lds(st, count, n4, stage, pf);
       __syncthreads();
       const float* stf = reinterpret_cast<const float*>(stage);
       op[0] = make_apply_operands(stf);
       op[1] = sg.two ? make_apply_operands(stf + kSF) : op[0];
     };
-    apply_pair_wave<U, Fm>(Q, Out, make_ops, eps, ld, sg.b * N * ld + sg.h * kD, H * kD,
+    apply_pair_wave<U, Fm>(Q, Out, pre_ops, make_ops, eps, ld, sg.b * N * ld + sg.h * kD, H * kD,
                            (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi, sub, S, sg.two,
                            slots[sub]);
     __syncthreads();  // every wave has its operands before `stage` is refilled
@@ -1200,15 +1236,16 @@ __global__ __launch_bounds__(64 * S) void fused_bf16_kernel(
   f32x16 acc[2] = {(f32x16)0, (f32x16)0};
   float ks[2] = {0.0f, 0.0f};
   reduce_pair_wave<U>(K, V, H * kD, base, 0, N, pc.sub, S, pc.two, lds.slot[pc.sub], acc, ks);
-  auto make_ops = [&](ApplyOperands (&op)[2]) {
+  auto pre_ops = [] { return 0; };
+  auto make_ops = [&](ApplyOperands (&op)[2], int) {
     // both heads, also for a one-head pair (its second head is never stored)
     block_sum_state<S, false>(acc, ks, lds.xchg, pc.sub, &st[0][0], true);
     __syncthreads();  // the state is complete; xchg is free for the tile slots
     op[0] = make_apply_operands(st[0]);
     op[1] = make_apply_operands(st[1]);
   };
-  apply_pair_wave<U>(Q, Out, make_ops, eps, H * kD, base, H * kD, base, 0, N, pc.sub, S, pc.two,
-                     lds.slot[pc.sub]);
+  apply_pair_wave<U>(Q, Out, pre_ops, make_ops, eps, H * kD, base, H * kD, base, 0, N, pc.sub, S,
+                     pc.two, lds.slot[pc.sub]);
 }
 
 template <int S, int U>
