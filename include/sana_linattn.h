@@ -85,9 +85,9 @@ typedef enum {
 
 typedef enum {
   SANA_VARIANT_AUTO = 0,   /* by shape and device: SPLIT for N > 1024; for N <= 1024,
-                              FUSED when the call is tiny (B * ceil(H/2) * N <= 4096) or
-                              has at least as many head pairs as co-resident fused blocks
-                              (one per CU on MI355X), SPLIT otherwise */
+                              FUSED when N <= 512, or the call is tiny (P * N <= 4096 for
+                              P = B * ceil(H/2) head pairs), or P * N >= CUs * 512 (P >= 128
+                              at N = 1024 on MI355X's 256 CUs), SPLIT otherwise */
   SANA_VARIANT_SPLIT = 1,  /* two launches: split-N state reduction into per-block partials,
                               then the apply, which sums a head pair's partials in fixed
                               order (bf16); fp32 folds them at the end of the reduction */

@@ -136,7 +136,6 @@ struct DeviceCaps {
   int cus = 0;
   int occ[2][2] = {{1, 1}, {1, 1}};  // [kernel: reduce, apply][dtype]
   int occ_bwd_kv = 1;                // backward k/v pass (bf16)
-  int occ_fused[2] = {1, 1};         // fused kernel [dtype]
 };
 
 const DeviceCaps& device_caps() {
@@ -155,7 +154,6 @@ const DeviceCaps& device_caps() {
       c.occ[1][dt] = occupancy_blocks_per_cu(KernelKind::kApply, dt);
     }
     c.occ_bwd_kv = occupancy_blocks_per_cu(KernelKind::kBwdKV, 1);
-    for (int dt = 0; dt < 2; ++dt) c.occ_fused[dt] = occupancy_blocks_per_cu(KernelKind::kFused, dt);
     caps[dev] = c;
   });
   return caps[dev];
@@ -267,27 +265,30 @@ bool valid_variant(int variant) {
 }
 
 // The kernel arrangement a call runs. AUTO, for sequences up to kFusedMaxN
-// tokens (beyond, the split pair):
-//  * the fused kernel when the whole call is tiny (launch-bound: one launch
-//    beats two), or when there are at least as many head-pair units as
-//    co-resident fused blocks;
-//  * the split pair when there are fewer (most CUs would idle under the
-//    one-block-per-unit fused grid; measured on 2 x 1024 x 36: 14.7 against
-//    15.7 us). Running the fused kernel over whole rounds of units and the
-//    split pair over the rest measured slower on 16 x 1024 x 70 (63.9
-//    against 61.1 us): the short last fused round costs less than two more
-//    launches over its units.
-// Queries the device (CU count, occupancy) once per device.
+// tokens (beyond, the split pair), the fused kernel (one block per head
+// pair over all N tokens: one launch, no partials) when
+//  * the call is tiny (units x N <= kTinyUnitTokens), or
+//  * N <= kFusedMaxN / 2 (a block's whole unit is short), or
+//  * units x N >= (CUs / 2) x kFusedMaxN (enough pairs that the fused grid
+//    keeps the device streaming),
+// else the split pair. Measured, split / fused us (256 CUs): N = 1024 with
+// 36 pairs 14.7 / 15.7, 48 pairs 14.3 / 19.0, 64 pairs 15.2 / 19.3, 96 pairs
+// 19.7 / 21.2, 128 pairs 21.5 / 21.5, 280 pairs 39.2 / 36.5, 560 pairs 65.9 /
+// 57.9; N = 512 with 36 pairs 14.0 / 10.7; N = 256 with 140 pairs 15.7 /
+// 8.1. Running the fused kernel over whole rounds of head pairs and the
+// split pair over the rest measured slower (16 x 1024 x 70: 63.9 against
+// 61.1 us with one fused block per CU): the short last fused round costs
+// less than two more launches over its units.
+// Queries the device's CU count once per device.
 constexpr int64_t kTinyUnitTokens = 4096;  // units x N at or below which one launch wins
 
 int resolve_variant(const Plan& p, int dtype, int variant) {
+  (void)dtype;
   if (variant != SANA_VARIANT_AUTO) return variant;
   if (p.N > kFusedMaxN) return SANA_VARIANT_SPLIT;
-  if (p.units * p.N <= kTinyUnitTokens) return SANA_VARIANT_FUSED;
-  const DeviceCaps& c = device_caps();
-  const int64_t slots =
-      static_cast<int64_t>(c.cus) * c.occ_fused[dtype == SANA_DTYPE_BF16 ? 1 : 0];
-  return p.units < slots ? SANA_VARIANT_SPLIT : SANA_VARIANT_FUSED;
+  if (p.units * p.N <= kTinyUnitTokens || 2 * p.N <= kFusedMaxN) return SANA_VARIANT_FUSED;
+  const int64_t cus = device_caps().cus;
+  return 2 * p.units * p.N >= cus * kFusedMaxN ? SANA_VARIANT_FUSED : SANA_VARIANT_SPLIT;
 }
 
 int kernels_of(int variant) { return variant == SANA_VARIANT_SPLIT ? 2 : 1; }

@@ -74,7 +74,7 @@ Plan make_plan(int64_t B, int64_t N, int64_t H);
 // Fills the chunk counts for the current device (makes HIP queries once per device).
 void fit_plan_to_device(Plan& p, int dtype);
 
-enum class KernelKind { kReduce, kApply, kBwdQ, kBwdKV, kFused };
+enum class KernelKind { kReduce, kApply, kBwdQ, kBwdKV };
 int occupancy_blocks_per_cu(KernelKind kind, int dtype);
 int block_waves(KernelKind kind, int dtype);  // waves per block
 

@@ -1841,7 +1841,6 @@ int block_waves(KernelKind kind, int dtype) {
   switch (kind) {
     case KernelKind::kBwdQ: return kBwqS;
     case KernelKind::kBwdKV: return kBwkvS;
-    case KernelKind::kFused: return dtype == 1 ? kFusS : 2 * kF32S;
     default: break;
   }
   if (dtype != 1) return 2 * kF32S;
@@ -1871,12 +1870,6 @@ int occupancy_blocks_per_cu(KernelKind kind, int dtype) {
     case KernelKind::kBwdKV:
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_kv_bf16_kernel<kBwkvS, kBwkvU>,
                                                        64 * kBwkvS, 0);
-      break;
-    case KernelKind::kFused:
-      e = dtype == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                           &n, fused_bf16_kernel<kFusS, kFusU>, 64 * kFusS, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                           &n, fused_f32_kernel<kF32S, kF32U>, 128 * kF32S, 0);
       break;
   }
   return e == hipSuccess && n > 0 ? n : 1;

@@ -101,13 +101,13 @@ def test_ragged_shapes(B, N, H, dtype):
 
 def test_auto_variant_by_shape():
     """AUTO runs the split pair for N > 1024 and for few head pairs at
-    N <= 1024, the fused kernel for a tiny call and for at least as many head
-    pairs as co-resident fused blocks (one or two per CU, 256 CUs on MI355X:
-    the shapes here sit below 256 or above 512 head pairs); each result
+    N in (512, 1024]; the fused kernel for a tiny call, for N <= 512 and for
+    at least CUs / 2 head pairs at N = 1024 (256 CUs on MI355X); each result
     matches the oracle."""
     t = torch()
     for (B, N, H, want) in ((2, 1024, 36, 2), (1, 64, 2, 1), (1, 2048, 4, 2),
-                            (16, 1024, 70, 1), (16, 1000, 65, 1), (2, 700, 251, 2)):
+                            (16, 1024, 70, 1), (9, 1000, 57, 1), (2, 700, 125, 2),
+                            (2, 512, 72, 1)):
         w = W.custom(f"arr_{B}_{N}_{H}", B, N, H, seed=7 + H)
         print(f"\n[case] AUTO B={B} N={N} H={H}", flush=True)
         x, dev = _inputs(w)
