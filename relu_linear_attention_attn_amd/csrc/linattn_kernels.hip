@@ -1351,12 +1351,11 @@ __device__ __forceinline__ void col_product(const ApplyOperands& op, bf16x8 px, 
   }
 }
 
-
-
 // Sum over the 4 lanes that hold one token's 32 channels (l, l^16, l^32, l^48).
-// (gfx950's permlane16/32_swap builtins would avoid the LDS round trip, but
-// this compiler folds the two results of a swap of x with itself into one
-// register, giving wrong sums; the shuffles are kept.)
+// (gfx950's permlane16/32_swap would avoid the LDS round trip, but this
+// compiler folds the builtin's two results of a swap of x with itself into
+// one register, and the same swaps written as inline assembly gave sums that
+// differ from the shuffles' on the GPU; the shuffles are kept.)
 __device__ __forceinline__ float token_sum(float x) {
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
@@ -1421,7 +1420,11 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
   RowOperands ro[2];
   make_ops(ro);
 
-  auto compute = [&](int64_t i, const u32x4 (&qin)[2], const u32x4 (&gin)[2]) {
+  // stage() moves a tile's lines from registers to LDS; the registers then
+  // take the next tile's loads, which stay in flight while compute() works
+  // from LDS. (Issuing them after compute instead, as the memory-bound
+  // passes do, measured 2.4 us slower here.)
+  auto stage = [&](int64_t i, const u32x4 (&qin)[2], const u32x4 (&gin)[2]) {
     const int64_t n0 = n_lo + (sub + i * S) * kTile;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -1430,6 +1433,9 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       *reinterpret_cast<u32x4*>(w.g + o) = gin[h2];
     }
     wave_lds_order();
+  };
+  auto compute = [&](int64_t i) {
+    const int64_t n0 = n_lo + (sub + i * S) * kTile;
     const bool valid = n0 + col < n_hi;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -1506,9 +1512,11 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
   for (; i0 + U <= mine_whole; i0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      compute(i0 + u, qb[u], gb[u]);
+      stage(i0 + u, qb[u], gb[u]);
       __builtin_amdgcn_sched_barrier(0);
       issue(i0 + u + U, qb[u], gb[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i0 + u);
       const u32x4 o0 = out_line(0), o1 = out_line(1);
       wave_lds_order();
       st16_stream(out_ptr(i0 + u, 0), o0);
@@ -1519,8 +1527,11 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (i0 + u < mine) {
-        compute(i0 + u, qb[u], gb[u]);
+        stage(i0 + u, qb[u], gb[u]);
+        __builtin_amdgcn_sched_barrier(0);
         issue(i0 + u + U, qb[u], gb[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i0 + u);
         const u32x4 o0 = out_line(0), o1 = out_line(1);
         wave_lds_order();
         const int64_t n = n_lo + (sub + (i0 + u) * S) * kTile + t0;
