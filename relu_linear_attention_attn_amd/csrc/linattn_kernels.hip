@@ -358,7 +358,10 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
 //     the block barrier that follows thread 0's acquire.
 // The control word holds (call epoch << 16 | finished blocks). A word left by
 // an earlier call, or garbage, carries another epoch and restarts the count,
-// so the workspace needs no clearing between calls.
+// so the workspace needs no clearing between calls. The last block also sets
+// the word back to 0 (a tag no call carries) once every block has counted
+// in: a launch replayed with the same epoch (a captured HIP graph) then
+// starts its count afresh too.
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -379,6 +382,8 @@ __device__ __forceinline__ bool arrive_last(unsigned long long* ctl, unsigned lo
         break;
     }
     last = static_cast<int64_t>(nxt & 0xFFFFull) == nchunks;
+    // every block of the pair has counted in: nothing else touches the word
+    if (last) __hip_atomic_store(ctl, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   return last != 0;
