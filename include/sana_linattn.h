@@ -41,6 +41,15 @@
  * stream reaches that point. Calls that share a workspace must be ordered on
  * one stream.
  *
+ * Graph capture. A call makes no allocation, copy, memset or synchronising
+ * HIP call on its way to the launches, so it can be captured into a HIP
+ * graph (make one ordinary call on the device first: the device's properties
+ * are looked up once, on first use). A replay reads the captured pointers'
+ * current contents and recomputes the result in full; replays that share a
+ * workspace must not overlap in time. (On ROCm 7 a graph launch costs a few
+ * microseconds more than the call's own launches, so capture pays only where
+ * it removes host work.)
+ *
  * Errors. Calls return a status code and never throw. All argument checks run
  * on the host before any HIP call, so an invalid call enqueues nothing. A
  * failed kernel launch returns SANA_ERR_HIP.

@@ -8,9 +8,10 @@
 // terms computed once per head and reused by every query). The review's
 // "Triton을 통한 학습/추론 가속화" names the element-wise work to keep inside
 // the contractions (activation, precision conversion, padding, division):
-// here ReLU runs on packed bf16 in registers, the [V | 1] padding is a second
-// MFMA against a ones operand, the division is one reciprocal per token, and
-// the bf16 rounding happens on the store.
+// here ReLU runs on packed bf16 in registers, the [V | 1] column is carried
+// alongside (ksum summed from the same registers in the reduction, a third
+// MFMA tile in the apply), the division is one reciprocal per token, and the
+// bf16 rounding happens on the store.
 //
 // Tensors are [B][N][H][d], d = 32. One wave owns one head over a run of
 // 16-token tiles; a block holds a head pair (2 x 64 bytes = one 128-byte line
@@ -22,7 +23,8 @@
 //           MFMA wants 8 consecutive tokens of one channel per lane, while
 //           memory holds 8 consecutive channels of one token, so each tile
 //           is staged through the wave's own LDS slot and gathered back
-//           transposed. ksum is the same contraction against ones.
+//           transposed. ksum is summed on the VALU from the same gathered
+//           phi(k) values, each widened exactly from bf16.
 //   apply:  out^T = KV^T phi(Q_tile)^T with v_mfma_f32_16x16x32_bf16, K = d
 //           in one instruction. The fp32 state is split into bf16 hi + lo
 //           parts (x = hi + lo to ~2^-17 relative), so the products keep
@@ -555,7 +557,10 @@ __device__ __forceinline__ void apply_pair_wave(const unsigned short* __restrict
     return Out + obase + (n_lo + (sub + i * S) * kTile + t0 + 8 * h2) * orow + 8 * j;
   };
   // Main loop over this wave's tiles that lie wholly inside the range: no
-  // branches, unconditional stores, U tiles in flight.
+  // branches, unconditional stores, the loads of U tiles issued ahead. (The
+  // compiler's wait before a tile also covers the stores and loads issued
+  // before the loads it needs, so fewer are in flight at that point than U
+  // tiles; variants that kept more in flight measured slower.)
   const int64_t whole = two ? (n_hi - n_lo) / kTile : 0;
   const int64_t mine_whole = whole > sub ? (whole - sub + S - 1) / S : 0;
   int64_t i0 = 0;
@@ -1791,7 +1796,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_block_states_kernel(
   }
 }
 
-// token sub-streams per head (S) and tiles in flight per wave (U)
+// token sub-streams per head (S) and tiles whose loads a wave issues ahead (U)
 constexpr int kRedS = 8, kRedU = 2;
 constexpr int kAppS = 8, kAppU = 2;
 // Dynamic LDS the bf16 apply requests on top of its own (about 25 KB), only

@@ -3,62 +3,132 @@
 A captured launch keeps the arguments it was captured with, among them the
 per-call tag of the control words through which the last block of a head
 pair folds the pair's partials (the fp32 reduction and sana_linattn_kv_state).
-Each case captures one call, then replays the graph four times; before each
-replay the inputs are overwritten with new values (eager work on the same
-stream, then a device synchronisation), and every replay's result must equal,
-bit for bit, an eager call on the same inputs with its own workspace (same
-kernels, grids and summation order). The eager results are themselves checked
-against the oracle by the parity tests."""
+Each case captures one call through the C ABI, then replays the graph four
+times; before each replay the inputs are overwritten with new values (eager
+work on the same stream, then a device synchronisation), and every replay's
+outputs must equal, bit for bit, an eager call on the same inputs with a
+workspace of its own (same kernels, grids and summation order). The eager
+results are themselves checked against the oracle by the parity tests."""
 import ctypes
 
 import numpy as np
 import pytest
 
 import relu_linear_attention_attn_amd as R
-from relu_linear_attention_attn_amd import workloads as W
 
-from gpu_util import to_device, to_host, torch
+from gpu_util import torch
 
 REPLAYS = 4
+BF16, F32 = R.DTYPE_BF16, R.DTYPE_F32
 
 
 def _stream():
     return torch().cuda.current_stream().cuda_stream
 
 
-def _ws(size_fn, *args):
-    t = torch()
+def _size(fn, *args):
     n = ctypes.c_size_t(0)
-    assert size_fn(*args, ctypes.byref(n)) == 0
-    return t.empty(max(n.value, 256), dtype=t.uint8, device="cuda")
+    assert fn(*args, ctypes.byref(n)) == 0
+    return max(n.value, 256)
 
 
-def _fwd(dev, w, out, ws, noalloc=False):
+def _p(x):
+    return x.data_ptr()
+
+
+class Case:
+    """One entry point: the tensors it reads (rewritten before each replay),
+    the tensors it writes (compared), its workspace size and the call."""
+
+    def __init__(self, inputs, outputs, ws_bytes, call):
+        self.inputs, self.outputs, self.ws_bytes, self.call = inputs, outputs, ws_bytes, call
+
+
+def _fwd_case(B, N, H, dt, noalloc=False, variant=None):
     lib = R.lib()
-    dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
-    ptrs = (dev["q"].data_ptr(), dev["k"].data_ptr(), dev["v"].data_ptr(), out.data_ptr())
-    if noalloc:
-        return lib.sana_linattn_fwd_noalloc(*ptrs, w.B, w.N, w.H, 32, w.eps, dt, _stream())
-    return lib.sana_linattn_fwd(*ptrs, w.B, w.N, w.H, 32, w.eps, dt, ws.data_ptr(), ws.numel(),
-                                _stream())
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_workspace_size, B, N, H, 32, dt)
+
+    def call(t, ws_t):
+        ptrs = (_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["out"]), B, N, H, 32, 1e-6, dt)
+        if noalloc:
+            return lib.sana_linattn_fwd_noalloc(*ptrs, _stream())
+        if variant is not None:
+            return lib.sana_linattn_fwd_variant(*ptrs, variant, _p(ws_t), ws_t.numel(), _stream())
+        return lib.sana_linattn_fwd(*ptrs, _p(ws_t), ws_t.numel(), _stream())
+    return Case({c: (shape, dt) for c in "qkv"}, {"out": (shape, dt)}, ws, call)
 
 
-def _kv_state(dev, w, state, ws):
-    dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
-    return R.lib().sana_linattn_kv_state(dev["k"].data_ptr(), dev["v"].data_ptr(),
-                                         state.data_ptr(), w.B, w.N, w.H, 32, dt, ws.data_ptr(),
-                                         ws.numel(), _stream())
+def _kv_case(B, N, H, dt):
+    lib = R.lib()
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_workspace_size, B, N, H, 32, dt)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_kv_state(_p(t["k"]), _p(t["v"]), _p(t["state"]), B, N, H, 32, dt,
+                                         _p(ws_t), ws_t.numel(), _stream())
+    return Case({c: (shape, dt) for c in "kv"}, {"state": ((B, H, 32, 33), F32)}, ws, call)
+
+
+def _bwd_case(B, N, H):
+    lib = R.lib()
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_bwd_workspace_size, B, N, H, 32, BF16)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_bwd(_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["g"]), _p(t["dq"]),
+                                    _p(t["dk"]), _p(t["dv"]), B, N, H, 32, 1e-6, BF16, _p(ws_t),
+                                    ws_t.numel(), _stream())
+    return Case({c: (shape, BF16) for c in "qkvg"}, {c: (shape, BF16) for c in ("dq", "dk", "dv")},
+                ws, call)
+
+
+def _block_causal_case(B, N, H, L, dt):
+    lib = R.lib()
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_block_causal_workspace_size, B, N, H, 32, L, dt)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_fwd_block_causal(_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["out"]),
+                                                 B, N, H, 32, L, 1e-6, dt, _p(ws_t), ws_t.numel(),
+                                                 _stream())
+    return Case({c: (shape, dt) for c in "qkv"}, {"out": (shape, dt)}, ws, call)
+
+
+def _qkv_case(B, N, C, H):
+    lib = R.lib()
+    D = H * 32
+    ws = _size(lib.sana_linattn_qkv_workspace_size, B, N, C, H, 32)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_qkv_fwd(_p(t["x"]), _p(t["w"]), _p(t["q"]), _p(t["out"]), B, N, C,
+                                        H, 32, 1e-6, _p(ws_t), ws_t.numel(), None, 0, _stream())
+    return Case({"x": ((B, N, C), BF16), "w": ((3 * D, C), BF16)},
+                {"q": ((B, N, H, 32), BF16), "out": ((B, N, H, 32), BF16)}, ws, call)
 
 
 CASES = {
-    # fp32 beyond the fused range: reduction with the fold, then the apply
-    "fwd_f32_split": (W.custom("g_f32", 2, 3000, 5, dtype="f32", seed=71), "fwd"),
-    "noalloc_f32_split": (W.custom("g_f32_na", 1, 4100, 6, dtype="f32", seed=72), "noalloc"),
+    # fp32 beyond the fused range: the reduction folds, then the apply
+    "fwd_f32_split": lambda: _fwd_case(2, 3000, 5, F32),
+    "noalloc_f32_split": lambda: _fwd_case(1, 4100, 6, F32, noalloc=True),
     # bf16 state alone: the bf16 reduction with the fold
-    "kv_state_bf16": (W.custom("g_kv", 2, 5000, 7, seed=73), "kv"),
-    # bf16 split forward (partials straight to the apply, no fold)
-    "fwd_bf16_split": (W.custom("g_bf16", 1, 8192, 6, seed=74), "fwd"),
+    "kv_state_bf16": lambda: _kv_case(2, 5000, 7, BF16),
+    # bf16 split forward (partials straight to the apply) and fused
+    "fwd_bf16_split": lambda: _fwd_case(1, 8192, 6, BF16),
+    "fwd_bf16_fused": lambda: _fwd_case(2, 700, 9, BF16, variant=R.VARIANT_FUSED),
+    "bwd_bf16": lambda: _bwd_case(1, 3000, 5),
+    # fp32 block-causal: the folding reduction over blocks, the scan, the apply
+    "block_causal_f32": lambda: _block_causal_case(2, 2048, 3, 512, F32),
+    "qkv_bf16": lambda: _qkv_case(1, 700, 200, 5),
 }
+
+
+def _fill(x, dtype, rng, scale=1.0):
+    """Seeded values (bf16 from fp32 draws) written into tensor x in place."""
+    t = torch()
+    a = rng.standard_normal(x.numel()).astype(np.float32) * np.float32(scale)
+    src = t.from_numpy(a).reshape(x.shape).cuda()
+    x.copy_(src.to(x.dtype))
 
 
 @pytest.mark.gpu
@@ -66,49 +136,41 @@ CASES = {
 def test_graph_replays_match_eager_calls(case):
     t = torch()
     assert t.cuda.is_available(), "GPU tests need a ROCm GPU"
-    w, kind = CASES[case]
-    dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
-    print(f"\n[case] graph {case}: {w.name} {w.shape} {w.dtype}", flush=True)
-    lib = R.lib()
-    x = W.generate(w)
-    dev = {c: to_device(x[c], w.dtype) for c in "qkv"}
-    if kind == "kv":
-        res = t.empty((w.B, w.H, 32, 33), dtype=t.float32, device="cuda")
-        ws = _ws(lib.sana_linattn_workspace_size, w.B, w.N, w.H, 32, dt)
-        run = lambda: _kv_state(dev, w, res, ws)  # noqa: E731
-    else:
-        res = t.empty_like(dev["q"])
-        ws = _ws(lib.sana_linattn_workspace_size, w.B, w.N, w.H, 32, dt)
-        run = lambda: _fwd(dev, w, res, ws, noalloc=kind == "noalloc")  # noqa: E731
-    assert run() == 0  # eager first: device look-ups happen outside the capture
+    print(f"\n[case] graph {case}", flush=True)
+    c = CASES[case]()
+    tdt = {BF16: t.bfloat16, F32: t.float32}
+    rng = np.random.default_rng(2000 + sorted(CASES).index(case))
+    scale = {"w": 1.0 / np.sqrt(200.0)}
+
+    def alloc(spec):
+        return {n: t.empty(shape, dtype=tdt[dt], device="cuda") for n, (shape, dt) in spec.items()}
+
+    ten = alloc(c.inputs)
+    ten.update(alloc(c.outputs))
+    for n in c.inputs:
+        _fill(ten[n], c.inputs[n][1], rng, scale.get(n, 1.0))
+    ws = t.empty(c.ws_bytes, dtype=t.uint8, device="cuda")
+    assert c.call(ten, ws) == 0  # eager first: one-time device look-ups outside the capture
     t.cuda.synchronize()
 
     g = t.cuda.CUDAGraph()
     with t.cuda.graph(g):
-        status = run()
+        status = c.call(ten, ws)
     assert status == 0
 
-    ref_ws = _ws(lib.sana_linattn_workspace_size, w.B, w.N, w.H, 32, dt)
-    rng = np.random.default_rng(1000 + sorted(CASES).index(case))
+    ref = {n: v for n, v in ten.items() if n in c.inputs}
+    ref.update(alloc(c.outputs))
+    ref_ws = t.empty(c.ws_bytes, dtype=t.uint8, device="cuda")
     for r in range(REPLAYS):
-        # new inputs for this replay: scaled and shifted copies of the first draw
-        for c in "qkv":
-            src = t.from_numpy(np.ascontiguousarray(x[c]).view(np.int16)).view(t.bfloat16) \
-                if w.dtype == "bf16" else t.from_numpy(np.ascontiguousarray(x[c]))
-            a, b = float(rng.uniform(0.5, 2.0)), float(rng.normal(0, 0.5))
-            dev[c].copy_((src.float() * a + b).to(dev[c].dtype).cuda())
+        for n in c.inputs:
+            _fill(ten[n], c.inputs[n][1], rng, scale.get(n, 1.0) * float(rng.uniform(0.5, 2.0)))
         t.cuda.synchronize()
         g.replay()
         t.cuda.synchronize()
-        got = res.clone()
-        if kind == "kv":
-            ref = t.empty_like(res)
-            assert _kv_state(dev, w, ref, ref_ws) == 0
-        else:
-            ref = t.empty_like(res)
-            assert _fwd(dev, w, ref, ref_ws) == 0
+        got = {n: ten[n].clone() for n in c.outputs}
+        assert c.call(ref, ref_ws) == 0
         t.cuda.synchronize()
-        gb = to_host(got, "f32" if kind == "kv" else w.dtype)
-        rb = to_host(ref, "f32" if kind == "kv" else w.dtype)
-        assert np.array_equal(gb.view(np.uint8), rb.view(np.uint8)), \
-            f"{case}: replay {r} differs from the eager call on the same inputs"
+        for n in c.outputs:
+            a = got[n].view(t.uint8).cpu().numpy()
+            b = ref[n].view(t.uint8).cpu().numpy()
+            assert np.array_equal(a, b), f"{case}: replay {r} output {n} differs from the eager call"
