@@ -48,7 +48,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the device takes a few hundred steps to "
+                         "settle (20 left the ELU + 1 forward 13 us per step slow)")
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
     ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "block_causal", "qkv"],
