@@ -104,10 +104,10 @@ int64_t qkv_m_tiles(int64_t N);
 int64_t qkv_grid_blocks(int64_t B, int64_t N, int64_t H);
 hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partials, int64_t B,
                             int64_t N, int64_t C, int64_t H, int64_t GM, hipStream_t stream);
-// Backward (bf16). bwd_q runs on balanced ranges: it sums the partials of
-// launch_reduce(fold = false) for the state (slots by red_rule), writes dq
-// and writes [dS | dz] partials on the balanced ranges' slots; bwd_kv sums
-// those and writes dk and dv.
+// Backward (bf16). bwd_q runs on the state reduction's grid: it sums the
+// partials of launch_reduce(fold = false) for the state (slots by
+// red_rule), writes dq and writes [dS | dz] partials in the same slots (same
+// rule); bwd_kv sums those and writes dk and dv.
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
                         const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream);
 hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,

@@ -1695,17 +1695,19 @@ struct StateOps {
   }
 };
 
-// bwd_q over one block's range of the flattened (unit, tile) index
-// (balanced ranges of Qb tiles): the forward state of a unit is the sum of
-// the reduction's partials fwd_parts (slots by rule Qf, see slot_count), and
-// the block writes its [dS | dz] partial of each unit it touches to
-// grad_parts (partial g - first, like the balanced reduction).
+// bwd_q over one block's range of the flattened (unit, tile) index, on the
+// state reduction's grid: one (unit, chunk) item in XCD runs when C > 0,
+// else balanced ranges of Qb tiles. The forward state of a unit is the sum
+// of the reduction's partials fwd_parts (slots by rule Qf, see slot_count),
+// and the block writes its [dS | dz] partial of each unit it touches to
+// grad_parts in the reduction's slot (the chunk, or g - first), so the
+// partials follow the same slot rule.
 template <int S, int U>
 __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ G,
     unsigned short* __restrict__ dQ, const float* __restrict__ fwd_parts,
     float* __restrict__ grad_parts, float eps, int64_t N, int64_t H, int64_t pairs, int64_t T,
-    int64_t Qb, int64_t F, int64_t slots, int64_t Qf) {
+    int64_t Qb, int64_t F, int64_t slots, int64_t Qf, int64_t C, int64_t X) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
   union alignas(16) Lds {
     BwdQWaveLds wave[S];
@@ -1715,11 +1717,22 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
   __shared__ f32x4 stage[2 * kSF / 4];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = blockIdx.x;
-  const int64_t f_lo = g * Qb;
-  const int64_t f_hi = f_lo + Qb < F ? f_lo + Qb : F;
+  // C > 0: (unit, chunk) items of Qb tiles in XCD runs, as the reduction's
+  // chunked grid; the chunk is the slot. C = 0: balanced ranges.
+  int64_t f_lo, f_hi, chunk = 0;
+  if (C > 0) {
+    const Item it = xcd_item(F / T, C, X);
+    if (!it.valid) return;  // the whole block
+    chunk = it.chunk;
+    f_lo = it.unit * T + it.chunk * Qb;
+    f_hi = f_lo + Qb < (it.unit + 1) * T ? f_lo + Qb : (it.unit + 1) * T;
+  } else {
+    f_lo = g * Qb;
+    f_hi = f_lo + Qb < F ? f_lo + Qb : F;
+  }
   for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
-    const SlotRange sr = slot_range(unit, T, Qb);
+    const int64_t slot = C > 0 ? chunk : g - slot_range(unit, T, Qb).first;
     const StateOps ops{reinterpret_cast<const f32x4*>(fwd_parts + unit * slots * 2 * kSF),
                        slot_count(unit, T, Qf), sg.two, stage};
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
@@ -1727,7 +1740,7 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     grad_q_pair_wave<U>(Q, G, dQ, ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
                         sg.n_hi, sub, S, sg.two, lds.wave[sub], acc, ks);
     block_sum_state<S, false>(acc, ks, lds.xchg, sub,
-                              grad_parts + (unit * slots + (g - sr.first)) * 2 * kSF, sg.two);
+                              grad_parts + (unit * slots + slot) * 2 * kSF, sg.two);
     __syncthreads();  // the LDS (tiles, exchange, stage) is reused by the next segment
   }
 }
@@ -1956,11 +1969,17 @@ hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partial
 
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
                         const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_q_bf16_kernel<kBwqS, kBwqU>), dim3((unsigned)p.red_blocks),
-                     dim3(64 * kBwqS), 0, stream, static_cast<const unsigned short*>(q),
+  // the reduction's grid: (unit, chunk) items when the plan has them, else
+  // balanced ranges; the [dS | dz] partials then follow the same slot rule
+  const bool chunked = p.red_cb > 0;
+  const int64_t X = apply_xcds(p);
+  const int64_t blocks = chunked ? xcd_grid(p.units * p.red_cb, X) : p.red_blocks;
+  hipLaunchKernelGGL((bwd_q_bf16_kernel<kBwqS, kBwqU>), dim3((unsigned)blocks), dim3(64 * kBwqS),
+                     0, stream, static_cast<const unsigned short*>(q),
                      static_cast<const unsigned short*>(g), static_cast<unsigned short*>(dq),
-                     fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles, p.red_q,
-                     p.units * p.tiles, p.slots, red_rule(p));
+                     fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles,
+                     chunked ? p.red_cq : p.red_q, p.units * p.tiles, p.slots, red_rule(p),
+                     chunked ? p.red_cb : int64_t(0), X);
   return hipGetLastError();
 }
 
@@ -1972,7 +1991,7 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
                      dim3(64 * kBwkvS), 0, stream, static_cast<const unsigned short*>(k),
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(dk),
                      static_cast<unsigned short*>(dv), grad_parts, p.N, p.H, p.pairs, p.units,
-                     p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, p.red_q, p.slots);
+                     p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, red_rule(p), p.slots);
   return hipGetLastError();
 }
 
