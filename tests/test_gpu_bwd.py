@@ -104,6 +104,25 @@ def test_bwd_matches_oracle(name):
     _check(got, ref, x, w.eps, name)
 
 
+def test_bwd_video_1m_tokens_two_heads():
+    """The 16 x 65,536-token video shape (B=1, N=1,048,576, H=36): the state
+    reduction's (head pair, chunk) grid cuts each of the 18 head pairs into
+    14 chunks here, so the q pass's chunked grid and the k/v pass's sum of
+    its 14 partials per pair run at their largest. Heads 0 and 35 (the
+    first and last pair) compared in full, every token."""
+    w = W.WORKLOADS["video_1m_tokens"]
+    print(f"\n[case] bwd workload {w.name} shape {w.shape}", flush=True)
+    x, dev = _inputs(w)
+    grads = R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps)
+    torch().cuda.synchronize()
+    del dev
+    for h in (0, w.H - 1):
+        xs = {t: np.ascontiguousarray(x[t][:, :, h:h + 1]) for t in "qkvg"}
+        got = [to_host(gr[:, :, h:h + 1].contiguous(), "bf16") for gr in grads]
+        ref = LB.linattn_bwd_from_inputs(xs["q"], xs["k"], xs["v"], xs["g"], w.eps, "bf16")
+        _check(got, ref, xs, w.eps, f"{w.name} head {h}")
+
+
 RAGGED = [(1, 1, 1), (1, 2, 2), (2, 15, 3), (1, 16, 1), (3, 17, 5), (1, 100, 2), (2, 257, 3),
           (1, 1000, 7), (2, 4099, 4), (1, 33000, 3)]
 
