@@ -18,14 +18,17 @@ phi = ReLU and eps:
   out_i = phi(q_i) S_c(i)[:, :d] / (phi(q_i) . S_c(i)[:, d] + eps)
 
 L = n gives the forward pass of oracle/linattn.py; L = 1 gives token-causal
-attention (query i sees keys 0..i).
+attention (query i sees keys 0..i). token_causal_rows computes single rows of
+that token-causal attention straight from the definition, for sequences whose
+per-token prefix states would not fit in memory.
 
 Pins (tests/test_oracle_block_causal.py): the explicit masked n x n form
 (mask[i][n] = block(n) <= block(i)) on small inputs; L = n against the
 non-causal oracle; L = 1 against a lower-triangular mask; the first block
 against the non-causal attention of that block alone; no output depends on
 later blocks (changing them leaves earlier outputs bitwise unchanged);
-invariance to the choice of L within one block-aligned split. A test plants
+invariance to the choice of L within one block-aligned split; the rows of
+token_causal_rows against the lower-triangular masked form. A test plants
 mistakes in this module and checks that the pins catch each one.
 """
 from __future__ import annotations
@@ -93,6 +96,25 @@ def block_causal_from_inputs(q: np.ndarray, k: np.ndarray, v: np.ndarray, L: int
         for h in range(H):
             out[b, :, h] = block_causal_head(to_f64(q[b, :, h], dtype), to_f64(k[b, :, h], dtype),
                                              to_f64(v[b, :, h], dtype), L, eps)
+    return out
+
+
+def token_causal_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, eps: float) -> np.ndarray:
+    """Token-causal attention (blocks of one token) of one head, [n, d]
+    float64, at the listed query rows only, each from its own definition:
+    S_i = phi(K[0..i])^T [V[0..i] | 1], out_i = phi(q_i) S_i[:, :d] /
+    (phi(q_i) . S_i[:, d] + eps). Cost O(i d^2) per row, memory O(i d): the
+    way to check single outputs of sequences too long for the prefix states
+    of every token. Returns [len(rows), d]."""
+    n, d = q.shape
+    out = np.empty((len(rows), d))
+    for r, i in enumerate(rows):
+        if not 0 <= i < n:
+            raise IndexError(f"row {i} outside 0..{n - 1}")
+        pk = phi(k[:i + 1])
+        s = pk.T @ np.concatenate([v[:i + 1], np.ones((i + 1, 1))], axis=1)
+        pq = phi(q[i])
+        out[r] = (pq @ s[:, :d]) / (pq @ s[:, d] + eps)
     return out
 
 

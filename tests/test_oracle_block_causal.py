@@ -1,7 +1,7 @@
 """Pins of the block-causal oracle (oracle/linattn_block_causal.py) against
 things other than itself: the explicit masked n x n form, the non-causal
-oracle (one block), token-causal attention (blocks of one token), the first
-block alone, and causality (no output depends on later blocks). A planted
+oracle (one block), token-causal attention (blocks of one token, and single
+rows from their definition), the first block alone, and causality (no output depends on later blocks). A planted
 mistake anywhere in the oracle must fail at least one pin."""
 import numpy as np
 import pytest
@@ -108,8 +108,23 @@ def pin_causality():
     return None
 
 
+def pin_token_causal_rows():
+    """Single token-causal rows, each from its definition, against the
+    lower-triangular masked form: the first row, rows inside, the last."""
+    eps = 1e-3
+    q, k, v = _inputs(10, 1, 37, 2)
+    mask = np.tril(np.ones((37, 37)))
+    want = BC.masked_quadratic_fp64(q, k, v, mask, eps)
+    rows = [0, 1, 15, 16, 17, 36]
+    for h in range(2):
+        got = BC.token_causal_rows(q[0, :, h], k[0, :, h], v[0, :, h], rows, eps)
+        if _rel(got, want[0, rows, h]) > 1e-12:
+            return f"head {h}: rows differ from the masked form by {_rel(got, want[0, rows, h]):.2e}"
+    return None
+
+
 PINS = [pin_masked_form_exact, pin_masked_quadratic, pin_one_block_is_noncausal,
-        pin_token_causal, pin_first_block_alone, pin_causality]
+        pin_token_causal, pin_first_block_alone, pin_causality, pin_token_causal_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -183,7 +198,26 @@ def _mut_apply(kind):
     return f
 
 
+def _mut_rows(kind):
+    def f(q, k, v, rows, eps):
+        n, d = q.shape
+        out = np.empty((len(rows), d))
+        for r, i in enumerate(rows):
+            hi = {"sees_next_key": min(i + 2, n), "misses_own_key": i}.get(kind, i + 1)
+            pk = L.phi(k[:hi])
+            s = pk.T @ np.concatenate([v[:hi], np.ones((hi, 1))], axis=1)
+            if kind == "den_without_keys":
+                s[:, d] = 0.0
+            pq = L.phi(q[i])
+            out[r] = (pq @ s[:, :d]) / (pq @ s[:, d] + eps)
+        return out
+    return f
+
+
 MUTANTS = {
+    "rows_see_next_key": ("token_causal_rows", _mut_rows("sees_next_key")),
+    "rows_miss_own_key": ("token_causal_rows", _mut_rows("misses_own_key")),
+    "rows_den_without_keys": ("token_causal_rows", _mut_rows("den_without_keys")),
     "exclusive_prefix": ("prefix_states", _mut_prefix("exclusive")),
     "no_prefix": ("prefix_states", _mut_prefix("no_prefix")),
     "reversed_prefix": ("prefix_states", _mut_prefix("reversed")),
