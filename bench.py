@@ -2,14 +2,16 @@
 """Throughput of ReLU linear self-attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--op fwd|bwd|block_causal|qkv] [--block L] [--fmap relu|elu1|cos]
+                    [--op fwd|bwd|block_causal|causal|qkv] [--block L] [--fmap relu|elu1|cos]
                     [--layout contiguous|packed] [--dtype bf16|f32]
 
 A step is one full forward pass (the state reduction over token ranges into
 per-block partials, then the apply, which sums them) - or, with --op bwd, one
 full backward pass (the state reduction, the q pass that also reduces the
 state gradient, the k/v pass), with --op block_causal one block-causal
-forward pass (per-block states, their prefix scan, the apply), or with --op
+forward pass (per-block states, their prefix scan, the apply), with --op
+causal one token-causal forward pass (chunk states, their exclusive prefix
+scan, the chunk-wise apply), or with --op
 qkv the QKV projection with the state in its epilogue, then the apply - over
 one batch of synthetic input already
 resident in HBM. Prints one JSON line: tokens/s (B*N per step), the whole
@@ -34,6 +36,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E spec peak
 METRIC = "linear-attn fwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
 METRIC_BWD = "linear-attn bwd tokens/s + achieved HBM GB/s (% roofline), N=16384 D=2240"
 METRIC_BC = "block-causal linear-attn fwd tokens/s + achieved HBM GB/s (% roofline)"
+METRIC_CAUSAL = "token-causal linear-attn fwd tokens/s + achieved HBM GB/s (% roofline)"
 METRIC_QKV = "QKV projection + linear-attn fwd tokens/s (state in the projection epilogue)"
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 CSRC = os.path.join(ROOT, "relu_linear_attention_attn_amd", "csrc")
@@ -41,7 +44,8 @@ TRAFFIC_FILES = {"fwd": os.path.join(ROOT, "profiles", "traffic_latent_4096px.js
                  "bwd": os.path.join(ROOT, "profiles", "traffic_bwd_latent_4096px.json"),
                  "block_causal": os.path.join(ROOT, "profiles",
                                               "traffic_block_causal_video_1m_tokens.json"),
-                 "qkv": os.path.join(ROOT, "profiles", "traffic_qkv_latent_4096px.json")}
+                 "qkv": os.path.join(ROOT, "profiles", "traffic_qkv_latent_4096px.json"),
+                 "causal": os.path.join(ROOT, "profiles", "traffic_causal_latent_4096px.json")}
 
 
 def parse():
@@ -53,9 +57,11 @@ def parse():
                          "settle (20 left the ELU + 1 forward 13 us per step slow)")
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
-    ap.add_argument("--op", default="fwd", choices=["fwd", "bwd", "block_causal", "qkv"],
-                    help="forward pass (the headline), backward pass, or block-causal "
-                         "forward (default workload: the 16-frame video, one block per frame)")
+    ap.add_argument("--op", default="fwd",
+                    choices=["fwd", "bwd", "block_causal", "causal", "qkv"],
+                    help="forward pass (the headline), backward pass, block-causal forward "
+                         "(default workload: the 16-frame video, one block per frame), "
+                         "token-causal forward, or QKV projection + forward")
     ap.add_argument("--fmap", default="relu", choices=["relu", "elu1", "cos"],
                     help="feature map of the forward (other than relu: the split kernels)")
     ap.add_argument("--dtype", default=None, choices=["bf16", "f32"],
@@ -436,31 +442,44 @@ def cpu_baseline_block_causal(w, inputs, block: int, budget_s: float):
                         f"block-causal forward, blocks of {block}")
 
 
-def run_block_causal(args, w):
-    """Block-causal forward: one JSON line like the forward's (see main)."""
+def cpu_baseline_causal(w, inputs, budget_s: float):
+    """The token-causal oracle (blocks of one token) on whole heads."""
+    return cpu_baseline_block_causal(w, inputs, 1, budget_s)
+
+
+def run_block_causal(args, w, causal: bool = False):
+    """Block-causal forward (or, causal=True, token-causal): one JSON line
+    like the forward's (see main)."""
     import numpy as np
     import torch
 
     import relu_linear_attention_attn_amd as R
 
-    block = args.block
-    log(args, f"workload {w.name} {w.shape} {w.dtype} block-causal, blocks of {block}: "
-              "generating inputs")
+    block = 1 if causal else args.block
+    what = "token-causal" if causal else f"block-causal, blocks of {block}"
+    log(args, f"workload {w.name} {w.shape} {w.dtype} {what}: generating inputs")
     from relu_linear_attention_attn_amd import workloads as W
     x = W.generate(w)
     elem = w.B * w.N * w.H * w.d * w.itemsize
     n_sets = n_input_sets(args, 4 * elem)
     sets = device_sets(x, "qkv", w.dtype, ("out",), n_sets)
     dt = R.DTYPE_BF16 if w.dtype == "bf16" else R.DTYPE_F32
-    ws = torch.empty(R.block_causal_workspace_size(w.B, w.N, w.H, block, w.d, dt),
-                     dtype=torch.uint8, device="cuda")
+    if causal:
+        ws_bytes = R.causal_workspace_size(w.B, w.N, w.H, w.d, dt)
+    else:
+        ws_bytes = R.block_causal_workspace_size(w.B, w.N, w.H, block, w.d, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
 
     def step(i, events=None):
         d = sets[i % n_sets]
-        R.forward_block_causal(d["q"], d["k"], d["v"], block, eps=w.eps, out=d["out"],
-                               workspace=ws, events=events)
+        if causal:
+            R.forward_causal(d["q"], d["k"], d["v"], eps=w.eps, out=d["out"], workspace=ws,
+                             events=events)
+        else:
+            R.forward_block_causal(d["q"], d["k"], d["v"], block, eps=w.eps, out=d["out"],
+                                   workspace=ws, events=events)
 
-    names = ["reduce", "scan", "apply"]
+    names = ["states", "scan", "apply"] if causal else ["reduce", "scan", "apply"]
     for i in range(args.warmup):
         step(i)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -476,12 +495,22 @@ def run_block_causal(args, w):
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
     step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
-    alg_bytes = {"reduce": 2 * elem, "apply": 2 * elem}
+    if causal:
+        # states: read k, v, write the chunk states; apply: read q, k, v and
+        # the chunk prefixes, write out (the workspace holds exactly the states)
+        alg_bytes = {"states": 2 * elem + ws_bytes, "apply": 4 * elem + ws_bytes}
+    else:
+        alg_bytes = {"reduce": 2 * elem, "apply": 2 * elem}
     dominant = max(alg_bytes, key=lambda n: per_kernel[n])
     achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-3) / 1e9
     path_gbps = w.algorithmic_bytes() / (ms_per_step * 1e-3) / 1e9
+    op = "causal" if causal else "block_causal"
+    config = {"workload": w.name, "op": op, "B": w.B, "N": w.N, "H": w.H, "d": w.d, "D": w.D,
+              "eps": w.eps, "input_sets": n_sets}
+    if not causal:
+        config["block"] = block
     result = {
-        "metric": METRIC_BC,
+        "metric": METRIC_CAUSAL if causal else METRIC_BC,
         "value": w.B * w.N / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -493,8 +522,7 @@ def run_block_causal(args, w):
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "op": "block_causal", "block": block, "B": w.B,
-                   "N": w.N, "H": w.H, "d": w.d, "D": w.D, "eps": w.eps, "input_sets": n_sets},
+        "config": config,
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "kernel_ms": per_kernel,
@@ -503,8 +531,11 @@ def run_block_causal(args, w):
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(dominant, w.name, "block_causal", block)},
+                     "traffic": measured_traffic(dominant, w.name, op,
+                                                 None if causal else block)},
     }
+    if causal:
+        result["path_bytes_moved_per_step"] = sum(alg_bytes.values()) + 2 * ws_bytes
     if args.copy_mib == 0:
         ceil = copy_ceiling(ws.device)
         result["achievable_copy"] = dict(ceil, step_frac=path_gbps / ceil["gbps"])
@@ -516,7 +547,8 @@ def run_block_causal(args, w):
         torch.cuda.synchronize()
     if args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline_block_causal(w, x, block, args.cpu_seconds)
+        result["cpu_baseline"] = (cpu_baseline_causal(w, x, args.cpu_seconds) if causal else
+                                  cpu_baseline_block_causal(w, x, block, args.cpu_seconds))
     print(json.dumps(result), flush=True)
 
 
@@ -735,6 +767,10 @@ def main():
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         R.lib()
         return run_block_causal(args, W.WORKLOADS[args.workload or "video_1m_tokens"])
+    if args.op == "causal":
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        R.lib()
+        return run_block_causal(args, w, causal=True)
     if args.op == "qkv":
         assert torch.cuda.is_available(), "bench.py needs a GPU"
         R.lib()

@@ -17,7 +17,8 @@
  * (phd-frog.tistory.com/40), section 2.2, "선형 어텐션 블럭" (ReLU linear
  * attention; the shared terms computed once and reused by every query).
  * eps is on no page: it is added to the denominator, outside the dot product.
- * Attention is non-causal; no positional term touches q or k.
+ * Attention is non-causal except in the block-causal and token-causal entry
+ * points below; no positional term touches q or k.
  *
  * Layout. q, k, v and out are dense, row-major [B][N][H][d] tensors of one
  * dtype: element (b, n, h, c) sits at index ((b*N + n)*H + h)*d + c. This is
@@ -373,6 +374,35 @@ sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* 
                                                      sana_dtype_t dtype, void* workspace,
                                                      size_t workspace_bytes, hipEvent_t* events,
                                                      int n_events, hipStream_t stream);
+
+/*
+ * Token-causal attention: query i of a batch item attends to keys 0..i of
+ * the same item. This is the block-causal attention above (the blog's
+ * "技术演进" section) with blocks of one token, computed with chunked
+ * prefix states instead of one state per token:
+ *
+ *     out_i = phi(q_i) S_i[:, :d] / (phi(q_i) . S_i[:, d] + eps),
+ *     S_i   = sum_{n <= i} phi(k_n)^T [v_n | 1].
+ *
+ * bf16 only (SANA_DTYPE_F32 returns SANA_ERR_UNSUPPORTED); same tensors,
+ * layout, alignment, overlap and eps rules as sana_linattn_fwd. The result
+ * equals sana_linattn_fwd_block_causal with block = 1 (up to rounding) at a
+ * fraction of its cost. Three kernels: the states of chunks of consecutive
+ * tokens, their exclusive prefix over each head's chunks (fixed order:
+ * results are bitwise repeatable), and the apply, which walks each chunk
+ * tile by tile from its prefix. workspace: at least
+ * sana_linattn_causal_workspace_size(...) bytes, 256-byte aligned, contents
+ * irrelevant on entry and undefined on return, overlapping no tensor of the
+ * call. events (may be NULL): events[0] is recorded before the first kernel
+ * and events[i] after kernel i (n_events >= 4).
+ */
+sana_status_t sana_linattn_causal_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
+                                                sana_dtype_t dtype, size_t* bytes);
+sana_status_t sana_linattn_fwd_causal(const void* q, const void* k, const void* v, void* out,
+                                      int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                      sana_dtype_t dtype, void* workspace,
+                                      size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                      hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" for a value
  * outside sana_status_t). Never NULL; the string is owned by the library. */

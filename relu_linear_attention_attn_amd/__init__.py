@@ -1,5 +1,5 @@
-"""ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward (non-causal and
-block-causal, ReLU or another feature map; also from the QKV projection, with the
+"""ReLU linear self-attention (Sana Linear DiT) for AMD MI355X: forward (non-causal,
+block-causal and token-causal, ReLU or another feature map; also from the QKV projection, with the
 state formed in the projection's epilogue) and backward.
 
 The compute runs in hand-written HIP kernels behind a C ABI
@@ -19,8 +19,10 @@ from .binding import (  # noqa: F401
     backward,
     block_causal_workspace_size,
     bwd_workspace_size,
+    causal_workspace_size,
     forward,
     forward_block_causal,
+    forward_causal,
     forward_fmap,
     forward_noalloc,
     forward_profiled,

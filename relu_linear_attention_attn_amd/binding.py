@@ -44,6 +44,8 @@ EXPORTS = (
     "sana_linattn_block_causal_workspace_size",
     "sana_linattn_fwd_block_causal",
     "sana_linattn_fwd_block_causal_profiled",
+    "sana_linattn_causal_workspace_size",
+    "sana_linattn_fwd_causal",
     "sana_linattn_fwd_fmap",
     "sana_linattn_fwd_strided",
     "sana_linattn_qkv_workspace_size",
@@ -120,6 +122,10 @@ def lib() -> ctypes.CDLL:
             ctypes.c_float, ctypes.c_int, _vp, _sz, _vp]
         L.sana_linattn_fwd_block_causal_profiled.argtypes = [_vp] * 4 + [_i64] * 5 + [
             ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+        L.sana_linattn_causal_workspace_size.argtypes = [_i64] * 4 + [ctypes.c_int,
+                                                                  ctypes.POINTER(_sz)]
+        L.sana_linattn_fwd_causal.argtypes = [_vp] * 4 + [_i64] * 4 + [
+            ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         L.sana_linattn_fwd_fmap.argtypes = [_vp] * 4 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
             ctypes.c_int, _vp]
@@ -130,7 +136,8 @@ def lib() -> ctypes.CDLL:
         L.sana_linattn_qkv_fwd.argtypes = [_vp] * 4 + [_i64] * 5 + [
             ctypes.c_float, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
-                     "sana_linattn_fwd_block_causal_profiled", "sana_linattn_fwd_fmap",
+                     "sana_linattn_fwd_block_causal_profiled", "sana_linattn_causal_workspace_size",
+                     "sana_linattn_fwd_causal", "sana_linattn_fwd_fmap",
                      "sana_linattn_fwd_strided",
                      "sana_linattn_qkv_workspace_size", "sana_linattn_qkv_fwd"):
             getattr(L, name).restype = ctypes.c_int
@@ -427,6 +434,47 @@ def forward_block_causal(q, k, v, block: int, eps: float = 1e-6, heads: Optional
         arr = (_vp * len(events))(*[e.cuda_event for e in events])
         _check(lib().sana_linattn_fwd_block_causal_profiled(*args, arr, len(events), _stream(q)),
                "sana_linattn_fwd_block_causal_profiled")
+    return out
+
+
+def causal_workspace_size(B: int, N: int, H: int, d: int = HEAD_DIM,
+                          dtype: int = DTYPE_BF16) -> int:
+    n = _sz(0)
+    _check(lib().sana_linattn_causal_workspace_size(B, N, H, d, dtype, ctypes.byref(n)),
+           "sana_linattn_causal_workspace_size")
+    return n.value
+
+
+def forward_causal(q, k, v, eps: float = 1e-6, heads: Optional[int] = None, out=None,
+                   workspace=None, events=None):
+    """Token-causal forward (bf16): query i sees keys 0..i of its batch item.
+    Same tensors as forward(); events: optional list of 4 torch.cuda.Event
+    recorded around the three kernels."""
+    torch = _torch()
+    B, N, H, d = _shape(q, heads)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", q)
+    _check_tensor(v, "v", q)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q)
+    if workspace is None:
+        workspace = torch.empty(max(causal_workspace_size(B, N, H, d, dt), 1),
+                                dtype=torch.uint8, device=q.device)
+    wb = workspace.numel() * workspace.element_size()
+    arr, n_ev = None, 0
+    if events is not None:
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event on first record
+                e.record()
+        arr = (_vp * len(events))(*[e.cuda_event for e in events])
+        n_ev = len(events)
+    _check(lib().sana_linattn_fwd_causal(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         B, N, H, d, float(eps), dt, workspace.data_ptr(), wb,
+                                         arr, n_ev, _stream(q)),
+           "sana_linattn_fwd_causal")
     return out
 
 

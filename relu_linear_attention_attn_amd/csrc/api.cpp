@@ -524,6 +524,65 @@ struct QkvPlan {
   size_t workspace_bytes; // the partial states
 };
 
+// Token-causal attention: chunks per unit so that every unit's chunks make
+// one round of kCausalWaves waves (the plan does not depend on the device).
+sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype, CausalPlan* cp,
+                          size_t* tensor_bytes) {
+  sana_status_t s = check_shape(B, N, H, d, dtype, tensor_bytes);
+  if (s != SANA_OK) return s;
+  if (dtype != SANA_DTYPE_BF16) return SANA_ERR_UNSUPPORTED;
+  cp->B = B;
+  cp->N = N;
+  cp->H = H;
+  cp->pairs = cdiv(H, 2);
+  cp->units = B * cp->pairs;
+  cp->tiles = cdiv(N, kTile);
+  const int64_t c = clamp64(kCausalWaves / cp->units, 1, std::min(cp->tiles, kMaxCausalChunks));
+  cp->W = cdiv(cp->tiles, c);
+  if (cp->W > 1 && cp->W % 2 == 0) ++cp->W;  // odd: chunk starts off power-of-two alignment
+  cp->chunks = cdiv(cp->tiles, cp->W);
+  cp->parts_bytes =
+      align_up(static_cast<size_t>(cp->units) * static_cast<size_t>(cp->chunks) * 2 * kStateFloats * 4);
+  if (cdiv(cp->units * cp->chunks, 8) > INT32_MAX || cp->units * 2 * kStateFloats > INT64_C(1) << 40)
+    return SANA_ERR_INVALID_ARG;
+  return SANA_OK;
+}
+
+sana_status_t causal_forward(const void* q, const void* k, const void* v, void* out, int64_t B,
+                             int64_t N, int64_t H, int64_t d, float eps, int dtype,
+                             void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                             int n_events, hipStream_t stream) {
+  CausalPlan cp;
+  size_t tb = 0;
+  sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, &tb);
+  if (s != SANA_OK) return s;
+  if (events) {
+    if (n_events < 4) return SANA_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+      if (!events[i]) return SANA_ERR_INVALID_ARG;
+  }
+  if (!q || !k || !v || !out) return SANA_ERR_INVALID_ARG;
+  if ((s = check_eps(eps)) != SANA_OK) return s;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return SANA_ERR_ALIGNMENT;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+    return SANA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < cp.parts_bytes) return SANA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SANA_ERR_ALIGNMENT;
+  for (const void* t : {static_cast<const void*>(out), q, k, v})
+    if (overlaps(t, tb, workspace, cp.parts_bytes)) return SANA_ERR_INVALID_ARG;
+
+  (void)hipGetLastError();
+  float* parts = static_cast<float*>(workspace);
+  auto mark = [&](int i) { return !events || hipEventRecord(events[i], stream) == hipSuccess; };
+  if (!mark(0)) return SANA_ERR_HIP;
+  if (launch_causal_states(cp, k, v, parts, stream) != hipSuccess) return SANA_ERR_HIP;
+  if (!mark(1)) return SANA_ERR_HIP;
+  if (launch_causal_scan(cp, parts, stream) != hipSuccess) return SANA_ERR_HIP;
+  if (!mark(2)) return SANA_ERR_HIP;
+  if (launch_causal_apply(cp, q, k, v, out, parts, eps, stream) != hipSuccess) return SANA_ERR_HIP;
+  return mark(3) ? SANA_OK : SANA_ERR_HIP;
+}
+
 sana_status_t plan_qkv(int64_t B, int64_t N, int64_t C, int64_t H, int64_t d, QkvPlan* qp) {
   size_t tb = 0;
   sana_status_t s = check_shape(B, N, H, d, SANA_DTYPE_BF16, &tb);
@@ -825,6 +884,27 @@ sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* 
   if (!events) return SANA_ERR_INVALID_ARG;
   return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
                             workspace_bytes, events, n_events, stream);
+}
+
+sana_status_t sana_linattn_causal_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,
+                                                sana_dtype_t dtype, size_t* bytes) {
+  if (!bytes) return SANA_ERR_INVALID_ARG;
+  *bytes = 0;
+  sana::CausalPlan cp;
+  size_t tb = 0;
+  const sana_status_t s = sana::plan_causal(B, N, H, d, dtype, &cp, &tb);
+  if (s != SANA_OK) return s;
+  *bytes = cp.parts_bytes;
+  return SANA_OK;
+}
+
+sana_status_t sana_linattn_fwd_causal(const void* q, const void* k, const void* v, void* out,
+                                      int64_t B, int64_t N, int64_t H, int64_t d, float eps,
+                                      sana_dtype_t dtype, void* workspace,
+                                      size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                      hipStream_t stream) {
+  return sana::causal_forward(q, k, v, out, B, N, H, d, eps, dtype, workspace, workspace_bytes,
+                              events, n_events, stream);
 }
 
 sana_status_t sana_linattn_qkv_workspace_size(int64_t B, int64_t N, int64_t C, int64_t H,

@@ -117,6 +117,20 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
 // reduction's result (bf16: its partials, launch_reduce(fold = false);
 // fp32: its folded state) into prefix, a [p.B][H][d][d+1] state for
 // launch_apply.
+// Token-causal attention (bf16): chunk states, their exclusive prefix,
+// then the causal apply. One wave per (unit, chunk) of W tiles; chunks per
+// unit chosen so the units' chunks make one round of kCausalWaves waves.
+constexpr int64_t kCausalWaves = 2048;      // 8 waves on each of 256 CUs
+constexpr int64_t kMaxCausalChunks = 1024;  // per unit
+struct CausalPlan {
+  int64_t B, N, H, pairs, units, tiles, chunks, W;
+  size_t parts_bytes;  // [units][chunks][2][d][d+1] fp32
+};
+hipError_t launch_causal_states(const CausalPlan& cp, const void* k, const void* v, float* parts,
+                                hipStream_t stream);
+hipError_t launch_causal_scan(const CausalPlan& cp, float* parts, hipStream_t stream);
+hipError_t launch_causal_apply(const CausalPlan& cp, const void* q, const void* k, const void* v,
+                               void* out, const float* parts, float eps, hipStream_t stream);
 hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* partials,
                               const float* state, float* prefix, hipStream_t stream);
 int64_t scan_grid_threads(int64_t B, int64_t pairs);  // work-items of that launch

@@ -1771,6 +1771,284 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
                        sub, S, sg.two, tiles[sub]);
 }
 
+// ------------------------------------------------------ causal attention
+//
+// Token-causal attention (query i attends to keys 0..i of its batch item),
+// computed chunk-wise: an exclusive prefix of chunk states plus, inside a
+// chunk, the running state and the causal terms of each 16-token tile.
+// Every wave owns one (unit, chunk) of W consecutive tiles; waves are
+// numbered chunk-major (wave = chunk * units + unit), so the 8 waves of a
+// block stream the same token range of 8 head pairs.
+//   causal_states_kernel: S_c = phi(K_c)^T [V_c | 1] per chunk, from the
+//     wave's registers to parts[unit][chunk] ([2][d][d+1], both heads);
+//   causal_scan_kernel: parts[unit][c] <- sum of parts[unit][0 .. c-1];
+//   causal_apply_kernel: from that prefix P, tile by tile:
+//     out_i = phi(q_i) (P + sum_{j <= i in the tile} phi(k_j)^T [v_j | 1])
+//     split into numerator and normaliser, then P += the tile's state.
+
+struct CausalWave {
+  int64_t unit, chunk, b, h, n_lo, n_hi;
+  bool two, valid;
+};
+
+__device__ __forceinline__ CausalWave causal_wave(int64_t units, int64_t chunks, int64_t pairs,
+                                                  int64_t H, int64_t N, int64_t W, int S) {
+  CausalWave c;
+  const int64_t wg = blockIdx.x * (int64_t)S + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.chunk = wg / units;
+  c.unit = wg - c.chunk * units;
+  c.valid = c.chunk < chunks;
+  c.b = c.unit / pairs;
+  c.h = 2 * (c.unit - c.b * pairs);
+  c.two = c.h + 1 < H;
+  c.n_lo = c.chunk * W * kTile;
+  c.n_hi = c.n_lo + W * kTile < N ? c.n_lo + W * kTile : N;
+  return c;
+}
+
+// A head pair's state from the 32x32 MFMA accumulator layout (lane l,
+// register r: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32; ksum of
+// channel c split over lanes c and c + 32) to [2][d][d+1] at dst, and back.
+// store_acc_state is called by the whole wave; dst may be LDS or global.
+__device__ __forceinline__ void store_acc_state(float* dst, const f32x16 (&acc)[2],
+                                                const float (&ks)[2]) {
+  const int l = lane_id();
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      dst[hh * kSF + (8 * (r >> 2) + 4 * (l >> 5) + (r & 3)) * kSC + (l & 31)] = acc[hh][r];
+    const float kq = ks[hh] + __shfl_xor(ks[hh], 32);
+    if (l < 32) dst[hh * kSF + l * kSC + kD] = kq;
+  }
+}
+
+__device__ __forceinline__ void load_acc_state(const float* src, f32x16 (&acc)[2],
+                                               float (&ks)[2]) {
+  const int l = lane_id();
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      acc[hh][r] = src[hh * kSF + (8 * (r >> 2) + 4 * (l >> 5) + (r & 3)) * kSC + (l & 31)];
+    ks[hh] = l < 32 ? src[hh * kSF + l * kSC + kD] : 0.0f;
+  }
+}
+
+constexpr int kCausalStateU = 2;  // tiles a states wave issues ahead
+
+template <int S>
+__global__ __launch_bounds__(64 * S) void causal_states_kernel(
+    const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
+    float* __restrict__ parts, int64_t N, int64_t H, int64_t pairs, int64_t units,
+    int64_t chunks, int64_t W) {
+  __shared__ alignas(16) unsigned char slots[S][2 * kTileBytes];
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const CausalWave cw = causal_wave(units, chunks, pairs, H, N, W, S);
+  if (!cw.valid) return;  // the whole wave; no block barrier below
+  f32x16 acc[2] = {(f32x16)0, (f32x16)0};
+  float ks[2] = {0.0f, 0.0f};
+  reduce_pair_wave<kCausalStateU>(K, V, H * kD, (cw.b * N * H + cw.h) * kD, cw.n_lo, cw.n_hi, 0, 1,
+                          cw.two, slots[sub], acc, ks);
+  store_acc_state(parts + (cw.unit * chunks + cw.chunk) * 2 * kSF, acc, ks);
+}
+
+// One thread per (unit, state element): the exclusive prefix over the
+// unit's chunks, in chunk order, in place.
+constexpr int kCausalScanThreads = 256;
+__global__ __launch_bounds__(kCausalScanThreads) void causal_scan_kernel(
+    float* __restrict__ parts, int64_t units, int64_t chunks) {
+  const int64_t t = blockIdx.x * (int64_t)kCausalScanThreads + threadIdx.x;
+  if (t >= units * 2 * kSF) return;
+  const int64_t unit = t / (2 * kSF);
+  float* x = parts + unit * chunks * 2 * kSF + (t - unit * 2 * kSF);
+  constexpr int kBatch = 8;  // loads in flight
+  float run = 0.0f;
+  for (int64_t c0 = 0; c0 < chunks; c0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = c0 + u < chunks ? x[(c0 + u) * 2 * kSF] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (c0 + u < chunks) x[(c0 + u) * 2 * kSF] = run;
+      run += v[u];
+    }
+  }
+}
+
+// One head's 16 outputs of a tile: the state term as apply_head's, plus the
+// tile's own causal term. Scores s[j][i] = phi(k_j) . phi(q_i) come from a
+// 16x16x32 MFMA with phi(k) as A (row = key token, the piece at the same
+// place as q's) and phi(q) as B, so a lane holds s[4 (l / 16) + r][l % 16],
+// r = 0..3. Keys after the query are zeroed and the scores split into bf16
+// hi + lo. One more 16x16x32 MFMA per accumulator adds [V | 1]^T s^T: its
+// 32 contraction slots are, per 16-lane group g, the hi parts of keys
+// 4 g .. 4 g + 3 (slots 8 g .. 8 g + 3) and their lo parts (the next four),
+// so the lane's own scores are its B operand [hi | lo] and its A operand is
+// v of those 4 keys at the tile row's output channel, twice (va[t], one
+// transpose read); a ones operand gives the normaliser's part. Every MFMA
+// on an accumulator then has one shape. (Chaining a 16x16x16 MFMA onto a
+// 16x16x32 result gave results that changed by an ulp from run to run: the
+// compiler left too few cycles between the two shapes, and the dependent
+// MFMA sometimes read the accumulator before the lo part of the state had
+// been added.)
+__device__ __forceinline__ u32x4 causal_head(const ApplyOperands& op, u32x4 qpiece,
+                                             u32x4 kpiece, s16x4 va0, s16x4 va1, float eps) {
+  const bf16x8 qv = __builtin_bit_cast(bf16x8, relu_bf16x8(qpiece));
+  const bf16x8 kv = __builtin_bit_cast(bf16x8, relu_bf16x8(kpiece));
+  f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qv, (f32x4)0, 0, 0, 0);
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_lo, qv, a0, 0, 0, 0);
+  f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_hi, qv, (f32x4)0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv1_lo, qv, a1, 0, 0, 0);
+  f32x4 ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_hi, qv, (f32x4)0, 0, 0, 0);
+  ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ks_lo, qv, ad, 0, 0, 0);
+  const f32x4 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qv, (f32x4)0, 0, 0, 0);
+  const int l = lane_id();
+  const int i = l & 15, j0 = 4 * (l >> 4);
+  s16x8 ss;  // [hi of the 4 scores | lo of the 4 scores]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float x = j0 + r <= i ? sc[r] : 0.0f;
+    const __bf16 h = (__bf16)x;
+    ss[r] = __builtin_bit_cast(short, h);
+    ss[4 + r] = __builtin_bit_cast(short, (__bf16)(x - (float)h));
+  }
+  const bf16x8 sb = __builtin_bit_cast(bf16x8, ss);
+  const bf16x8 v0 = __builtin_bit_cast(
+      bf16x8, (s16x8){va0[0], va0[1], va0[2], va0[3], va0[0], va0[1], va0[2], va0[3]});
+  const bf16x8 v1 = __builtin_bit_cast(
+      bf16x8, (s16x8){va1[0], va1[1], va1[2], va1[3], va1[0], va1[1], va1[2], va1[3]});
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, (s16x8)(short)0x3F80);  // bf16 1.0
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, sb, a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, sb, a1, 0, 0, 0);
+  ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, sb, ad, 0, 0, 0);
+  const float rinv = 1.0f / (ad[0] + eps);
+  bf16x8 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    o[r] = (__bf16)(a0[r] * rinv);
+    o[4 + r] = (__bf16)(a1[r] * rinv);
+  }
+  return __builtin_bit_cast(u32x4, o);
+}
+
+// v of keys 4 (l / 16) + 0..3 at the output channel that row l % 16 of tile
+// t stands for (8 (i / 4) + 4 t + i % 4, as in make_apply_operands): one
+// 64-bit transpose read per lane. In each 16-lane group lane p reads token
+// 4 (l / 16) + p / 4, channels 8 (p % 4) + 4 t .. + 3, and lane m receives
+// element m % 4 of the rows of lanes 4 k + m / 4, k = 0..3.
+__device__ __forceinline__ s16x4 gather_v_keys4(const unsigned char* vtile, int hh, int t) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int l = lane_id();
+  const int p = l & 15;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(vtile + tile_off(4 * (l >> 4) + (p >> 2), hh * 4 + (p & 3)) + 8 * t));
+}
+
+struct alignas(16) CausalWaveLds {
+  unsigned char q[kTileBytes];
+  unsigned char k[kTileBytes];
+  unsigned char v[kTileBytes];
+  float st[2 * kSF];
+};
+
+template <int S>
+__global__ __launch_bounds__(64 * S) void causal_apply_kernel(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
+    const unsigned short* __restrict__ V, unsigned short* __restrict__ Out,
+    const float* __restrict__ parts, float eps, int64_t N, int64_t H, int64_t pairs,
+    int64_t units, int64_t chunks, int64_t W) {
+  __shared__ CausalWaveLds lds[S];
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const CausalWave cw = causal_wave(units, chunks, pairs, H, N, W, S);
+  if (!cw.valid) return;  // the whole wave; no block barrier below
+  CausalWaveLds& w = lds[sub];
+  const int64_t row = H * kD;
+  const int64_t base = (cw.b * N * H + cw.h) * kD;
+  const int l = lane_id();
+  const int t0 = l >> 3, j = l & 7;
+  const int jl = cw.two ? j : (j & 3);
+  const int g = l >> 4, col = l & 15;
+  const int64_t n_lo = cw.n_lo, n_hi = cw.n_hi;
+  const int64_t tiles = (n_hi - n_lo + kTile - 1) / kTile;
+
+  f32x16 acc[2];
+  float ks[2];
+  load_acc_state(parts + (cw.unit * chunks + cw.chunk) * 2 * kSF, acc, ks);
+
+  // unpredicated loads: a token past n_hi reads row n_lo (its k is zeroed
+  // when staged and its output is not stored)
+  u32x4 qb[2], kb[2], vb[2];
+  auto issue = [&](int64_t i) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int64_t n = n_lo + i * kTile + t0 + 8 * h2;
+      const int64_t off = base + (n < n_hi ? n : n_lo) * row + 8 * jl;
+      qb[h2] = ld16_stream(Q + off);
+      kb[h2] = ld16_stream(K + off);
+      vb[h2] = ld16_stream(V + off);
+    }
+  };
+  issue(0);
+  for (int64_t i = 0; i < tiles; ++i) {
+    const int64_t n0 = n_lo + i * kTile;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int o = tile_off(t0 + 8 * h2, j);
+      *reinterpret_cast<u32x4*>(w.q + o) = qb[h2];
+      *reinterpret_cast<u32x4*>(w.k + o) = n0 + t0 + 8 * h2 < n_hi ? kb[h2] : (u32x4)0;
+      *reinterpret_cast<u32x4*>(w.v + o) = vb[h2];
+    }
+    store_acc_state(w.st, acc, ks);  // P: every token before this tile
+    wave_lds_order();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(i + 1);  // the next tile's loads overlap this tile's work
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 res[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const ApplyOperands op = make_apply_operands(w.st + hh * kSF);
+      const int po = tile_off(col, hh * 4 + g);
+      const u32x4 qp = *reinterpret_cast<const u32x4*>(w.q + po);
+      const u32x4 kp = *reinterpret_cast<const u32x4*>(w.k + po);
+      res[hh] = causal_head(op, qp, kp, gather_v_keys4(w.v, hh, 0), gather_v_keys4(w.v, hh, 1),
+                            eps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P += this tile's state (keys past n_hi are zero)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const s16x8 a = gather_tokens8(w.k, hh);
+      const s16x8 bv = gather_tokens8(w.v, hh);
+      const s16x8 pk = __builtin_elementwise_max(a, (s16x8)0);
+      acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                        __builtin_bit_cast(bf16x8, bv),
+                                                        acc[hh], 0, 0, 0);
+      const u32x4 wk = __builtin_bit_cast(u32x4, pk);
+      float sum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sum += __builtin_bit_cast(float, wk[e] << 16);
+        sum += __builtin_bit_cast(float, wk[e] & 0xFFFF0000u);
+      }
+      ks[hh] += sum;
+    }
+    wave_lds_order();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<u32x4*>(w.q + tile_off(col, hh * 4 + g)) = res[hh];
+    wave_lds_order();
+    const u32x4 o0 = *reinterpret_cast<const u32x4*>(w.q + tile_off(t0, j));
+    const u32x4 o1 = *reinterpret_cast<const u32x4*>(w.q + tile_off(t0 + 8, j));
+    wave_lds_order();
+    if (cw.two || j < 4) {
+      const int64_t n = n0 + t0;
+      if (n < n_hi) st16_stream(Out + base + n * row + 8 * j, o0);
+      if (n + 8 < n_hi) st16_stream(Out + base + (n + 8) * row + 8 * j, o1);
+    }
+  }
+}
+
 // ------------------------------------------------------ block-causal scan
 //
 // Block-causal attention runs the forward kernels on a plan whose batch
@@ -1992,6 +2270,37 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
                      static_cast<const unsigned short*>(v), static_cast<unsigned short*>(dk),
                      static_cast<unsigned short*>(dv), grad_parts, p.N, p.H, p.pairs, p.units,
                      p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, red_rule(p), p.slots);
+  return hipGetLastError();
+}
+
+constexpr int kCausalS = 8;  // waves per block of the causal kernels (independent waves)
+
+hipError_t launch_causal_states(const CausalPlan& cp, const void* k, const void* v, float* parts,
+                                hipStream_t stream) {
+  const int64_t blocks = (cp.units * cp.chunks + kCausalS - 1) / kCausalS;
+  hipLaunchKernelGGL((causal_states_kernel<kCausalS>), dim3((unsigned)blocks),
+                     dim3(64 * kCausalS), 0, stream, static_cast<const unsigned short*>(k),
+                     static_cast<const unsigned short*>(v), parts, cp.N, cp.H, cp.pairs,
+                     cp.units, cp.chunks, cp.W);
+  return hipGetLastError();
+}
+
+hipError_t launch_causal_scan(const CausalPlan& cp, float* parts, hipStream_t stream) {
+  const int64_t threads = cp.units * 2 * kSF;
+  hipLaunchKernelGGL(causal_scan_kernel,
+                     dim3((unsigned)((threads + kCausalScanThreads - 1) / kCausalScanThreads)),
+                     dim3(kCausalScanThreads), 0, stream, parts, cp.units, cp.chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_causal_apply(const CausalPlan& cp, const void* q, const void* k, const void* v,
+                               void* out, const float* parts, float eps, hipStream_t stream) {
+  const int64_t blocks = (cp.units * cp.chunks + kCausalS - 1) / kCausalS;
+  hipLaunchKernelGGL((causal_apply_kernel<kCausalS>), dim3((unsigned)blocks),
+                     dim3(64 * kCausalS), 0, stream, static_cast<const unsigned short*>(q),
+                     static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
+                     static_cast<unsigned short*>(out), parts, eps, cp.N, cp.H, cp.pairs,
+                     cp.units, cp.chunks, cp.W);
   return hipGetLastError();
 }
 

@@ -266,6 +266,46 @@ def test_block_causal_workspace_and_errors(L):
                                                     BF16, P_W, need, events, 3, None) == INVALID
 
 
+def cws(L, B, N, H, d=32, dt=BF16):
+    n = ctypes.c_size_t(123)
+    st = L.sana_linattn_causal_workspace_size(B, N, H, d, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_causal_workspace_and_errors(L):
+    state = 2 * 32 * 33 * 4                                  # one head pair's [2][d][d+1] fp32
+    st, n = cws(L, 2, 16384, 70)
+    assert st == OK and n % 256 == 0 and n >= 70 * state     # at least one chunk per head pair
+    assert n <= 70 * 1024 * state                            # at most 1024 chunks per head pair
+    assert cws(L, 1, 1, 2) == (OK, state)                    # one token: one chunk
+    assert cws(L, 1, 16, 3)[1] == 2 * state                  # two head pairs, one chunk each
+    assert 512 * state <= cws(L, 1, 1 << 20, 2)[1] <= 1024 * state  # long sequence: the cap
+    assert cws(L, 1, 1000, 2, dt=F32) == (UNSUPPORTED, 0)    # bf16 only
+    assert cws(L, 1, 1000, 2, d=64) == (UNSUPPORTED, 0)
+    assert cws(L, 0, 1000, 2) == (INVALID, 0)
+    assert cws(L, 1, 0, 2) == (INVALID, 0)
+    assert L.sana_linattn_causal_workspace_size(1, 16, 2, 32, BF16, None) == INVALID
+    need = cws(L, 1, 64, 2)[1]
+    f = L.sana_linattn_fwd_causal
+
+    def call(q=P_Q, k=P_K, v=P_V, o=P_O, eps=1e-6, dt=BF16, ws=P_W, wsb=need, ev=None, nev=0):
+        return f(q, k, v, o, 1, 64, 2, 32, eps, dt, ws, wsb, ev, nev, None)
+    assert call(o=None) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(q=P_Q + 8) == ALIGNMENT
+    assert call(o=P_Q + 64) == INVALID                       # out overlaps q
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(ws=P_W + 16) == ALIGNMENT
+    assert call(ws=P_O) == INVALID                           # workspace overlaps out
+    events = (ctypes.c_void_p * 3)(None, None, None)
+    assert call(ev=events, nev=3) == INVALID                 # needs 4 events
+    events4 = (ctypes.c_void_p * 4)(None, None, None, None)
+    assert call(ev=events4, nev=4) == INVALID                # null events
+
+
 def test_fwd_fmap_rejects_invalid_arguments(L):
     need = ws_size(L, 1, 64, 2)[1]
 

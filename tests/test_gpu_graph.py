@@ -95,6 +95,18 @@ def _block_causal_case(B, N, H, L, dt):
     return Case({c: (shape, dt) for c in "qkv"}, {"out": (shape, dt)}, ws, call)
 
 
+def _causal_case(B, N, H):
+    lib = R.lib()
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_causal_workspace_size, B, N, H, 32, BF16)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_fwd_causal(_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["out"]), B, N,
+                                           H, 32, 1e-6, BF16, _p(ws_t), ws_t.numel(), None, 0,
+                                           _stream())
+    return Case({c: (shape, BF16) for c in "qkv"}, {"out": (shape, BF16)}, ws, call)
+
+
 def _qkv_case(B, N, C, H):
     lib = R.lib()
     D = H * 32
@@ -120,6 +132,8 @@ CASES = {
     # fp32 block-causal: the folding reduction over blocks, the scan, the apply
     "block_causal_f32": lambda: _block_causal_case(2, 2048, 3, 512, F32),
     "qkv_bf16": lambda: _qkv_case(1, 700, 200, 5),
+    # token-causal: chunk states, their prefix scan, the chunk-wise apply
+    "causal_bf16": lambda: _causal_case(2, 3000, 5),
 }
 
 
