@@ -537,9 +537,12 @@ sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
   cp->pairs = cdiv(H, 2);
   cp->units = B * cp->pairs;
   cp->tiles = cdiv(N, kTile);
+  // about kCausalWaves waves in all (one block of 8 per CU) over chunks of
+  // W tiles (rounding W to an odd count, as once tried, left the 4096px
+  // latent with 245 blocks instead of 254 and the apply 8 us slower; chunks
+  // of W and W + 1 tiles were 1 us slower than a short last chunk)
   const int64_t c = clamp64(kCausalWaves / cp->units, 1, std::min(cp->tiles, kMaxCausalChunks));
   cp->W = cdiv(cp->tiles, c);
-  if (cp->W > 1 && cp->W % 2 == 0) ++cp->W;  // odd: chunk starts off power-of-two alignment
   cp->chunks = cdiv(cp->tiles, cp->W);
   cp->parts_bytes =
       align_up(static_cast<size_t>(cp->units) * static_cast<size_t>(cp->chunks) * 2 * kStateFloats * 4);

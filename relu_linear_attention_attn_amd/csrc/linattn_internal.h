@@ -118,8 +118,8 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
 // fp32: its folded state) into prefix, a [p.B][H][d][d+1] state for
 // launch_apply.
 // Token-causal attention (bf16): chunk states, their exclusive prefix,
-// then the causal apply. One wave per (unit, chunk) of W tiles; chunks per
-// unit chosen so the units' chunks make one round of kCausalWaves waves.
+// then the causal apply. One wave per (unit, chunk of W consecutive tiles);
+// W chosen so the units' chunks make one round of about kCausalWaves waves.
 constexpr int64_t kCausalWaves = 2048;      // 8 waves on each of 256 CUs
 constexpr int64_t kMaxCausalChunks = 1024;  // per unit
 struct CausalPlan {
