@@ -136,7 +136,9 @@ def _kernel_key(name: str) -> str:
     for k, v in (("reduce_bf16_kernel", "reduce"), ("apply_bf16_kernel", "apply"),
                  ("scan_block_states_kernel", "scan"), ("qkv_state_kernel", "projection"),
                  ("fused_bf16_kernel", "fused"), ("bwd_q_bf16_kernel", "bwd_q"),
-                 ("bwd_kv_bf16_kernel", "bwd_kv"), ("bitwise_not", "copy")):
+                 ("bwd_kv_bf16_kernel", "bwd_kv"), ("causal_states_kernel", "states"),
+                 ("causal_scan_kernel", "scan"), ("causal_apply_kernel", "apply"),
+                 ("bitwise_not", "copy")):
         if k in name:
             return v
     return ""
