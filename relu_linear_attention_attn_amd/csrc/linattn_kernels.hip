@@ -51,6 +51,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kD = kHeadDim;      // 32
@@ -1811,7 +1812,8 @@ __device__ __forceinline__ CausalWave causal_wave(int64_t units, int64_t chunks,
 // A head pair's state from the 32x32 MFMA accumulator layout (lane l,
 // register r: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32; ksum of
 // channel c split over lanes c and c + 32) to [2][d][d+1] at dst, and back.
-// store_acc_state is called by the whole wave; dst may be LDS or global.
+// store_acc_state is called by the whole wave (dst: the chunk states in the
+// workspace).
 __device__ __forceinline__ void store_acc_state(float* dst, const f32x16 (&acc)[2],
                                                 const float (&ks)[2]) {
   const int l = lane_id();
@@ -1948,11 +1950,75 @@ __device__ __forceinline__ s16x4 gather_v_keys4(const unsigned char* vtile, int 
       (lds_s16x4*)(vtile + tile_off(4 * (l >> 4) + (p >> 2), hh * 4 + (p & 3)) + 8 * t));
 }
 
+// The causal apply's running state P, kept in LDS the way its MFMAs take
+// it: split into bf16 hi + lo and transposed, so the 8 contraction values a
+// lane supplies (input channels 8 (l / 16) .. + 7 of the output channel its
+// MFMA row stands for) are one 16-byte read. The split happens in registers
+// before the store, on the values make_apply_operands would read back, so
+// the operands are the same bits. Rows of kOpPitch bf16 = 80 bytes: a
+// multiple of 16, and 20 banks apart, so the 32 lanes that write one
+// 8-byte piece each to 32 rows meet at most two to a bank.
+constexpr int kOpPitch = 40;
+struct alignas(16) CausalOpsLds {
+  unsigned short hi[2][kD * kOpPitch];  // [head][output channel][input channel]
+  unsigned short lo[2][kD * kOpPitch];
+  unsigned short ks_hi[2][kD];          // [head][input channel]
+  unsigned short ks_lo[2][kD];
+};
+
+// P from the 32x32 MFMA accumulator layout (lane l holds column l % 32, rows
+// 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive input channels per
+// quarter of acc) into ops; called by the whole wave.
+__device__ __forceinline__ void store_acc_ops(CausalOpsLds& o, const f32x16 (&acc)[2],
+                                              const float (&ks)[2]) {
+  const int l = lane_id();
+  const int col = l & 31;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      unsigned int h[2], w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x0 = acc[hh][4 * q + 2 * e], x1 = acc[hh][4 * q + 2 * e + 1];
+        h[e] = cvt_pk_bf16(x0, x1);
+        w[e] = cvt_pk_bf16(x0 - __builtin_bit_cast(float, h[e] << 16),
+                           x1 - __builtin_bit_cast(float, h[e] & 0xFFFF0000u));
+      }
+      const int at = col * kOpPitch + 8 * q + 4 * (l >> 5);
+      *reinterpret_cast<u32x2*>(o.hi[hh] + at) = (u32x2){h[0], h[1]};
+      *reinterpret_cast<u32x2*>(o.lo[hh] + at) = (u32x2){w[0], w[1]};
+    }
+    const float kq = ks[hh] + __shfl_xor(ks[hh], 32);
+    if (l < 32) {
+      const __bf16 kh = (__bf16)kq;
+      o.ks_hi[hh][l] = __builtin_bit_cast(unsigned short, kh);
+      o.ks_lo[hh][l] = __builtin_bit_cast(unsigned short, (__bf16)(kq - (float)kh));
+    }
+  }
+}
+
+// The apply's six A operands of head hh (make_apply_operands's layout).
+__device__ __forceinline__ ApplyOperands load_acc_ops(const CausalOpsLds& o, int hh) {
+  const int l = lane_id();
+  const int g = l >> 4, i = l & 15;
+  const int c0 = 8 * (i >> 2) + (i & 3);  // output channel of row i in tile 0
+  const int a0 = c0 * kOpPitch + 8 * g, a1 = (c0 + 4) * kOpPitch + 8 * g;
+  ApplyOperands op;
+  op.kv0_hi = *reinterpret_cast<const bf16x8*>(o.hi[hh] + a0);
+  op.kv0_lo = *reinterpret_cast<const bf16x8*>(o.lo[hh] + a0);
+  op.kv1_hi = *reinterpret_cast<const bf16x8*>(o.hi[hh] + a1);
+  op.kv1_lo = *reinterpret_cast<const bf16x8*>(o.lo[hh] + a1);
+  op.ks_hi = *reinterpret_cast<const bf16x8*>(o.ks_hi[hh] + 8 * g);
+  op.ks_lo = *reinterpret_cast<const bf16x8*>(o.ks_lo[hh] + 8 * g);
+  return op;
+}
+
 struct alignas(16) CausalWaveLds {
   unsigned char q[kTileBytes];
   unsigned char k[kTileBytes];
   unsigned char v[kTileBytes];
-  float st[2 * kSF];
+  CausalOpsLds ops;
 };
 
 // Tiles whose loads an apply wave has in flight while it works on one.
@@ -2006,7 +2072,7 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
       *reinterpret_cast<u32x4*>(w.k + o) = n0 + t0 + 8 * h2 < n_hi ? kd[h2] : (u32x4)0;
       *reinterpret_cast<u32x4*>(w.v + o) = vd[h2];
     }
-    store_acc_state(w.st, acc, ks);  // P: every token before this tile
+    store_acc_ops(w.ops, acc, ks);  // P: every token before this tile
     wave_lds_order();
     __builtin_amdgcn_sched_barrier(0);
     issue(i + U, qd, kd, vd);
@@ -2014,7 +2080,7 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
     u32x4 res[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const ApplyOperands op = make_apply_operands(w.st + hh * kSF);
+      const ApplyOperands op = load_acc_ops(w.ops, hh);
       const int po = tile_off(col, hh * 4 + g);
       const u32x4 qp = *reinterpret_cast<const u32x4*>(w.q + po);
       const u32x4 kp = *reinterpret_cast<const u32x4*>(w.k + po);
