@@ -173,3 +173,32 @@ def test_causal_video_1m_tokens_sampled_rows():
         dec = {t: decode(x[t][0, :, h], "bf16") for t in "qkv"}
         ref = BC.token_causal_rows(dec["q"], dec["k"], dec["v"], rows, w.eps)
         assert_causal_close(decode(got[0, rows, h], "bf16"), ref, f"video head {h}")
+
+
+def test_causal_workspace_garbage_guards_and_reuse():
+    """A workspace full of NaN bytes on entry, inside a larger buffer, and
+    an output inside a larger buffer: results bitwise those of a fresh
+    call, no byte outside either region touched; the same workspace then
+    serves a smaller shape."""
+    t = torch()
+    pad = 4096
+    shapes = [(2, 3000, 5), (1, 777, 3)]
+    need = max(R.causal_workspace_size(*s) for s in shapes)
+    wbuf = t.full((need + 2 * pad,), 0xA5, dtype=t.uint8, device="cuda")
+    ws = wbuf[pad:pad + need]
+    for i, (B, N, H) in enumerate(shapes):
+        print(f"\n[case] causal guards B={B} N={N} H={H}", flush=True)
+        w = W.custom(f"causal_guard_{i}", B, N, H, seed=76 + i)
+        x, dev = _inputs(w)
+        ref = _run(dev, w.eps)
+        ws.fill_(0xFF)  # NaN floats everywhere in the workspace
+        n = B * N * H * 32
+        obuf = t.full((n + 2 * pad,), 1.5, dtype=t.bfloat16, device="cuda")
+        out = obuf[pad:pad + n].view(B, N, H, 32)
+        R.forward_causal(dev["q"], dev["k"], dev["v"], eps=w.eps, out=out, workspace=ws)
+        t.cuda.synchronize()
+        assert np.array_equal(to_host(out, "bf16"), ref)
+        guards = t.cat([obuf[:pad], obuf[pad + n:]])
+        assert bool((guards == 1.5).all()), "a store landed outside out"
+        wg = t.cat([wbuf[:pad], wbuf[pad + need:]])
+        assert bool((wg == 0xA5).all()), "a store landed outside the workspace"
