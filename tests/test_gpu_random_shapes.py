@@ -1,16 +1,17 @@
 """Seeded random shapes through every entry point, against the CPU float64
 oracles: the forward (each variant and dtype), the strided forward on a
 packed projection output with a random row padding, the other feature maps,
-block-causal attention with a random block length, the backward, and the
-QKV projection path. The shapes are drawn from a fixed seed, with token
+block-causal attention with a random block length, token-causal attention,
+the backward, and the QKV projection path. The shapes are drawn from a fixed seed, with token
 counts near the kernels' boundaries (multiples of the 16-token tile, the
 256-token projection tile, the fused variant's 1024-token limit) more often
 than elsewhere, and small enough for the oracle to finish in seconds.
 
 Tolerances are the ones each entry point's own parity file states: bf16
 max-abs <= 1e-2 and rel-L2 <= 5e-3, fp32 rel-L2 <= 1e-5 (gpu_util); other
-maps max-abs <= max(1e-2, 2^-8 max|ref|); the backward's and the QKV q's
-term-scaled bounds (imported from those files)."""
+maps max-abs <= max(1e-2, 2^-8 max|ref|); token-causal per element
+2^-8 |ref| + 2e-3; the backward's and the QKV q's term-scaled bounds
+(imported from those files)."""
 import numpy as np
 import pytest
 
@@ -135,6 +136,22 @@ def test_block_causal_random(i):
     ref = BC.block_causal_from_inputs(x["q"], x["k"], x["v"], block, w.eps, "bf16")
     assert_close(decode(to_host(out, "bf16"), "bf16"), ref, "bf16",
                  f"block-causal B={B} N={N} H={H} block={block}")
+
+
+@pytest.mark.parametrize("i", range(COUNT))
+def test_causal_random(i):
+    from test_gpu_causal import assert_causal_close
+
+    B, N, H = _draw(1007)[i]
+    w = _workload("causal", B, N, H, "bf16", 7000 + i)
+    print(f"\n[case] random token-causal B={B} N={N} H={H}", flush=True)
+    x = W.generate(w)
+    dev = {t: to_device(x[t], "bf16") for t in "qkv"}
+    out = R.forward_causal(dev["q"], dev["k"], dev["v"], eps=w.eps)
+    torch().cuda.synchronize()
+    ref = BC.block_causal_from_inputs(x["q"], x["k"], x["v"], 1, w.eps, "bf16")
+    assert_causal_close(decode(to_host(out, "bf16"), "bf16"), ref,
+                        f"token-causal B={B} N={N} H={H}")
 
 
 @pytest.mark.parametrize("i", range(COUNT))
