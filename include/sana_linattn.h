@@ -64,6 +64,11 @@
  * eps = 0 a query row with phi(q_i) = 0 gives 0/0 = NaN, otherwise such a row
  * gives exactly 0. Tensor pointers must be 16-byte aligned
  * (SANA_ERR_ALIGNMENT otherwise). Inputs must be finite.
+ *
+ * Language. The header is C99 as well as C++; from a C or C++ compiler other
+ * than hipcc, define __HIP_PLATFORM_AMD__ (as hipcc does) so that
+ * <hip/hip_runtime_api.h> declares hipStream_t and hipEvent_t, and link the
+ * library (it brings its HIP runtime dependency with it).
  */
 #ifndef SANA_LINATTN_H
 #define SANA_LINATTN_H

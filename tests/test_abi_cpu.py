@@ -444,3 +444,44 @@ def test_library_shares_torchs_hip_runtime():
     libs = eval(r.stdout.strip().splitlines()[-1])
     assert sum("libamdhip64" in p for p in libs) == 1, libs
     assert sum("hsa-runtime64" in p for p in libs) == 1, libs
+
+
+C_PROGRAM = r"""
+#include "sana_linattn.h"
+#include <stdio.h>
+int main(void) {
+  size_t n = 0;
+  sana_status_t s = sana_linattn_causal_workspace_size(1, 1, 2, 32, SANA_DTYPE_BF16, &n);
+  printf("%d %zu\n", (int)s, n);
+  s = sana_linattn_workspace_size(1, 16, 2, 64, SANA_DTYPE_BF16, &n);
+  printf("%d %s\n", (int)s, sana_linattn_strerror(s));
+  s = sana_linattn_fwd(NULL, NULL, NULL, NULL, 1, 16, 2, 32, 1e-6f, SANA_DTYPE_BF16, NULL, 0,
+                       NULL);
+  printf("%d\n", (int)s);
+  return sana_linattn_version() > 0 ? 0 : 1;
+}
+"""
+
+
+def test_header_is_c_and_library_links_from_c(tmp_path):
+    """The header compiles as C99 and a C program linked against the library
+    calls its host-side entry points (no GPU needed for these)."""
+    import shutil
+
+    from relu_linear_attention_attn_amd import binding
+
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists(binding.LIB_PATH):
+        pytest.skip("needs gcc and the built library")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(binding.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe), binding.LIB_PATH,
+                    f"-Wl,-rpath,{libdir}"], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    assert out[0] == f"{OK} {2 * 32 * 33 * 4}"             # one chunk state of one head pair
+    assert out[1].startswith(f"{UNSUPPORTED} ")            # d = 64
+    assert out[2] == f"{INVALID}"                          # null pointers, checked on the host
