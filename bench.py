@@ -481,7 +481,9 @@ def run_block_causal(args, w, causal: bool = False):
             R.forward_block_causal(d["q"], d["k"], d["v"], block, eps=w.eps, out=d["out"],
                                    workspace=ws, events=events)
 
-    names = ["states", "scan", "apply"] if causal else ["reduce", "scan", "apply"]
+    # bf16 blocks of 1, 2, 4, 8 or 16 tokens run on the token-causal kernels
+    chunked = causal or (w.dtype == "bf16" and block in (1, 2, 4, 8, 16))
+    names = ["states", "scan", "apply"] if chunked else ["reduce", "scan", "apply"]
     for i in range(args.warmup):
         step(i)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -497,7 +499,7 @@ def run_block_causal(args, w, causal: bool = False):
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
     step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
-    if causal:
+    if chunked:
         # states: read k, v, write the chunk states; apply: read q, k, v and
         # the chunk prefixes, write out (the workspace holds exactly the states)
         alg_bytes = {"states": 2 * elem + ws_bytes, "apply": 4 * elem + ws_bytes}
@@ -536,7 +538,7 @@ def run_block_causal(args, w, causal: bool = False):
                      "traffic": measured_traffic(dominant, w.name, op,
                                                  None if causal else block)},
     }
-    if causal:
+    if chunked:
         result["path_bytes_moved_per_step"] = sum(alg_bytes.values()) + 2 * ws_bytes
     if args.copy_mib == 0:
         ceil = copy_ceiling(ws.device)

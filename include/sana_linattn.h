@@ -355,13 +355,17 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
  * The Linear-DiT 4K blog, section "技术演进", names Block Causal Linear
  * Attention (SANA-Video) without a formula; this is its plainest reading.
  * block = N is sana_linattn_fwd's non-causal attention; block = 1 is
- * token-causal attention (correct but slow: the work is done per block).
- * N must be a multiple of block (SANA_ERR_INVALID_ARG otherwise). Tensors,
- * dtypes, eps, alignment and overlap rules as for sana_linattn_fwd;
- * workspace: at least sana_linattn_block_causal_workspace_size(...) bytes,
- * 256-byte aligned, contents irrelevant on entry. Three kernels: the state
- * reduction per block, an inclusive prefix sum over each batch item's blocks
- * (fixed order: results are bitwise repeatable), the apply.
+ * token-causal attention. N must be a multiple of block
+ * (SANA_ERR_INVALID_ARG otherwise). Tensors, dtypes, eps, alignment and
+ * overlap rules as for sana_linattn_fwd; workspace: at least
+ * sana_linattn_block_causal_workspace_size(...) bytes, 256-byte aligned,
+ * contents irrelevant on entry. Three kernels, in fixed order (results are
+ * bitwise repeatable): in general the state reduction per block, an
+ * inclusive prefix sum over each batch item's blocks, the apply; in bf16
+ * with blocks of 1, 2, 4, 8 or 16 tokens (which never straddle a 16-token
+ * tile) the token-causal kernels of sana_linattn_fwd_causal instead, with
+ * their in-tile mask widened to whole blocks (block = 1 gives bitwise the
+ * result of sana_linattn_fwd_causal).
  */
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,
                                                       int64_t d, int64_t block, sana_dtype_t dtype,
@@ -391,8 +395,8 @@ sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* 
  *
  * bf16 only (SANA_DTYPE_F32 returns SANA_ERR_UNSUPPORTED); same tensors,
  * layout, alignment, overlap and eps rules as sana_linattn_fwd. The result
- * equals sana_linattn_fwd_block_causal with block = 1 (up to rounding) at a
- * fraction of its cost. Three kernels: the states of chunks of consecutive
+ * equals sana_linattn_fwd_block_causal's with block = 1, bit for bit.
+ * Three kernels: the states of chunks of consecutive
  * tokens, their exclusive prefix over each head's chunks (fixed order:
  * results are bitwise repeatable), and the apply, which walks each chunk
  * tile by tile from its prefix. workspace: at least

@@ -527,10 +527,11 @@ struct QkvPlan {
 // Token-causal attention: chunks per unit so that every unit's chunks make
 // one round of kCausalWaves waves (the plan does not depend on the device).
 sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype, CausalPlan* cp,
-                          size_t* tensor_bytes) {
+                          size_t* tensor_bytes, int lg = 0) {
   sana_status_t s = check_shape(B, N, H, d, dtype, tensor_bytes);
   if (s != SANA_OK) return s;
   if (dtype != SANA_DTYPE_BF16) return SANA_ERR_UNSUPPORTED;
+  cp->lg = lg;
   cp->B = B;
   cp->N = N;
   cp->H = H;
@@ -554,10 +555,10 @@ sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
 sana_status_t causal_forward(const void* q, const void* k, const void* v, void* out, int64_t B,
                              int64_t N, int64_t H, int64_t d, float eps, int dtype,
                              void* workspace, size_t workspace_bytes, hipEvent_t* events,
-                             int n_events, hipStream_t stream) {
+                             int n_events, hipStream_t stream, int lg = 0) {
   CausalPlan cp;
   size_t tb = 0;
-  sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, &tb);
+  sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, &tb, lg);
   if (s != SANA_OK) return s;
   if (events) {
     if (n_events < 4) return SANA_ERR_INVALID_ARG;
@@ -584,6 +585,52 @@ sana_status_t causal_forward(const void* q, const void* k, const void* v, void* 
   if (!mark(2)) return SANA_ERR_HIP;
   if (launch_causal_apply(cp, q, k, v, out, parts, eps, stream) != hipSuccess) return SANA_ERR_HIP;
   return mark(3) ? SANA_OK : SANA_ERR_HIP;
+}
+
+// Blocks of 1, 2, 4, 8 or 16 tokens in bf16: every chunk and tile boundary of
+// the token-causal kernels is then a block boundary, so those kernels compute
+// block-causal attention exactly with their in-tile mask widened to whole
+// blocks, one state per chunk instead of one per block. Returns log2 of the
+// block length, or -1 for the per-block path.
+int small_block_lg(int64_t L, int dtype) {
+  if (dtype != SANA_DTYPE_BF16) return -1;
+  for (int lg = 0; lg <= 4; ++lg)
+    if (L == (int64_t(1) << lg)) return lg;
+  return -1;
+}
+
+sana_status_t block_causal_workspace(int64_t B, int64_t N, int64_t H, int64_t d, int64_t L,
+                                     int dtype, size_t* bytes) {
+  const int lg = small_block_lg(L, dtype);
+  if (lg >= 0) {
+    CausalPlan cp;
+    const sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, nullptr, lg);
+    if (s != SANA_OK) return s;
+    if (N % L != 0) return SANA_ERR_INVALID_ARG;
+    *bytes = cp.parts_bytes;
+    return SANA_OK;
+  }
+  BlockCausalPlan bc;
+  const sana_status_t s = plan_block_causal(B, N, H, d, L, dtype, &bc, nullptr);
+  if (s != SANA_OK) return s;
+  *bytes = bc.workspace_bytes;
+  return SANA_OK;
+}
+
+sana_status_t block_causal_any(const void* q, const void* k, const void* v, void* out, int64_t B,
+                               int64_t N, int64_t H, int64_t d, int64_t L, float eps, int dtype,
+                               void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                               int n_events, hipStream_t stream) {
+  const int lg = small_block_lg(L, dtype);
+  if (lg < 0)
+    return block_causal(q, k, v, out, B, N, H, d, L, eps, dtype, workspace, workspace_bytes,
+                        events, n_events, stream);
+  CausalPlan cp;
+  const sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, nullptr, lg);
+  if (s != SANA_OK) return s;
+  if (N % L != 0) return SANA_ERR_INVALID_ARG;
+  return causal_forward(q, k, v, out, B, N, H, d, eps, dtype, workspace, workspace_bytes, events,
+                        n_events, stream, lg);
 }
 
 sana_status_t plan_qkv(int64_t B, int64_t N, int64_t C, int64_t H, int64_t d, QkvPlan* qp) {
@@ -862,11 +909,7 @@ sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int
                                                       size_t* bytes) {
   if (!bytes) return SANA_ERR_INVALID_ARG;
   *bytes = 0;
-  sana::BlockCausalPlan bc;
-  const sana_status_t s = sana::plan_block_causal(B, N, H, d, block, dtype, &bc, nullptr);
-  if (s != SANA_OK) return s;
-  *bytes = bc.workspace_bytes;
-  return SANA_OK;
+  return sana::block_causal_workspace(B, N, H, d, block, dtype, bytes);
 }
 
 sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const void* v,
@@ -874,8 +917,8 @@ sana_status_t sana_linattn_fwd_block_causal(const void* q, const void* k, const 
                                             int64_t d, int64_t block, float eps, sana_dtype_t dtype,
                                             void* workspace, size_t workspace_bytes,
                                             hipStream_t stream) {
-  return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
-                            workspace_bytes, nullptr, 0, stream);
+  return sana::block_causal_any(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
+                                workspace_bytes, nullptr, 0, stream);
 }
 
 sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* k, const void* v,
@@ -885,8 +928,8 @@ sana_status_t sana_linattn_fwd_block_causal_profiled(const void* q, const void* 
                                                      size_t workspace_bytes, hipEvent_t* events,
                                                      int n_events, hipStream_t stream) {
   if (!events) return SANA_ERR_INVALID_ARG;
-  return sana::block_causal(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
-                            workspace_bytes, events, n_events, stream);
+  return sana::block_causal_any(q, k, v, out, B, N, H, d, block, eps, dtype, workspace,
+                                workspace_bytes, events, n_events, stream);
 }
 
 sana_status_t sana_linattn_causal_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d,

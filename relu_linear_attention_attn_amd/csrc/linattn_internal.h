@@ -124,6 +124,7 @@ constexpr int64_t kCausalWaves = 2048;      // 8 waves on each of 256 CUs
 constexpr int64_t kMaxCausalChunks = 1024;  // per unit
 struct CausalPlan {
   int64_t B, N, H, pairs, units, tiles, chunks, W;
+  int lg;              // blocks of 2^lg tokens (0: token-causal; at most 4)
   size_t parts_bytes;  // [units][chunks][2][d][d+1] fp32
 };
 hipError_t launch_causal_states(const CausalPlan& cp, const void* k, const void* v, float* parts,

@@ -1896,9 +1896,13 @@ __global__ __launch_bounds__(kCausalScanThreads) void causal_scan_kernel(
 // 16x16x32 result gave results that changed by an ulp from run to run: the
 // compiler left too few cycles between the two shapes, and the dependent
 // MFMA sometimes read the accumulator before the lo part of the state had
-// been added.)
+// been added.) With lg > 0 a key is masked only when its block of 2^lg
+// tokens comes after the query's (block-causal attention with blocks that
+// divide the tile; tiles start at multiples of 16 tokens, so tile-relative
+// block numbers compare like absolute ones).
 __device__ __forceinline__ u32x4 causal_head(const ApplyOperands& op, u32x4 qpiece,
-                                             u32x4 kpiece, s16x4 va0, s16x4 va1, float eps) {
+                                             u32x4 kpiece, s16x4 va0, s16x4 va1, float eps,
+                                             int lg) {
   const bf16x8 qv = __builtin_bit_cast(bf16x8, relu_bf16x8(qpiece));
   const bf16x8 kv = __builtin_bit_cast(bf16x8, relu_bf16x8(kpiece));
   f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.kv0_hi, qv, (f32x4)0, 0, 0, 0);
@@ -1913,7 +1917,7 @@ __device__ __forceinline__ u32x4 causal_head(const ApplyOperands& op, u32x4 qpie
   s16x8 ss;  // [hi of the 4 scores | lo of the 4 scores]
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float x = j0 + r <= i ? sc[r] : 0.0f;
+    const float x = (j0 + r) >> lg <= i >> lg ? sc[r] : 0.0f;
     const __bf16 h = (__bf16)x;
     ss[r] = __builtin_bit_cast(short, h);
     ss[4 + r] = __builtin_bit_cast(short, (__bf16)(x - (float)h));
@@ -2029,7 +2033,7 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
     const unsigned short* __restrict__ V, unsigned short* __restrict__ Out,
     const float* __restrict__ parts, float eps, int64_t N, int64_t H, int64_t pairs,
-    int64_t units, int64_t chunks, int64_t W) {
+    int64_t units, int64_t chunks, int64_t W, int lg) {
   __shared__ CausalWaveLds lds[S];
   const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const CausalWave cw = causal_wave(units, chunks, pairs, H, N, W, S);
@@ -2085,7 +2089,7 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
       const u32x4 qp = *reinterpret_cast<const u32x4*>(w.q + po);
       const u32x4 kp = *reinterpret_cast<const u32x4*>(w.k + po);
       res[hh] = causal_head(op, qp, kp, gather_v_keys4(w.v, hh, 0), gather_v_keys4(w.v, hh, 1),
-                            eps);
+                            eps, lg);
       __builtin_amdgcn_sched_barrier(0);
     }
     // P += this tile's state (keys past n_hi are zero)
@@ -2386,7 +2390,7 @@ hipError_t launch_causal_apply(const CausalPlan& cp, const void* q, const void* 
                      dim3(64 * kCausalS), 0, stream, static_cast<const unsigned short*>(q),
                      static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
                      static_cast<unsigned short*>(out), parts, eps, cp.N, cp.H, cp.pairs,
-                     cp.units, cp.chunks, cp.W);
+                     cp.units, cp.chunks, cp.W, cp.lg);
   return hipGetLastError();
 }
 

@@ -244,12 +244,20 @@ def test_block_causal_workspace_and_errors(L):
     assert bcws(L, 1, 1000, 2, 0) == (INVALID, 0)
     assert bcws(L, 1, 1000, 2, -8) == (INVALID, 0)
     assert bcws(L, 1, 1000, 2, 1000, d=16) == (UNSUPPORTED, 0)
-    # blocks as batch items: B * (N / L) * ceil(H/2) at most 2^22 head pairs
-    assert bcws(L, 1, 1 << 22, 2, 1)[0] == OK
-    assert bcws(L, 2, 1 << 22, 2, 1)[0] == INVALID
-    # the prefix scan runs 2304 work-items per (b, head pair): within 2^32
-    assert bcws(L, 1 << 20, 16, 2, 16)[0] == OK
-    assert bcws(L, 1 << 21, 16, 2, 16)[0] == INVALID
+    # per-block path (fp32, or block lengths other than 1, 2, 4, 8, 16): blocks
+    # as batch items, B * (N / L) * ceil(H/2) at most 2^22 head pairs
+    assert bcws(L, 1, 1 << 22, 2, 1, dt=F32)[0] == OK
+    assert bcws(L, 2, 1 << 22, 2, 1, dt=F32)[0] == INVALID
+    # and its prefix scan runs 2304 work-items per (b, head pair): within 2^32
+    assert bcws(L, 1 << 20, 16, 2, 16, dt=F32)[0] == OK
+    assert bcws(L, 1 << 21, 16, 2, 16, dt=F32)[0] == INVALID
+    # bf16 blocks of 1, 2, 4, 8 or 16 tokens run on the token-causal kernels:
+    # the token-causal workspace (chunk states), whatever the block count
+    for blk in (1, 2, 4, 8, 16):
+        assert bcws(L, 2, 16384, 70, blk) == cws(L, 2, 16384, 70)
+    assert bcws(L, 2, 1 << 22, 2, 1)[0] == OK
+    assert bcws(L, 1, 1000, 2, 16) == (INVALID, 0)                     # 1000 % 16 != 0
+    assert bcws(L, 1, 1024, 2, 32) != cws(L, 1, 1024, 2)               # 32: per block
     assert L.sana_linattn_block_causal_workspace_size(1, 16, 2, 32, 16, BF16, None) == INVALID
     need = bcws(L, 1, 64, 2, 16)[1]
     f = L.sana_linattn_fwd_block_causal

@@ -1,7 +1,11 @@
 """GPU parity of block-causal attention: the HIP path against the CPU
 float64 block-causal oracle, element by element, on the same seeded bits.
 Tolerances as for the forward pass: bf16 max-abs <= 1e-2 and rel-L2 <= 5e-3;
-fp32 rel-L2 <= 1e-5 and max-abs <= 1e-5 * max|ref|."""
+fp32 rel-L2 <= 1e-5 and max-abs <= 1e-5 * max|ref|. Blocks of at most 16
+tokens take the token-causal bound instead (per element 2^-8 |ref| + 2e-3,
+rel-L2 <= 5e-3): a query in an early block averages v over a few keys, so
+|out| reaches max |v| and the bf16 rounding of the output alone can exceed
+a flat 1e-2 there."""
 import numpy as np
 import pytest
 
@@ -33,10 +37,12 @@ def _run(w, dev, block):
     return to_host(out, w.dtype)
 
 
-CASES = [  # (B, N, H, block, dtype)
+CASES = [  # (B, N, H, block, dtype); bf16 blocks of 1..16 tokens take the token-causal kernels
     (2, 4096, 6, 1024, "bf16"), (2, 4096, 6, 1024, "f32"), (1, 16384, 36, 1024, "bf16"),
     (3, 5000, 7, 1000, "bf16"), (3, 5000, 7, 1000, "f32"), (2, 160, 3, 16, "bf16"),
     (1, 2048, 5, 2048, "bf16"), (1, 64, 2, 1, "bf16"), (1, 64, 2, 1, "f32"), (2, 96, 1, 32, "bf16"),
+    (2, 1000, 3, 2, "bf16"), (1, 4100, 5, 4, "bf16"), (2, 3000, 4, 8, "bf16"),
+    (1, 16384, 6, 16, "bf16"), (2, 100, 3, 4, "f32"),
 ]
 
 
@@ -48,7 +54,24 @@ def test_block_causal_matches_oracle(B, N, H, block, dtype):
     x, dev = _inputs(w)
     ref = BC.block_causal_from_inputs(x["q"], x["k"], x["v"], block, w.eps, dtype)
     got = decode(_run(w, dev, block), dtype)
-    assert_close(got, ref, dtype, f"B={B} N={N} H={H} block={block} {dtype}")
+    what = f"B={B} N={N} H={H} block={block} {dtype}"
+    if dtype == "bf16" and block <= 16:
+        from test_gpu_causal import assert_causal_close
+
+        assert_causal_close(got, ref, what)
+    else:
+        assert_close(got, ref, dtype, what)
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 64, 2), (2, 3000, 5), (2, 16384, 70)])
+def test_unit_blocks_are_the_token_causal_kernels(B, N, H):
+    """bf16 blocks of one token: bitwise the token-causal entry point's result."""
+    w = W.custom(f"bc1_{B}_{N}_{H}", B, N, H, seed=77 + N)
+    x, dev = _inputs(w)
+    a = _run(w, dev, 1)
+    b = R.forward_causal(dev["q"], dev["k"], dev["v"], eps=w.eps)
+    torch().cuda.synchronize()
+    assert np.array_equal(a, to_host(b, "bf16"))
 
 
 def test_one_block_matches_noncausal_forward():

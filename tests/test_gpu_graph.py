@@ -134,6 +134,8 @@ CASES = {
     "qkv_bf16": lambda: _qkv_case(1, 700, 200, 5),
     # token-causal: chunk states, their prefix scan, the chunk-wise apply
     "causal_bf16": lambda: _causal_case(2, 3000, 5),
+    # bf16 blocks of 4 tokens: the block-causal entry point on the token-causal kernels
+    "block_causal_bf16_small_blocks": lambda: _block_causal_case(1, 2048, 5, 4, BF16),
 }
 
 
