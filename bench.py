@@ -481,8 +481,10 @@ def run_block_causal(args, w, causal: bool = False):
             R.forward_block_causal(d["q"], d["k"], d["v"], block, eps=w.eps, out=d["out"],
                                    workspace=ws, events=events)
 
-    # bf16 blocks of 1, 2, 4, 8 or 16 tokens run on the token-causal kernels
-    chunked = causal or (w.dtype == "bf16" and block in (1, 2, 4, 8, 16))
+    # bf16 blocks of 1, 2, 4, 8 or 16 tokens, or of whole tiles up to 256
+    # tokens, run on the chunk-wise kernels (chunk states, scan, apply)
+    chunked = causal or (w.dtype == "bf16" and (block in (1, 2, 4, 8, 16)
+                                                  or (block % 16 == 0 and block <= 256)))
     names = ["states", "scan", "apply"] if chunked else ["reduce", "scan", "apply"]
     for i in range(args.warmup):
         step(i)

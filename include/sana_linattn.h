@@ -361,11 +361,14 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
  * sana_linattn_block_causal_workspace_size(...) bytes, 256-byte aligned,
  * contents irrelevant on entry. Three kernels, in fixed order (results are
  * bitwise repeatable): in general the state reduction per block, an
- * inclusive prefix sum over each batch item's blocks, the apply; in bf16
- * with blocks of 1, 2, 4, 8 or 16 tokens (which never straddle a 16-token
- * tile) the token-causal kernels of sana_linattn_fwd_causal instead, with
+ * inclusive prefix sum over each batch item's blocks, the apply. In bf16,
+ * short blocks run chunk-wise instead (one state per chunk of consecutive
+ * tokens, not per block): blocks of 1, 2, 4, 8 or 16 tokens (which never
+ * straddle a 16-token tile) on the kernels of sana_linattn_fwd_causal with
  * their in-tile mask widened to whole blocks (block = 1 gives bitwise the
- * result of sana_linattn_fwd_causal).
+ * result of sana_linattn_fwd_causal), and blocks of 32 to 256 tokens that
+ * are whole 16-token tiles on a block-wise apply over chunks of whole
+ * blocks (each block's states first, then its queries).
  */
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,
                                                       int64_t d, int64_t block, sana_dtype_t dtype,

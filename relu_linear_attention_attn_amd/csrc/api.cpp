@@ -527,11 +527,12 @@ struct QkvPlan {
 // Token-causal attention: chunks per unit so that every unit's chunks make
 // one round of kCausalWaves waves (the plan does not depend on the device).
 sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype, CausalPlan* cp,
-                          size_t* tensor_bytes, int lg = 0) {
+                          size_t* tensor_bytes, int lg = 0, int64_t m = 0) {
   sana_status_t s = check_shape(B, N, H, d, dtype, tensor_bytes);
   if (s != SANA_OK) return s;
   if (dtype != SANA_DTYPE_BF16) return SANA_ERR_UNSUPPORTED;
   cp->lg = lg;
+  cp->m = m;
   cp->B = B;
   cp->N = N;
   cp->H = H;
@@ -544,6 +545,7 @@ sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
   // of W and W + 1 tiles were 1 us slower than a short last chunk)
   const int64_t c = clamp64(kCausalWaves / cp->units, 1, std::min(cp->tiles, kMaxCausalChunks));
   cp->W = cdiv(cp->tiles, c);
+  if (m > 1) cp->W = cdiv(cp->W, m) * m;  // chunks of whole blocks
   cp->chunks = cdiv(cp->tiles, cp->W);
   cp->parts_bytes =
       align_up(static_cast<size_t>(cp->units) * static_cast<size_t>(cp->chunks) * 2 * kStateFloats * 4);
@@ -555,10 +557,10 @@ sana_status_t plan_causal(int64_t B, int64_t N, int64_t H, int64_t d, int dtype,
 sana_status_t causal_forward(const void* q, const void* k, const void* v, void* out, int64_t B,
                              int64_t N, int64_t H, int64_t d, float eps, int dtype,
                              void* workspace, size_t workspace_bytes, hipEvent_t* events,
-                             int n_events, hipStream_t stream, int lg = 0) {
+                             int n_events, hipStream_t stream, int lg = 0, int64_t m = 0) {
   CausalPlan cp;
   size_t tb = 0;
-  sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, &tb, lg);
+  sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, &tb, lg, m);
   if (s != SANA_OK) return s;
   if (events) {
     if (n_events < 4) return SANA_ERR_INVALID_ARG;
@@ -583,28 +585,45 @@ sana_status_t causal_forward(const void* q, const void* k, const void* v, void* 
   if (!mark(1)) return SANA_ERR_HIP;
   if (launch_causal_scan(cp, parts, stream) != hipSuccess) return SANA_ERR_HIP;
   if (!mark(2)) return SANA_ERR_HIP;
-  if (launch_causal_apply(cp, q, k, v, out, parts, eps, stream) != hipSuccess) return SANA_ERR_HIP;
+  const hipError_t e = cp.m > 1 ? launch_causal_block_apply(cp, q, k, v, out, parts, eps, stream)
+                                : launch_causal_apply(cp, q, k, v, out, parts, eps, stream);
+  if (e != hipSuccess) return SANA_ERR_HIP;
   return mark(3) ? SANA_OK : SANA_ERR_HIP;
 }
 
-// Blocks of 1, 2, 4, 8 or 16 tokens in bf16: every chunk and tile boundary of
-// the token-causal kernels is then a block boundary, so those kernels compute
-// block-causal attention exactly with their in-tile mask widened to whole
-// blocks, one state per chunk instead of one per block. Returns log2 of the
-// block length, or -1 for the per-block path.
-int small_block_lg(int64_t L, int dtype) {
-  if (dtype != SANA_DTYPE_BF16) return -1;
+// Block-causal attention on the chunk-wise kernels (bf16), one state per
+// chunk instead of one per block:
+//   * blocks of 1, 2, 4, 8 or 16 tokens never straddle a tile, so every chunk
+//     and tile boundary is a block boundary and the token-causal apply
+//     computes them with its in-tile mask widened to whole blocks (lg);
+//   * blocks of m = L / 16 whole tiles, chunks made of whole blocks: the
+//     block-wise apply (each block's states first, then its queries).
+// Longer blocks keep the per-block path, which is faster there: one state per
+// block costs little once blocks are long, while chunks of whole long blocks
+// leave too few waves (4096px latent, us per step, chunk-wise / per block:
+// L = 64 178 / 584, 256 190 / 208, 512 222 / 163, 1024 220 / 141).
+constexpr int64_t kMaxChunkedBlock = 256;  // tokens
+
+struct ChunkedBlocks {
+  bool on;
+  int lg;
+  int64_t m;
+};
+
+ChunkedBlocks chunked_blocks(int64_t L, int dtype) {
+  if (dtype != SANA_DTYPE_BF16) return {false, 0, 0};
   for (int lg = 0; lg <= 4; ++lg)
-    if (L == (int64_t(1) << lg)) return lg;
-  return -1;
+    if (L == (int64_t(1) << lg)) return {true, lg, 0};
+  if (L > kTile && L <= kMaxChunkedBlock && L % kTile == 0) return {true, 0, L / kTile};
+  return {false, 0, 0};
 }
 
 sana_status_t block_causal_workspace(int64_t B, int64_t N, int64_t H, int64_t d, int64_t L,
                                      int dtype, size_t* bytes) {
-  const int lg = small_block_lg(L, dtype);
-  if (lg >= 0) {
+  const ChunkedBlocks cb = chunked_blocks(L, dtype);
+  if (cb.on) {
     CausalPlan cp;
-    const sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, nullptr, lg);
+    const sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, nullptr, cb.lg, cb.m);
     if (s != SANA_OK) return s;
     if (N % L != 0) return SANA_ERR_INVALID_ARG;
     *bytes = cp.parts_bytes;
@@ -621,16 +640,16 @@ sana_status_t block_causal_any(const void* q, const void* k, const void* v, void
                                int64_t N, int64_t H, int64_t d, int64_t L, float eps, int dtype,
                                void* workspace, size_t workspace_bytes, hipEvent_t* events,
                                int n_events, hipStream_t stream) {
-  const int lg = small_block_lg(L, dtype);
-  if (lg < 0)
+  const ChunkedBlocks cb = chunked_blocks(L, dtype);
+  if (!cb.on)
     return block_causal(q, k, v, out, B, N, H, d, L, eps, dtype, workspace, workspace_bytes,
                         events, n_events, stream);
   CausalPlan cp;
-  const sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, nullptr, lg);
+  const sana_status_t s = plan_causal(B, N, H, d, dtype, &cp, nullptr, cb.lg, cb.m);
   if (s != SANA_OK) return s;
   if (N % L != 0) return SANA_ERR_INVALID_ARG;
   return causal_forward(q, k, v, out, B, N, H, d, eps, dtype, workspace, workspace_bytes, events,
-                        n_events, stream, lg);
+                        n_events, stream, cb.lg, cb.m);
 }
 
 sana_status_t plan_qkv(int64_t B, int64_t N, int64_t C, int64_t H, int64_t d, QkvPlan* qp) {

@@ -125,11 +125,15 @@ constexpr int64_t kMaxCausalChunks = 1024;  // per unit
 struct CausalPlan {
   int64_t B, N, H, pairs, units, tiles, chunks, W;
   int lg;              // blocks of 2^lg tokens (0: token-causal; at most 4)
+  int64_t m;           // > 1: blocks of m whole tiles (the block-wise apply); W a multiple
   size_t parts_bytes;  // [units][chunks][2][d][d+1] fp32
 };
 hipError_t launch_causal_states(const CausalPlan& cp, const void* k, const void* v, float* parts,
                                 hipStream_t stream);
 hipError_t launch_causal_scan(const CausalPlan& cp, float* parts, hipStream_t stream);
+hipError_t launch_causal_block_apply(const CausalPlan& cp, const void* q, const void* k,
+                                     const void* v, void* out, const float* parts, float eps,
+                                     hipStream_t stream);
 hipError_t launch_causal_apply(const CausalPlan& cp, const void* q, const void* k, const void* v,
                                void* out, const float* parts, float eps, hipStream_t stream);
 hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* partials,

@@ -2139,6 +2139,130 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
     if (i0 + u < tiles) step(i0 + u, qb[u], kb[u], vb[u]);
 }
 
+// Block-causal attention with blocks of m >= 2 whole tiles, chunk-wise (the
+// chunks are whole blocks). From its prefix P a wave walks its chunk block by
+// block: first the block's k, v tiles add their states to P, then every
+// query of the block reads P, which now covers exactly its own block and
+// every earlier one (out = phi(q) P, the apply's arithmetic): two passes per
+// block, each tensor read once, no masks. The next tile's loads (k and v in
+// the first pass, q in the second, the first pass of the next block after
+// the last q tile) are in flight while a tile is worked on.
+template <int S>
+__global__ __launch_bounds__(64 * S) void causal_block_apply_kernel(
+    const unsigned short* __restrict__ Q, const unsigned short* __restrict__ K,
+    const unsigned short* __restrict__ V, unsigned short* __restrict__ Out,
+    const float* __restrict__ parts, float eps, int64_t N, int64_t H, int64_t pairs,
+    int64_t units, int64_t chunks, int64_t W, int64_t m) {
+  __shared__ CausalWaveLds lds[S];
+  const int sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const CausalWave cw = causal_wave(units, chunks, pairs, H, N, W, S);
+  if (!cw.valid) return;  // the whole wave; no block barrier below
+  CausalWaveLds& w = lds[sub];
+  const int64_t row = H * kD;
+  const int64_t base = (cw.b * N * H + cw.h) * kD;
+  const int l = lane_id();
+  const int t0 = l >> 3, j = l & 7;
+  const int jl = cw.two ? j : (j & 3);
+  const int g = l >> 4, col = l & 15;
+  const int64_t n_lo = cw.n_lo;
+  // whole blocks: N is a multiple of 16 m and chunks end on block boundaries
+  const int64_t blocks = (cw.n_hi - n_lo) / (m * kTile);
+
+  f32x16 acc[2];
+  float ks[2];
+  load_acc_state(parts + (cw.unit * chunks + cw.chunk) * 2 * kSF, acc, ks);
+
+  u32x4 qb[2], kb[2], vb[2];
+  auto offset = [&](int64_t tile, int h2) {
+    return base + (n_lo + tile * kTile + t0 + 8 * h2) * row + 8 * jl;
+  };
+  auto issue_kv = [&](int64_t tile) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      kb[h2] = ld16_stream(K + offset(tile, h2));
+      vb[h2] = ld16_stream(V + offset(tile, h2));
+    }
+  };
+  auto issue_q = [&](int64_t tile) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) qb[h2] = ld16_stream(Q + offset(tile, h2));
+  };
+  issue_kv(0);
+  for (int64_t b = 0; b < blocks; ++b) {
+    const int64_t first = b * m;
+    // pass 1: P += the block's k, v tiles
+    for (int64_t t = 0; t < m; ++t) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int o = tile_off(t0 + 8 * h2, j);
+        *reinterpret_cast<u32x4*>(w.k + o) = kb[h2];
+        *reinterpret_cast<u32x4*>(w.v + o) = vb[h2];
+      }
+      wave_lds_order();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < m) {
+        issue_kv(first + t + 1);
+      } else {
+        issue_q(first);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const s16x8 a = gather_tokens8(w.k, hh);
+        const s16x8 bv = gather_tokens8(w.v, hh);
+        const s16x8 pk = __builtin_elementwise_max(a, (s16x8)0);
+        acc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pk),
+                                                          __builtin_bit_cast(bf16x8, bv),
+                                                          acc[hh], 0, 0, 0);
+        const u32x4 wk = __builtin_bit_cast(u32x4, pk);
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum += __builtin_bit_cast(float, wk[e] << 16);
+          sum += __builtin_bit_cast(float, wk[e] & 0xFFFF0000u);
+        }
+        ks[hh] += sum;
+      }
+      wave_lds_order();
+    }
+    // P now covers the whole block: the apply's operands, once per block
+    store_acc_ops(w.ops, acc, ks);
+    wave_lds_order();
+    const ApplyOperands op0 = load_acc_ops(w.ops, 0);
+    const ApplyOperands op1 = load_acc_ops(w.ops, 1);
+    // pass 2: the block's queries
+    for (int64_t t = 0; t < m; ++t) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        *reinterpret_cast<u32x4*>(w.q + tile_off(t0 + 8 * h2, j)) = qb[h2];
+      wave_lds_order();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < m) {
+        issue_q(first + t + 1);
+      } else if (b + 1 < blocks) {
+        issue_kv(first + m);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 q0 = *reinterpret_cast<const u32x4*>(w.q + tile_off(col, g));
+      const u32x4 q1 = *reinterpret_cast<const u32x4*>(w.q + tile_off(col, 4 + g));
+      const u32x4 r0 = apply_head(op0, q0, eps);
+      const u32x4 r1 = apply_head(op1, q1, eps);
+      wave_lds_order();
+      *reinterpret_cast<u32x4*>(w.q + tile_off(col, g)) = r0;
+      *reinterpret_cast<u32x4*>(w.q + tile_off(col, 4 + g)) = r1;
+      wave_lds_order();
+      const u32x4 o0 = *reinterpret_cast<const u32x4*>(w.q + tile_off(t0, j));
+      const u32x4 o1 = *reinterpret_cast<const u32x4*>(w.q + tile_off(t0 + 8, j));
+      wave_lds_order();
+      if (cw.two || j < 4) {
+        const int64_t n = n_lo + (first + t) * kTile + t0;
+        st16_stream(Out + base + n * row + 8 * j, o0);
+        st16_stream(Out + base + (n + 8) * row + 8 * j, o1);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------ block-causal scan
 //
 // Block-causal attention runs the forward kernels on a plan whose batch
@@ -2391,6 +2515,18 @@ hipError_t launch_causal_apply(const CausalPlan& cp, const void* q, const void* 
                      static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
                      static_cast<unsigned short*>(out), parts, eps, cp.N, cp.H, cp.pairs,
                      cp.units, cp.chunks, cp.W, cp.lg);
+  return hipGetLastError();
+}
+
+hipError_t launch_causal_block_apply(const CausalPlan& cp, const void* q, const void* k,
+                                     const void* v, void* out, const float* parts, float eps,
+                                     hipStream_t stream) {
+  const int64_t blocks = (cp.units * cp.chunks + kCausalS - 1) / kCausalS;
+  hipLaunchKernelGGL((causal_block_apply_kernel<kCausalS>), dim3((unsigned)blocks),
+                     dim3(64 * kCausalS), 0, stream, static_cast<const unsigned short*>(q),
+                     static_cast<const unsigned short*>(k), static_cast<const unsigned short*>(v),
+                     static_cast<unsigned short*>(out), parts, eps, cp.N, cp.H, cp.pairs,
+                     cp.units, cp.chunks, cp.W, cp.m);
   return hipGetLastError();
 }
 

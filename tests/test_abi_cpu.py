@@ -257,7 +257,11 @@ def test_block_causal_workspace_and_errors(L):
         assert bcws(L, 2, 16384, 70, blk) == cws(L, 2, 16384, 70)
     assert bcws(L, 2, 1 << 22, 2, 1)[0] == OK
     assert bcws(L, 1, 1000, 2, 16) == (INVALID, 0)                     # 1000 % 16 != 0
-    assert bcws(L, 1, 1024, 2, 32) != cws(L, 1, 1024, 2)               # 32: per block
+    # bf16 blocks of 2..16 whole tiles: chunks of whole blocks (here 64 tiles
+    # in chunks of 2 for blocks of 32 tokens), longer blocks one state each
+    assert bcws(L, 1, 1024, 2, 32) == (OK, 32 * 2 * 32 * 33 * 4)
+    assert bcws(L, 1, 1024, 2, 48) == (INVALID, 0)                     # 1024 % 48 != 0
+    assert bcws(L, 1, 4096, 2, 512)[1] != cws(L, 1, 4096, 2)[1]        # per block
     assert L.sana_linattn_block_causal_workspace_size(1, 16, 2, 32, 16, BF16, None) == INVALID
     need = bcws(L, 1, 64, 2, 16)[1]
     f = L.sana_linattn_fwd_block_causal

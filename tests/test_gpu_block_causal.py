@@ -37,12 +37,16 @@ def _run(w, dev, block):
     return to_host(out, w.dtype)
 
 
-CASES = [  # (B, N, H, block, dtype); bf16 blocks of 1..16 tokens take the token-causal kernels
+CASES = [  # (B, N, H, block, dtype); bf16 blocks up to 256 tokens take the chunk-wise kernels
     (2, 4096, 6, 1024, "bf16"), (2, 4096, 6, 1024, "f32"), (1, 16384, 36, 1024, "bf16"),
     (3, 5000, 7, 1000, "bf16"), (3, 5000, 7, 1000, "f32"), (2, 160, 3, 16, "bf16"),
     (1, 2048, 5, 2048, "bf16"), (1, 64, 2, 1, "bf16"), (1, 64, 2, 1, "f32"), (2, 96, 1, 32, "bf16"),
     (2, 1000, 3, 2, "bf16"), (1, 4100, 5, 4, "bf16"), (2, 3000, 4, 8, "bf16"),
     (1, 16384, 6, 16, "bf16"), (2, 100, 3, 4, "f32"),
+    # bf16 blocks of 2..16 whole tiles: the block-wise chunked apply (512: per block)
+    (2, 4096, 6, 32, "bf16"), (1, 4800, 5, 48, "bf16"), (2, 16384, 8, 64, "bf16"),
+    (1, 8192, 3, 256, "bf16"), (2, 5120, 5, 512, "bf16"), (3, 64, 7, 32, "bf16"),
+    (2, 4096, 6, 64, "f32"),
 ]
 
 

@@ -136,6 +136,8 @@ CASES = {
     "causal_bf16": lambda: _causal_case(2, 3000, 5),
     # bf16 blocks of 4 tokens: the block-causal entry point on the token-causal kernels
     "block_causal_bf16_small_blocks": lambda: _block_causal_case(1, 2048, 5, 4, BF16),
+    # bf16 blocks of 4 tiles: the block-wise chunked apply
+    "block_causal_bf16_tile_blocks": lambda: _block_causal_case(2, 2048, 5, 64, BF16),
 }
 
 
