@@ -120,6 +120,9 @@ hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, 
 // Token-causal attention (bf16): chunk states, their exclusive prefix,
 // then the causal apply. One wave per (unit, chunk of W consecutive tiles);
 // W chosen so the units' chunks make one round of about kCausalWaves waves.
+// The same plan serves block-causal attention with short bf16 blocks: blocks
+// of 2^lg <= 16 tokens on the causal apply, blocks of m whole tiles on the
+// block-wise apply (W then a multiple of m).
 constexpr int64_t kCausalWaves = 2048;      // 8 waves on each of 256 CUs
 constexpr int64_t kMaxCausalChunks = 1024;  // per unit
 struct CausalPlan {

@@ -1776,18 +1776,22 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
 //
 // Token-causal attention (query i attends to keys 0..i of its batch item),
 // computed chunk-wise: an exclusive prefix of chunk states plus, inside a
-// chunk, the running state and the causal terms of each 16-token tile.
-// Every wave owns one (unit, chunk) of W consecutive tiles (the last chunk
-// may be shorter); waves are
-// numbered unit-major (wave = unit * chunks + chunk), so the 8 waves of a
-// block mostly stream consecutive chunks of one head pair (measured 1-2 us
-// faster per kernel on the 4096px latent than 8 head pairs at one chunk).
+// chunk, the running state and the causal terms of each 16-token tile; and
+// block-causal attention with short blocks the same way. Every wave owns
+// one (unit, chunk) of W consecutive tiles (the last chunk may be shorter);
+// waves are numbered unit-major (wave = unit * chunks + chunk), so the 8
+// waves of a block mostly stream consecutive chunks of one head pair
+// (measured 1-2 us faster per kernel on the 4096px latent than 8 head pairs
+// at one chunk).
 //   causal_states_kernel: S_c = phi(K_c)^T [V_c | 1] per chunk, from the
 //     wave's registers to parts[unit][chunk] ([2][d][d+1], both heads);
 //   causal_scan_kernel: parts[unit][c] <- sum of parts[unit][0 .. c-1];
 //   causal_apply_kernel: from that prefix P, tile by tile:
 //     out_i = phi(q_i) (P + sum_{j <= i in the tile} phi(k_j)^T [v_j | 1])
-//     split into numerator and normaliser, then P += the tile's state.
+//     split into numerator and normaliser, then P += the tile's state
+//     (with blocks of 2^lg <= 16 tokens, j runs over the query's block);
+//   causal_block_apply_kernel: blocks of whole tiles, block by block (see
+//     there).
 
 struct CausalWave {
   int64_t unit, chunk, b, h, n_lo, n_hi;
