@@ -497,3 +497,38 @@ def test_header_is_c_and_library_links_from_c(tmp_path):
     assert out[0] == f"{OK} {2 * 32 * 33 * 4}"             # one chunk state of one head pair
     assert out[1].startswith(f"{UNSUPPORTED} ")            # d = 64
     assert out[2] == f"{INVALID}"                          # null pointers, checked on the host
+
+
+def test_workspace_sizes_never_misreport(L):
+    """Property test over random and extreme shapes (negative, zero, near the
+    int64 limits): every size query returns a documented status, leaves 0 on
+    error, and on success a 256-byte multiple below 2^62."""
+    hyp = pytest.importorskip("hypothesis")
+    st = hyp.strategies
+
+    dims = st.one_of(st.integers(-3, 70000), st.sampled_from([0, 1, 2, 15, 16, 17, 32, 33, 64]),
+                     st.integers(1 << 20, 1 << 40), st.integers(-(1 << 63), (1 << 63) - 1))
+    calls = {
+        "fwd": lambda B, N, H, d, dt, x, s: L.sana_linattn_workspace_size(B, N, H, d, dt, s),
+        "bwd": lambda B, N, H, d, dt, x, s: L.sana_linattn_bwd_workspace_size(B, N, H, d, dt, s),
+        "block_causal": lambda B, N, H, d, dt, x, s: L.sana_linattn_block_causal_workspace_size(
+            B, N, H, d, x, dt, s),
+        "causal": lambda B, N, H, d, dt, x, s: L.sana_linattn_causal_workspace_size(
+            B, N, H, d, dt, s),
+        "qkv": lambda B, N, H, d, dt, x, s: L.sana_linattn_qkv_workspace_size(B, N, x, H, d, s),
+    }
+
+    @hyp.settings(max_examples=400, deadline=None, derandomize=True)
+    @hyp.given(name=st.sampled_from(sorted(calls)), B=dims, N=dims, H=dims,
+               d=st.sampled_from([32, 32, 32, 16, 64, 0, -32]), dt=st.sampled_from([0, 1, 2, -1]),
+               x=dims)
+    def check(name, B, N, H, d, dt, x):
+        n = ctypes.c_size_t(12345)
+        status = calls[name](B, N, H, d, dt, x, ctypes.byref(n))
+        assert status in (OK, INVALID, UNSUPPORTED), (name, status)
+        if status != OK:
+            assert n.value == 0, (name, status, n.value)
+        else:
+            assert n.value % 256 == 0 and 0 < n.value < (1 << 62), (name, n.value)
+
+    check()
