@@ -1967,58 +1967,54 @@ __device__ __forceinline__ s16x4 gather_v_keys4(const unsigned char* vtile, int 
 // multiple of 16, and 20 banks apart, so the 32 lanes that write one
 // 8-byte piece each to 32 rows meet at most two to a bank.
 constexpr int kOpPitch = 40;
-struct alignas(16) CausalOpsLds {
-  unsigned short hi[2][kD * kOpPitch];  // [head][output channel][input channel]
-  unsigned short lo[2][kD * kOpPitch];
-  unsigned short ks_hi[2][kD];          // [head][input channel]
-  unsigned short ks_lo[2][kD];
+struct alignas(16) CausalOpsLds {  // one head at a time
+  unsigned short hi[kD * kOpPitch];  // [output channel][input channel]
+  unsigned short lo[kD * kOpPitch];
+  unsigned short ks_hi[kD];          // [input channel]
+  unsigned short ks_lo[kD];
 };
 
-// P from the 32x32 MFMA accumulator layout (lane l holds column l % 32, rows
-// 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive input channels per
-// quarter of acc) into ops; called by the whole wave.
-__device__ __forceinline__ void store_acc_ops(CausalOpsLds& o, const f32x16 (&acc)[2],
-                                              const float (&ks)[2]) {
+// Head hh of P from the 32x32 MFMA accumulator layout (lane l holds column
+// l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive input
+// channels per quarter of acc) into ops; called by the whole wave.
+__device__ __forceinline__ void store_acc_ops(CausalOpsLds& o, const f32x16& acc, float ks) {
   const int l = lane_id();
   const int col = l & 31;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
+  for (int q = 0; q < 4; ++q) {
+    unsigned int h[2], w[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      unsigned int h[2], w[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float x0 = acc[hh][4 * q + 2 * e], x1 = acc[hh][4 * q + 2 * e + 1];
-        h[e] = cvt_pk_bf16(x0, x1);
-        w[e] = cvt_pk_bf16(x0 - __builtin_bit_cast(float, h[e] << 16),
-                           x1 - __builtin_bit_cast(float, h[e] & 0xFFFF0000u));
-      }
-      const int at = col * kOpPitch + 8 * q + 4 * (l >> 5);
-      *reinterpret_cast<u32x2*>(o.hi[hh] + at) = (u32x2){h[0], h[1]};
-      *reinterpret_cast<u32x2*>(o.lo[hh] + at) = (u32x2){w[0], w[1]};
+    for (int e = 0; e < 2; ++e) {
+      const float x0 = acc[4 * q + 2 * e], x1 = acc[4 * q + 2 * e + 1];
+      h[e] = cvt_pk_bf16(x0, x1);
+      w[e] = cvt_pk_bf16(x0 - __builtin_bit_cast(float, h[e] << 16),
+                         x1 - __builtin_bit_cast(float, h[e] & 0xFFFF0000u));
     }
-    const float kq = ks[hh] + __shfl_xor(ks[hh], 32);
-    if (l < 32) {
-      const __bf16 kh = (__bf16)kq;
-      o.ks_hi[hh][l] = __builtin_bit_cast(unsigned short, kh);
-      o.ks_lo[hh][l] = __builtin_bit_cast(unsigned short, (__bf16)(kq - (float)kh));
-    }
+    const int at = col * kOpPitch + 8 * q + 4 * (l >> 5);
+    *reinterpret_cast<u32x2*>(o.hi + at) = (u32x2){h[0], h[1]};
+    *reinterpret_cast<u32x2*>(o.lo + at) = (u32x2){w[0], w[1]};
+  }
+  const float kq = ks + __shfl_xor(ks, 32);
+  if (l < 32) {
+    const __bf16 kh = (__bf16)kq;
+    o.ks_hi[l] = __builtin_bit_cast(unsigned short, kh);
+    o.ks_lo[l] = __builtin_bit_cast(unsigned short, (__bf16)(kq - (float)kh));
   }
 }
 
-// The apply's six A operands of head hh (make_apply_operands's layout).
-__device__ __forceinline__ ApplyOperands load_acc_ops(const CausalOpsLds& o, int hh) {
+// The apply's six A operands of the head in ops (make_apply_operands's layout).
+__device__ __forceinline__ ApplyOperands load_acc_ops(const CausalOpsLds& o) {
   const int l = lane_id();
   const int g = l >> 4, i = l & 15;
   const int c0 = 8 * (i >> 2) + (i & 3);  // output channel of row i in tile 0
   const int a0 = c0 * kOpPitch + 8 * g, a1 = (c0 + 4) * kOpPitch + 8 * g;
   ApplyOperands op;
-  op.kv0_hi = *reinterpret_cast<const bf16x8*>(o.hi[hh] + a0);
-  op.kv0_lo = *reinterpret_cast<const bf16x8*>(o.lo[hh] + a0);
-  op.kv1_hi = *reinterpret_cast<const bf16x8*>(o.hi[hh] + a1);
-  op.kv1_lo = *reinterpret_cast<const bf16x8*>(o.lo[hh] + a1);
-  op.ks_hi = *reinterpret_cast<const bf16x8*>(o.ks_hi[hh] + 8 * g);
-  op.ks_lo = *reinterpret_cast<const bf16x8*>(o.ks_lo[hh] + 8 * g);
+  op.kv0_hi = *reinterpret_cast<const bf16x8*>(o.hi + a0);
+  op.kv0_lo = *reinterpret_cast<const bf16x8*>(o.lo + a0);
+  op.kv1_hi = *reinterpret_cast<const bf16x8*>(o.hi + a1);
+  op.kv1_lo = *reinterpret_cast<const bf16x8*>(o.lo + a1);
+  op.ks_hi = *reinterpret_cast<const bf16x8*>(o.ks_hi + 8 * g);
+  op.ks_lo = *reinterpret_cast<const bf16x8*>(o.ks_lo + 8 * g);
   return op;
 }
 
@@ -2080,7 +2076,6 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
       *reinterpret_cast<u32x4*>(w.k + o) = n0 + t0 + 8 * h2 < n_hi ? kd[h2] : (u32x4)0;
       *reinterpret_cast<u32x4*>(w.v + o) = vd[h2];
     }
-    store_acc_ops(w.ops, acc, ks);  // P: every token before this tile
     wave_lds_order();
     __builtin_amdgcn_sched_barrier(0);
     issue(i + U, qd, kd, vd);
@@ -2088,7 +2083,10 @@ __global__ __launch_bounds__(64 * S) void causal_apply_kernel(
     u32x4 res[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const ApplyOperands op = load_acc_ops(w.ops, hh);
+      store_acc_ops(w.ops, acc[hh], ks[hh]);  // P: every token before this tile
+      wave_lds_order();
+      const ApplyOperands op = load_acc_ops(w.ops);
+      wave_lds_order();  // the next head's store waits for these reads
       const int po = tile_off(col, hh * 4 + g);
       const u32x4 qp = *reinterpret_cast<const u32x4*>(w.q + po);
       const u32x4 kp = *reinterpret_cast<const u32x4*>(w.k + po);
@@ -2230,10 +2228,13 @@ __global__ __launch_bounds__(64 * S) void causal_block_apply_kernel(
       wave_lds_order();
     }
     // P now covers the whole block: the apply's operands, once per block
-    store_acc_ops(w.ops, acc, ks);
+    store_acc_ops(w.ops, acc[0], ks[0]);
     wave_lds_order();
-    const ApplyOperands op0 = load_acc_ops(w.ops, 0);
-    const ApplyOperands op1 = load_acc_ops(w.ops, 1);
+    const ApplyOperands op0 = load_acc_ops(w.ops);
+    wave_lds_order();
+    store_acc_ops(w.ops, acc[1], ks[1]);
+    wave_lds_order();
+    const ApplyOperands op1 = load_acc_ops(w.ops);
     // pass 2: the block's queries
     for (int64_t t = 0; t < m; ++t) {
 #pragma unroll
