@@ -168,7 +168,7 @@ def test_causal_video_1m_tokens_sampled_rows():
     """One sequence of 1,048,576 tokens, 36 heads: rows from the start, tile
     and chunk edges, the middle and the end of three heads, each row from
     the oracle's definition (the prefix states of every token would take
-    8.6 GB per head)."""
+    8.6 GB per head), and two heads over the first 65,536 tokens in full."""
     w = W.WORKLOADS["video_1m_tokens"]
     print(f"\n[case] causal {w.name} {w.shape}", flush=True)
     x, dev = _inputs(w)
@@ -180,6 +180,14 @@ def test_causal_video_1m_tokens_sampled_rows():
         dec = {t: decode(x[t][0, :, h], "bf16") for t in "qkv"}
         ref = BC.token_causal_rows(dec["q"], dec["k"], dec["v"], rows, w.eps)
         assert_causal_close(decode(got[0, rows, h], "bf16"), ref, f"video head {h}")
+    # outputs of the first 65,536 tokens depend on those tokens only: two
+    # heads in full there, across the first seven chunk boundaries
+    T = 1 << 16
+    for h in (0, 35):
+        sub = {t: x[t][:, :T, h:h + 1] for t in "qkv"}
+        ref = BC.block_causal_from_inputs(sub["q"], sub["k"], sub["v"], 1, w.eps, "bf16")
+        assert_causal_close(decode(got[:, :T, h:h + 1], "bf16"), ref,
+                            f"video head {h}, first {T} tokens in full")
 
 
 def test_causal_workspace_garbage_guards_and_reuse():
