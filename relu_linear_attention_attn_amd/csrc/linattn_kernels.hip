@@ -2315,7 +2315,15 @@ constexpr int kAppS = 8, kAppU = 2;
 // than 16 (measured on the 2 x 16384 x 70 forward: apply 61 -> 55 us), as
 // fewer concurrent streams contend for HBM rows.
 constexpr unsigned kApplyLdsPad = 64 << 10;
+// Fused bf16 blocks: 8 waves with two tiles in flight each, or, where the
+// grid has at least two head-pair units per CU, 4 waves with one tile in
+// flight (fewer bytes in flight per CU, as for the apply). Measured, us (256
+// CUs; N x H with B batch items, units = B x ceil(H / 2)): 16 x 1024 x 70
+// (560 units) 57.8 -> 56.4, 16 x 1024 x 64 (512) 55.2 -> 52.1, 16 x 512 x 70
+// (560) 31.1 -> 29.2, 32 x 256 x 70 (1120) 30.6 / 30.7; below two units per
+// CU the narrow blocks lose: 280 units 36.1 -> 36.7, 256 units 28.5 -> 33.3.
 constexpr int kFusS = 8, kFusU = 2;
+constexpr int kFusNarrowS = 4, kFusNarrowU = 1;
 constexpr int kBwqS = 8, kBwqU = 1;
 constexpr int kBwkvS = 8, kBwkvU = 1;
 // XCDs of MI355X (the round-robin width of block dispatch). Fewer units than
@@ -2551,11 +2559,13 @@ int64_t scan_grid_threads(int64_t B, int64_t pairs) {
   return B * pairs * kScanBlocksPerPair * kScanThreads;
 }
 
-hipError_t launch_fused(const Plan& p, int dtype, const void* q, const void* k, const void* v,
-                        void* out, float eps, hipStream_t stream) {
+hipError_t launch_fused(const Plan& p, int dtype, bool narrow, const void* q, const void* k,
+                        const void* v, void* out, float eps, hipStream_t stream) {
   const dim3 grid((unsigned)p.units);
   if (dtype == 1) {
-    hipLaunchKernelGGL((fused_bf16_kernel<kFusS, kFusU>), grid, dim3(64 * kFusS), 0, stream,
+    auto* kernel = narrow ? fused_bf16_kernel<kFusNarrowS, kFusNarrowU>
+                          : fused_bf16_kernel<kFusS, kFusU>;
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * (narrow ? kFusNarrowS : kFusS)), 0, stream,
                        static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                        static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out),
                        eps, p.N, p.H, p.pairs);
