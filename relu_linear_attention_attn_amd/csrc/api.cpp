@@ -429,8 +429,7 @@ sana_status_t forward(const void* q, const void* k, const void* v, void* out, in
   if (!mark(0)) return SANA_ERR_HIP;
   const WorkspaceParts w = split_workspace(fp, workspace);
   if (run == SANA_VARIANT_FUSED) {
-    const bool narrow = fp.units >= 2 * static_cast<int64_t>(device_caps().cus);
-    if (launch_fused(fp, dtype, narrow, q, k, v, out, eps, stream) != hipSuccess)
+    if (launch_fused(fp, dtype, device_caps().cus, q, k, v, out, eps, stream) != hipSuccess)
       return SANA_ERR_HIP;
     return mark(1) ? SANA_OK : SANA_ERR_HIP;
   }

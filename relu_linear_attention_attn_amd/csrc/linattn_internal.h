@@ -142,9 +142,9 @@ hipError_t launch_causal_apply(const CausalPlan& cp, const void* q, const void* 
 hipError_t launch_scan_blocks(const Plan& p, int dtype, int64_t F, const float* partials,
                               const float* state, float* prefix, hipStream_t stream);
 int64_t scan_grid_threads(int64_t B, int64_t pairs);  // work-items of that launch
-// narrow: bf16 blocks of 4 waves with one tile in flight each, for grids of
-// at least two head-pair units per CU; else 8 waves with two tiles in flight.
-hipError_t launch_fused(const Plan& p, int dtype, bool narrow, const void* q, const void* k,
+// cus: the device's CU count, which picks the bf16 block shape (waves per
+// block and tiles in flight per wave) from the head-pair units per CU.
+hipError_t launch_fused(const Plan& p, int dtype, int64_t cus, const void* q, const void* k,
                         const void* v, void* out, float eps, hipStream_t stream);
 
 }  // namespace sana

@@ -2322,14 +2322,18 @@ constexpr int app_u() { return Fm == kFmapRelu ? kAppU : kAppFmapU; }
 // than 16 (measured on the 2 x 16384 x 70 forward: apply 61 -> 55 us), as
 // fewer concurrent streams contend for HBM rows.
 constexpr unsigned kApplyLdsPad = 64 << 10;
-// Fused bf16 blocks: 8 waves with two tiles in flight each, or, where the
-// grid has at least two head-pair units per CU, 4 waves with one tile in
-// flight (fewer bytes in flight per CU, as for the apply). Measured, us (256
-// CUs; N x H with B batch items, units = B x ceil(H / 2)): 16 x 1024 x 70
-// (560 units) 57.8 -> 56.4, 16 x 1024 x 64 (512) 55.2 -> 52.1, 16 x 512 x 70
-// (560) 31.1 -> 29.2, 32 x 256 x 70 (1120) 30.6 / 30.7; below two units per
-// CU the narrow blocks lose: 280 units 36.1 -> 36.7, 256 units 28.5 -> 33.3.
+// Fused bf16 block shapes by head-pair units per CU (fewer bytes in flight
+// per CU as more blocks share it, as for the apply): below one unit per CU,
+// 8 waves with two tiles in flight each; from one, 8 waves with one tile;
+// from two, 4 waves with one tile. Measured, us (256 CUs; B x N x H, units =
+// B x ceil(H / 2); shape 8.2 / 8.1 / 4.1): 4 x 1024 x 70 (140 units)
+// 18.3 / 20.4 / -; 8 x 1024 x 64 (256) 28.5 / 27.2 / 33.3; 8 x 1024 x 70
+// (280) 36.3 / 34.0 / 36.7; 8 x 512 x 70 (280) 19.9 / 18.6 / 20.7;
+// 16 x 1024 x 64 (512) 55.2 / - / 52.1; 16 x 1024 x 70 (560) 57.8 / 61.3 /
+// 56.4; 16 x 512 x 70 (560) 31.1 / - / 29.2; 32 x 256 x 70 (1120) 30.6 / - /
+// 30.7.
 constexpr int kFusS = 8, kFusU = 2;
+constexpr int kFusMidS = 8, kFusMidU = 1;
 constexpr int kFusNarrowS = 4, kFusNarrowU = 1;
 constexpr int kBwqS = 8, kBwqU = 1;
 constexpr int kBwkvS = 8, kBwkvU = 1;
@@ -2566,13 +2570,16 @@ int64_t scan_grid_threads(int64_t B, int64_t pairs) {
   return B * pairs * kScanBlocksPerPair * kScanThreads;
 }
 
-hipError_t launch_fused(const Plan& p, int dtype, bool narrow, const void* q, const void* k,
+hipError_t launch_fused(const Plan& p, int dtype, int64_t cus, const void* q, const void* k,
                         const void* v, void* out, float eps, hipStream_t stream) {
   const dim3 grid((unsigned)p.units);
   if (dtype == 1) {
-    auto* kernel = narrow ? fused_bf16_kernel<kFusNarrowS, kFusNarrowU>
-                          : fused_bf16_kernel<kFusS, kFusU>;
-    hipLaunchKernelGGL(kernel, grid, dim3(64 * (narrow ? kFusNarrowS : kFusS)), 0, stream,
+    const int per_cu = p.units >= 2 * cus ? 2 : p.units >= cus ? 1 : 0;
+    auto* kernel = per_cu == 2   ? fused_bf16_kernel<kFusNarrowS, kFusNarrowU>
+                   : per_cu == 1 ? fused_bf16_kernel<kFusMidS, kFusMidU>
+                                 : fused_bf16_kernel<kFusS, kFusU>;
+    const int waves = per_cu == 2 ? kFusNarrowS : per_cu == 1 ? kFusMidS : kFusS;
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * waves), 0, stream,
                        static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
                        static_cast<const unsigned short*>(v), static_cast<unsigned short*>(out),
                        eps, p.N, p.H, p.pairs);

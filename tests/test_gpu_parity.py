@@ -99,19 +99,21 @@ def test_ragged_shapes(B, N, H, dtype):
 # ------------------------------------- fused kernel at two units per CU
 
 
-@pytest.mark.parametrize("B,N,H", [(16, 1000, 65), (32, 77, 33), (40, 300, 27), (16, 1024, 64)])
-def test_narrow_fused_blocks(B, N, H):
-    """At two or more head-pair units per CU (512 on MI355X's 256 CUs) the
-    fused kernel runs 4-wave blocks with one tile in flight: ragged token
-    counts, odd head counts (a one-head last pair) and a unit count of
-    exactly 512 against the oracle, and repeat calls bit for bit."""
-    w = W.custom(f"narrow_{B}_{N}_{H}", B, N, H, seed=300 + N + H,
+@pytest.mark.parametrize("B,N,H", [(16, 1000, 65), (32, 77, 33), (40, 300, 27), (16, 1024, 64),
+                                   (8, 1000, 65), (9, 300, 57), (8, 1024, 64), (4, 1024, 70)])
+def test_fused_block_shapes(B, N, H):
+    """The fused kernel's block shape follows the head-pair units per CU
+    (MI355X: 256 CUs): 4-wave blocks with one tile in flight from 512 units,
+    8-wave blocks with one tile from 256, with two below. Ragged token counts,
+    odd head counts (a one-head last pair) and unit counts of exactly 512 and
+    256 against the oracle, and repeat calls bit for bit."""
+    w = W.custom(f"fused_{B}_{N}_{H}", B, N, H, seed=300 + N + H,
                  q=W.Dist("normal", 0.1, 1.0), k=W.Dist("normal", 0.1, 1.0))
-    print(f"\n[case] narrow fused B={B} N={N} H={H}", flush=True)
+    print(f"\n[case] fused block shape B={B} N={N} H={H}", flush=True)
     x, dev = _inputs(w)
     ref = _oracle(w, x)
     first = _run(w, dev, R.VARIANT_FUSED)
-    assert_close(first, ref, "bf16", f"narrow fused B={B} N={N} H={H}")
+    assert_close(first, ref, "bf16", f"fused B={B} N={N} H={H}")
     assert np.array_equal(first, _run(w, dev, R.VARIANT_FUSED)), "repeat differs"
     assert_close(_run(w, dev, R.VARIANT_AUTO), ref, "bf16", f"AUTO B={B} N={N} H={H}")
 
