@@ -63,7 +63,8 @@ def parse():
                          "(default workload: the 16-frame video, one block per frame), "
                          "token-causal forward, or QKV projection + forward")
     ap.add_argument("--fmap", default="relu", choices=["relu", "elu1", "cos"],
-                    help="feature map of the forward (other than relu: the split kernels)")
+                    help="feature map of the forward, or with --op bwd of the backward (other "
+                         "than relu: the split kernels)")
     ap.add_argument("--dtype", default=None, choices=["bf16", "f32"],
                     help="forward: run the workload's shape and recipe in this dtype "
                          "(default: the workload's own)")
@@ -334,15 +335,21 @@ def cpu_baseline(w, inputs, budget_s: float, fmap: str = "relu"):
     return timed_oracle(w, budget_s, decode, compute, f"forward ({fmap})")
 
 
-def cpu_baseline_bwd(w, inputs, budget_s: float):
-    """The backward oracle (oracle/linattn_bwd.py) on whole heads."""
+def cpu_baseline_bwd(w, inputs, budget_s: float, fmap: str = "relu"):
+    """The backward oracle (oracle/linattn_bwd.py, or for other feature maps
+    oracle/linattn_bwd_fmap.py) on whole heads."""
     import oracle.linattn as L
     import oracle.linattn_bwd as LB
+    import oracle.linattn_bwd_fmap as LBF
 
     def decode(b, h):
         return tuple(L.to_f64(inputs[t][b, :, h, :], w.dtype) for t in "qkvg")
 
-    return timed_oracle(w, budget_s, decode, lambda a: LB.backward_head(*a, w.eps), "backward")
+    if fmap == "relu":
+        return timed_oracle(w, budget_s, decode, lambda a: LB.backward_head(*a, w.eps),
+                            "backward")
+    return timed_oracle(w, budget_s, decode,
+                        lambda a: LBF.backward_head_fmap(*a, w.eps, fmap), f"backward ({fmap})")
 
 
 def run_bwd(args, w):
@@ -365,7 +372,7 @@ def run_bwd(args, w):
     def step(i, events=None):
         d = sets[i % n_sets]
         R.backward(d["q"], d["k"], d["v"], d["g"], eps=w.eps, grads=(d["dq"], d["dk"], d["dv"]),
-                   workspace=ws, events=events)
+                   workspace=ws, events=events, fmap=args.fmap)
 
     names = ["reduce", "bwd_q", "bwd_kv"]
     log(args, f"warmup {args.warmup} steps ({len(names)} kernels per step, {n_sets} input sets)")
@@ -404,7 +411,7 @@ def run_bwd(args, w):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "op": "bwd", "B": w.B, "N": w.N, "H": w.H, "d": w.d,
-                   "D": w.D, "eps": w.eps, "input_sets": n_sets},
+                   "D": w.D, "fmap": args.fmap, "eps": w.eps, "input_sets": n_sets},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": total_bytes,
@@ -414,7 +421,8 @@ def run_bwd(args, w):
         "step_ms_events": {"median": step_ms[len(step_ms) // 2], "min": step_ms[0]},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(dominant, w.name, "bwd")},
+                     "traffic": (measured_traffic(dominant, w.name, "bwd")
+                                 if args.fmap == "relu" else None)},
     }
     if args.copy_mib == 0:
         ceil = copy_ceiling(ws.device)
@@ -427,7 +435,7 @@ def run_bwd(args, w):
         torch.cuda.synchronize()
     if args.cpu_seconds > 0:
         log(args, f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline_bwd(w, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_bwd(w, x, args.cpu_seconds, args.fmap)
     print(json.dumps(result), flush=True)
 
 

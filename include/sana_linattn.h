@@ -344,6 +344,33 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
                                         hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
+ * The backward pass of sana_linattn_fwd_fmap (bf16 only): the gradients of
+ * sana_linattn_bwd with feature map `fmap` (sana_fmap_t) in place of ReLU,
+ * the map's derivative in place of the mask [x > 0]:
+ *
+ *     dq_i = (KV dnum_i + ksum dden_i) * phi'(q_i)
+ *     dk_n = (dKV v_n + dksum) * phi'(k_n),   dv_n = phi(k_n) dKV
+ *
+ * with KV, ksum, dnum, dden, dKV and dksum as there, from phi of this map.
+ * phi'(x): ELU + 1, 1 for x > 0 and exp(x) otherwise; cos, -sin(x); ReLU, as
+ * sana_linattn_bwd (SANA_FMAP_RELU computes exactly what sana_linattn_bwd
+ * computes). No page writes these gradients out: the chain rule through the
+ * course notes' kernel-function form ("Linear Attention 的原理") with the
+ * blog's normaliser ("核心架构"). In bf16, phi and phi' of ELU + 1 and cos
+ * are evaluated in fp32 and phi is split into bf16 hi + lo parts for the
+ * MFMAs. Tensors, workspace (sana_linattn_bwd_workspace_size), checks and
+ * errors as sana_linattn_bwd; an fmap outside sana_fmap_t returns
+ * SANA_ERR_UNSUPPORTED. events may be NULL; otherwise as for
+ * sana_linattn_bwd_profiled (n_events >= 4).
+ */
+sana_status_t sana_linattn_bwd_fmap(const void* q, const void* k, const void* v,
+                                    const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                                    int64_t N, int64_t H, int64_t d, float eps,
+                                    sana_dtype_t dtype, sana_fmap_t fmap, void* workspace,
+                                    size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                    hipStream_t stream);
+
+/*
  * Block-causal forward pass. The N tokens of each batch item form N / block
  * consecutive blocks of `block` tokens (a video frame is such a block); a
  * query in block c attends to every key in blocks 0..c - its own block

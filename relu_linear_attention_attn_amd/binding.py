@@ -41,6 +41,7 @@ EXPORTS = (
     "sana_linattn_bwd_workspace_size",
     "sana_linattn_bwd",
     "sana_linattn_bwd_profiled",
+    "sana_linattn_bwd_fmap",
     "sana_linattn_block_causal_workspace_size",
     "sana_linattn_fwd_block_causal",
     "sana_linattn_fwd_block_causal_profiled",
@@ -116,6 +117,9 @@ def lib() -> ctypes.CDLL:
                                                                 _vp, _sz, _vp]
         L.sana_linattn_bwd_profiled.argtypes = [_vp] * 7 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+        L.sana_linattn_bwd_fmap.argtypes = [_vp] * 7 + [_i64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
+            ctypes.c_int, _vp]
         L.sana_linattn_block_causal_workspace_size.argtypes = [_i64] * 5 + [
             ctypes.c_int, ctypes.POINTER(_sz)]
         L.sana_linattn_fwd_block_causal.argtypes = [_vp] * 4 + [_i64] * 5 + [
@@ -138,7 +142,7 @@ def lib() -> ctypes.CDLL:
         for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
                      "sana_linattn_fwd_block_causal_profiled", "sana_linattn_causal_workspace_size",
                      "sana_linattn_fwd_causal", "sana_linattn_fwd_fmap",
-                     "sana_linattn_fwd_strided",
+                     "sana_linattn_bwd_fmap", "sana_linattn_fwd_strided",
                      "sana_linattn_qkv_workspace_size", "sana_linattn_qkv_fwd"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
@@ -357,13 +361,17 @@ def bwd_workspace_size(B: int, N: int, H: int, d: int = HEAD_DIM, dtype: int = D
 
 
 def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grads=None,
-             workspace=None, events=None):
+             workspace=None, events=None, fmap: str = "relu"):
     """(dq, dk, dv) of the forward pass for the upstream gradient dout (bf16).
 
     q, k, v, dout: contiguous bf16 GPU tensors of one shape. grads: optional
     preallocated (dq, dk, dv). events: optional list of 4 torch.cuda.Event
     (enable_timing=True) recorded before the first and after each of the
-    three kernels. Enqueued on torch's current stream; no synchronisation."""
+    three kernels. fmap: the forward's feature map ("relu", "elu1", "cos";
+    anything but "relu" calls sana_linattn_bwd_fmap). Enqueued on torch's
+    current stream; no synchronisation."""
+    if fmap not in FMAPS:
+        raise ValueError(f"unknown feature map {fmap!r}; one of {sorted(FMAPS)}")
     torch = _torch()
     B, N, H, d = _shape(q, heads)
     _check_tensor(q, "q")
@@ -380,7 +388,12 @@ def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grad
                                 device=q.device)
     wb = workspace.numel() * workspace.element_size()
     ptrs = [t.data_ptr() for t in (q, k, v, dout, *grads)]
-    if events is None:
+    if fmap != "relu":
+        arr, n = _event_array(events)
+        _check(lib().sana_linattn_bwd_fmap(*ptrs, B, N, H, d, float(eps), dt, FMAPS[fmap],
+                                           workspace.data_ptr(), wb, arr, n, _stream(q)),
+               "sana_linattn_bwd_fmap")
+    elif events is None:
         _check(lib().sana_linattn_bwd(*ptrs, B, N, H, d, float(eps), dt, workspace.data_ptr(),
                                       wb, _stream(q)), "sana_linattn_bwd")
     else:

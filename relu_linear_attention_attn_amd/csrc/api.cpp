@@ -731,11 +731,11 @@ sana_status_t qkv_forward(const void* x, const void* w, void* q, void* out, int6
 sana_status_t backward(const void* q, const void* k, const void* v, const void* g, void* dq,
                        void* dk, void* dv, int64_t B, int64_t N, int64_t H, int64_t d, float eps,
                        int dtype, void* workspace, size_t workspace_bytes, hipEvent_t* events,
-                       int n_events, hipStream_t stream) {
+                       int n_events, hipStream_t stream, int fmap = SANA_FMAP_RELU) {
   size_t tb = 0;
   sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
   if (s != SANA_OK) return s;
-  if (dtype != SANA_DTYPE_BF16) return SANA_ERR_UNSUPPORTED;
+  if (dtype != SANA_DTYPE_BF16 || !valid_fmap(fmap)) return SANA_ERR_UNSUPPORTED;
   if (events) {
     if (n_events < kBwdKernels + 1) return SANA_ERR_INVALID_ARG;
     for (int i = 0; i <= kBwdKernels; ++i)
@@ -776,13 +776,15 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
   float* grad_parts =
       reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.bf16_partial_bytes);
   if (!mark(0)) return SANA_ERR_HIP;
-  if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream) != hipSuccess)
+  if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream, fmap) !=
+      hipSuccess)
     return SANA_ERR_HIP;
   if (!mark(1)) return SANA_ERR_HIP;
-  if (launch_bwd_q(fp, q, g, dq, fwd_parts, grad_parts, eps, stream) != hipSuccess)
+  if (launch_bwd_q(fp, q, g, dq, fwd_parts, grad_parts, eps, stream, fmap) != hipSuccess)
     return SANA_ERR_HIP;
   if (!mark(2)) return SANA_ERR_HIP;
-  if (launch_bwd_kv(fp, k, v, dk, dv, grad_parts, stream) != hipSuccess) return SANA_ERR_HIP;
+  if (launch_bwd_kv(fp, k, v, dk, dv, grad_parts, stream, fmap) != hipSuccess)
+    return SANA_ERR_HIP;
   return mark(3) ? SANA_OK : SANA_ERR_HIP;
 }
 
@@ -922,6 +924,16 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
   if (!events) return SANA_ERR_INVALID_ARG;
   return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
                         workspace_bytes, events, n_events, stream);
+}
+
+sana_status_t sana_linattn_bwd_fmap(const void* q, const void* k, const void* v,
+                                    const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                                    int64_t N, int64_t H, int64_t d, float eps,
+                                    sana_dtype_t dtype, sana_fmap_t fmap, void* workspace,
+                                    size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                    hipStream_t stream) {
+  return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
+                        workspace_bytes, events, n_events, stream, fmap);
 }
 
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,

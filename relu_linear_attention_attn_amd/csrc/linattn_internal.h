@@ -108,10 +108,12 @@ hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partia
 // partials of launch_reduce(fold = false) for the state (slots by
 // red_rule), writes dq and writes [dS | dz] partials in the same slots (same
 // rule); bwd_kv sums those and writes dk and dv.
+// fmap: the feature map (sana_fmap_t values) whose backward the passes take
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
-                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream);
+                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream,
+                        int fmap);
 hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
-                         const float* grad_parts, hipStream_t stream);
+                         const float* grad_parts, hipStream_t stream, int fmap);
 // Block-causal attention: p's batch items are the F blocks of each of the
 // p.B / F original batch items. Inclusive prefix sums over the blocks of the
 // reduction's result (bf16: its partials, launch_reduce(fold = false);

@@ -164,6 +164,27 @@ __device__ __forceinline__ float fmap_hw(float x) {
   if (Fm == kFmapCos) return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(x * kInv2Pi));
   return fmaxf(x, 0.0f);
 }
+// phi(x), as fmap_hw gives it, and phi'(x) from the same instructions, for
+// the backward pass: ELU + 1 has 1 above 0 and exp(x) at or below it
+// (continuous at 0; that exp(x) is phi there too), cos has -sin(x) (v_sin_f32
+// of the same fraction of revolutions); ReLU's is taken as 0 at 0.
+template <int Fm>
+__device__ __forceinline__ void fmap_dfmap_hw(float x, float& phi, float& dphi) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kInv2Pi = 0.15915494309189535f;
+  if (Fm == kFmapElu1) {
+    const float e = __builtin_amdgcn_exp2f(x * kLog2e);
+    phi = x > 0.0f ? x + 1.0f : e;
+    dphi = x > 0.0f ? 1.0f : e;
+  } else if (Fm == kFmapCos) {
+    const float r = __builtin_amdgcn_fractf(x * kInv2Pi);
+    phi = __builtin_amdgcn_cosf(r);
+    dphi = -__builtin_amdgcn_sinf(r);
+  } else {
+    phi = fmaxf(x, 0.0f);
+    dphi = x > 0.0f ? 1.0f : 0.0f;
+  }
+}
 
 // -------------------------------------------------- line tiles in LDS
 //
@@ -1397,7 +1418,7 @@ struct alignas(16) BwdQWaveLds {
 // (gathered from the g tile) and phi(q) / den split into bf16 hi + lo.
 // Padded tokens (n >= n_hi) read row n_lo, are zeroed in the q tile and get
 // 1 / den = dden = 0, so they add nothing even where eps = 0.
-template <int U, class MakeOps>
+template <int U, int Fm, class MakeOps>
 __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restrict__ Q,
                                                  const unsigned short* __restrict__ G,
                                                  unsigned short* __restrict__ dQ,
@@ -1453,9 +1474,17 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       const int po = tile_off(col, hh * 4 + g);
       const u32x4 qraw = *reinterpret_cast<const u32x4*>(w.q + po);
       const u32x4 graw = *reinterpret_cast<const u32x4*>(w.g + po);
-      float pq[8], u[8];
+      float pq[8], u[8], dph[8];
       const u32x4 rq = relu_bf16x8(qraw);
-      widen_bf16x8(rq, pq);
+      if (Fm == kFmapRelu) {
+        widen_bf16x8(rq, pq);
+      } else {
+        // phi(q) and phi'(q) in fp32 (a padded token's zeroed q gives
+        // finite values, and its 1 / den and dden of 0 keep it out)
+        widen_bf16x8(qraw, pq);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) fmap_dfmap_hw<Fm>(pq[m], pq[m], dph[m]);
+      }
       row_product<false>(ro[hh], __builtin_bit_cast(bf16x8, graw), (bf16x8)0, u);  // u = S g
       float dp = 0.0f, p = 0.0f;
 #pragma unroll
@@ -1469,10 +1498,12 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       // dq for the lane's channels: S dnum + z dden = u / den + z dden, then the ReLU gate
       u32x4 dqw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dqw[e] = relu_gate_pk(cvt_pk_bf16(u[2 * e] * rinv + ro[hh].last[2 * e] * dden,
-                                          u[2 * e + 1] * rinv + ro[hh].last[2 * e + 1] * dden),
-                              rq[e]);
+      for (int e = 0; e < 4; ++e) {
+        const float d0 = u[2 * e] * rinv + ro[hh].last[2 * e] * dden;
+        const float d1 = u[2 * e + 1] * rinv + ro[hh].last[2 * e + 1] * dden;
+        dqw[e] = Fm == kFmapRelu ? relu_gate_pk(cvt_pk_bf16(d0, d1), rq[e])
+                                 : cvt_pk_bf16(d0 * dph[2 * e], d1 * dph[2 * e + 1]);
+      }
       const bf16x8 dq = __builtin_bit_cast(bf16x8, dqw);
       // the token reduction: 1 / den and dden rows to LDS, the operands
       // gathered transposed (k = the lane's 8 tokens, channel l%32)
@@ -1489,7 +1520,13 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
       const f32x4 dd1 = *reinterpret_cast<const f32x4*>(w.dd + rt + 4);
       wave_lds_order();
       float pf[8], sc[8];
-      widen_bf16x8(relu_bf16x8(__builtin_bit_cast(u32x4, a)), pf);
+      if (Fm == kFmapRelu) {
+        widen_bf16x8(relu_bf16x8(__builtin_bit_cast(u32x4, a)), pf);
+      } else {
+        widen_bf16x8(__builtin_bit_cast(u32x4, a), pf);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) pf[s] = fmap_hw<Fm>(pf[s]);
+      }
       float zs = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -1559,7 +1596,7 @@ __device__ __forceinline__ void grad_q_pair_wave(const unsigned short* __restric
 // [n_lo, n_hi): dk = ([dS | dz] [v | 1]^T) * [k > 0] and dv = phi(k) dS.
 // slot holds the wave's k tile and v tile. Padded tokens are computed from
 // row n_lo and never stored.
-template <int U, class MakeOps>
+template <int U, int Fm, class MakeOps>
 __device__ __forceinline__ void grad_kv_pair_wave(const unsigned short* __restrict__ K,
                                                   const unsigned short* __restrict__ V,
                                                   unsigned short* __restrict__ dK,
@@ -1606,16 +1643,31 @@ __device__ __forceinline__ void grad_kv_pair_wave(const unsigned short* __restri
       const int po = tile_off(col, hh * 4 + g);
       const u32x4 kraw = *reinterpret_cast<const u32x4*>(slot + po);
       const u32x4 vraw = *reinterpret_cast<const u32x4*>(slot + kTileBytes + po);
-      float y[8], x[8];
+      float y[8], x[8], dph[8];
       const u32x4 rk = relu_bf16x8(kraw);
       row_product<false>(ro[hh], __builtin_bit_cast(bf16x8, vraw), (bf16x8)0, y);
-      col_product(ao[hh], __builtin_bit_cast(bf16x8, rk), x);
+      if (Fm == kFmapRelu) {
+        col_product(ao[hh], __builtin_bit_cast(bf16x8, rk), x);
+      } else {
+        // phi(k) in fp32, split into bf16 hi + lo: dv = hi dS + lo dS
+        float pk[8], x2[8];
+        widen_bf16x8(kraw, pk);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) fmap_dfmap_hw<Fm>(pk[m], pk[m], dph[m]);
+        bf16x8 hi, lo;
+        split_bf16x8(pk, hi, lo);
+        col_product(ao[hh], hi, x);
+        col_product(ao[hh], lo, x2);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) x[m] += x2[m];
+      }
       u32x4 dk, dv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dk[e] = relu_gate_pk(cvt_pk_bf16(y[2 * e] + ro[hh].last[2 * e],
-                                         y[2 * e + 1] + ro[hh].last[2 * e + 1]),
-                             rk[e]);
+        const float d0 = y[2 * e] + ro[hh].last[2 * e];
+        const float d1 = y[2 * e + 1] + ro[hh].last[2 * e + 1];
+        dk[e] = Fm == kFmapRelu ? relu_gate_pk(cvt_pk_bf16(d0, d1), rk[e])
+                                : cvt_pk_bf16(d0 * dph[2 * e], d1 * dph[2 * e + 1]);
         dv[e] = cvt_pk_bf16(x[2 * e], x[2 * e + 1]);
       }
       *reinterpret_cast<u32x4*>(slot + po) = dk;
@@ -1703,7 +1755,7 @@ struct StateOps {
 // and the block writes its [dS | dz] partial of each unit it touches to
 // grad_parts in the reduction's slot (the chunk, or g - first), so the
 // partials follow the same slot rule.
-template <int S, int U>
+template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ G,
     unsigned short* __restrict__ dQ, const float* __restrict__ fwd_parts,
@@ -1738,7 +1790,7 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
                        slot_count(unit, T, Qf), sg.two, stage};
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
-    grad_q_pair_wave<U>(Q, G, dQ, ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
+    grad_q_pair_wave<U, Fm>(Q, G, dQ, ops, eps, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo,
                         sg.n_hi, sub, S, sg.two, lds.wave[sub], acc, ks);
     block_sum_state<S, false>(acc, ks, lds.xchg, sub,
                               grad_parts + (unit * slots + slot) * 2 * kSF, sg.two);
@@ -1750,7 +1802,7 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
 // a unit's [dS | dz] is the sum of bwd_q's partials (slots of grid Qr).
 // (Balanced ranges of the flattened index, as in the reduction, measured
 // slower: a block that straddles two units pays the state prologue twice.)
-template <int S, int U>
+template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
     unsigned short* __restrict__ dK, unsigned short* __restrict__ dV,
@@ -1768,7 +1820,7 @@ __global__ __launch_bounds__(64 * S) void bwd_kv_bf16_kernel(
   const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
   const StateOps ops{reinterpret_cast<const f32x4*>(grad_parts + unit * slots * 2 * kSF),
                      slot_count(unit, T, Qr), sg.two, stage};
-  grad_kv_pair_wave<U>(K, V, dK, dV, ops, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi,
+  grad_kv_pair_wave<U, Fm>(K, V, dK, dV, ops, H * kD, (sg.b * N * H + sg.h) * kD, sg.n_lo, sg.n_hi,
                        sub, S, sg.two, tiles[sub]);
 }
 
@@ -2484,31 +2536,38 @@ hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partial
 }
 
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
-                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream) {
+                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream,
+                        int fmap) {
   // the reduction's grid: (unit, chunk) items when the plan has them, else
   // balanced ranges; the [dS | dz] partials then follow the same slot rule
   const bool chunked = p.red_cb > 0;
   const int64_t X = apply_xcds(p);
   const int64_t blocks = chunked ? xcd_grid(p.units * p.red_cb, X) : p.red_blocks;
-  hipLaunchKernelGGL((bwd_q_bf16_kernel<kBwqS, kBwqU>), dim3((unsigned)blocks), dim3(64 * kBwqS),
-                     0, stream, static_cast<const unsigned short*>(q),
-                     static_cast<const unsigned short*>(g), static_cast<unsigned short*>(dq),
-                     fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles,
-                     chunked ? p.red_cq : p.red_q, p.units * p.tiles, p.slots, red_rule(p),
-                     chunked ? p.red_cb : int64_t(0), X);
-  return hipGetLastError();
+  return with_fmap(fmap, [&](auto fm) {
+    constexpr int Fm = decltype(fm)::value;
+    hipLaunchKernelGGL((bwd_q_bf16_kernel<kBwqS, kBwqU, Fm>), dim3((unsigned)blocks),
+                       dim3(64 * kBwqS), 0, stream, static_cast<const unsigned short*>(q),
+                       static_cast<const unsigned short*>(g), static_cast<unsigned short*>(dq),
+                       fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles,
+                       chunked ? p.red_cq : p.red_q, p.units * p.tiles, p.slots, red_rule(p),
+                       chunked ? p.red_cb : int64_t(0), X);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
-                         const float* grad_parts, hipStream_t stream) {
+                         const float* grad_parts, hipStream_t stream, int fmap) {
   const int64_t X = apply_xcds(p);
-  hipLaunchKernelGGL((bwd_kv_bf16_kernel<kBwkvS, kBwkvU>),
-                     dim3((unsigned)xcd_grid(p.units * p.bkv_chunks, X)),
-                     dim3(64 * kBwkvS), 0, stream, static_cast<const unsigned short*>(k),
-                     static_cast<const unsigned short*>(v), static_cast<unsigned short*>(dk),
-                     static_cast<unsigned short*>(dv), grad_parts, p.N, p.H, p.pairs, p.units,
-                     p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, red_rule(p), p.slots);
-  return hipGetLastError();
+  return with_fmap(fmap, [&](auto fm) {
+    constexpr int Fm = decltype(fm)::value;
+    hipLaunchKernelGGL((bwd_kv_bf16_kernel<kBwkvS, kBwkvU, Fm>),
+                       dim3((unsigned)xcd_grid(p.units * p.bkv_chunks, X)),
+                       dim3(64 * kBwkvS), 0, stream, static_cast<const unsigned short*>(k),
+                       static_cast<const unsigned short*>(v), static_cast<unsigned short*>(dk),
+                       static_cast<unsigned short*>(dv), grad_parts, p.N, p.H, p.pairs, p.units,
+                       p.tiles, p.bkv_chunks, p.bkv_chunk / kTile, X, red_rule(p), p.slots);
+    return hipGetLastError();
+  });
 }
 
 constexpr int kCausalS = 8;  // waves per block of the causal kernels (independent waves)

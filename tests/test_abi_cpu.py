@@ -230,6 +230,33 @@ def test_bwd_rejects_invalid_arguments(L):
                                        BF16, P_W, 1 << 30, None, 4, None) == INVALID
 
 
+def bwd_fmap(L, fmap=1, q=P_Q, k=P_K, v=P_V, g=P_G, dq=P_DQ, dk=P_DK, dv=P_DV, B=1, N=64, H=2,
+             d=32, eps=1e-6, dt=BF16, ws=P_W, wsb=1 << 30, events=None, n_events=0):
+    return L.sana_linattn_bwd_fmap(q, k, v, g, dq, dk, dv, B, N, H, d, eps, dt, fmap, ws, wsb,
+                                   events, n_events, None)
+
+
+def test_bwd_fmap_rejects_invalid_arguments(L):
+    """The feature-map backward runs sana_linattn_bwd's checks, plus the map."""
+    for fmap in (0, 1, 2):
+        assert bwd_fmap(L, fmap, B=0) == INVALID
+        assert bwd_fmap(L, fmap, d=16) == UNSUPPORTED
+        assert bwd_fmap(L, fmap, dt=F32) == UNSUPPORTED
+        assert bwd_fmap(L, fmap, dq=P_Q + 4096) == INVALID
+        assert bwd_fmap(L, fmap, ws=None) == WORKSPACE
+    for fmap in (-1, 3, 1 << 20):
+        assert bwd_fmap(L, fmap) == UNSUPPORTED
+    for name in ("q", "k", "v", "g", "dq", "dk", "dv"):
+        assert bwd_fmap(L, **{name: None}) == INVALID, name
+        assert bwd_fmap(L, **{name: A * 11 + 8}) == ALIGNMENT, name
+    for eps in (-1.0, math.nan, math.inf):
+        assert bwd_fmap(L, eps=eps) == INVALID
+    need = bws(L, 1, 64, 2)[1]
+    assert bwd_fmap(L, wsb=need - 1) == WORKSPACE
+    events = (ctypes.c_void_p * 3)(None, None, None)
+    assert bwd_fmap(L, events=events, n_events=3) == INVALID
+
+
 def bcws(L, B, N, H, blk, d=32, dt=BF16):
     n = ctypes.c_size_t(123)
     st = L.sana_linattn_block_causal_workspace_size(B, N, H, d, blk, dt, ctypes.byref(n))
