@@ -2,7 +2,7 @@
 oracles: the forward (each variant and dtype), the strided forward on a
 packed projection output with a random row padding, the other feature maps,
 block-causal attention with a random block length, token-causal attention,
-the backward, and the QKV projection path. The shapes are drawn from a fixed seed, with token
+the backward (ReLU, ELU + 1, cos), and the QKV projection path. The shapes are drawn from a fixed seed, with token
 counts near the kernels' boundaries (multiples of the 16-token tile, the
 256-token projection tile, the fused variant's 1024-token limit) more often
 than elsewhere, and small enough for the oracle to finish in seconds.
@@ -168,6 +168,26 @@ def test_backward_random(i):
     got = [to_host(t, "bf16") for t in (dq, dk, dv)]
     ref = LB.linattn_bwd_from_inputs(x["q"], x["k"], x["v"], x["g"], w.eps, "bf16")
     _check(got, ref, x, w.eps, f"B={B} N={N} H={H}")
+
+
+@pytest.mark.parametrize("i", range(COUNT))
+def test_backward_fmap_random(i):
+    import oracle.linattn_bwd_fmap as LBF
+    from test_gpu_bwd_fmap import _check as _check_fmap, _cos_conditioning
+
+    B, N, H = _draw(1007)[i]
+    fmap = ("elu1", "cos")[i % 2]
+    w = _workload("bwdfm", B, N, H, "bf16", 6500 + i)
+    print(f"\n[case] random backward {fmap} B={B} N={N} H={H}", flush=True)
+    x = W.generate(w, grad=True)
+    if fmap == "cos":
+        assert _cos_conditioning(x) > 0.3
+    dev = {t: to_device(x[t], "bf16") for t in "qkvg"}
+    dq, dk, dv = R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps, fmap=fmap)
+    torch().cuda.synchronize()
+    got = [to_host(t, "bf16") for t in (dq, dk, dv)]
+    ref = LBF.linattn_bwd_fmap_from_inputs(x["q"], x["k"], x["v"], x["g"], w.eps, "bf16", fmap)
+    _check_fmap(got, ref, x, w.eps, fmap, f"{fmap} B={B} N={N} H={H}")
 
 
 @pytest.mark.parametrize("i", range(COUNT))
