@@ -776,8 +776,12 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
   float* grad_parts =
       reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.bf16_partial_bytes);
   if (!mark(0)) return SANA_ERR_HIP;
-  if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream, fmap) !=
-      hipSuccess)
+  // k and v are read again by the k/v pass after the q pass: the reduction
+  // reads them with ordinary loads so that part of them is still in the
+  // Infinity Cache then (2 x 16384 x 70 step 243 -> 233 us: reduction
+  // 47.7 -> 53.1 us, k/v pass 113.3 -> 97.8 us)
+  if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream, fmap,
+                    true) != hipSuccess)
     return SANA_ERR_HIP;
   if (!mark(1)) return SANA_ERR_HIP;
   if (launch_bwd_q(fp, q, g, dq, fwd_parts, grad_parts, eps, stream, fmap) != hipSuccess)
