@@ -777,9 +777,10 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
       reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.bf16_partial_bytes);
   if (!mark(0)) return SANA_ERR_HIP;
   // k and v are read again by the k/v pass after the q pass: the reduction
-  // reads them with ordinary loads so that part of them is still in the
-  // Infinity Cache then (2 x 16384 x 70 step 243 -> 233 us: reduction
-  // 47.7 -> 53.1 us, k/v pass 113.3 -> 97.8 us)
+  // reads k with ordinary loads so that much of it is still in the Infinity
+  // Cache then (2 x 16384 x 70 step 243 -> 230.6 us: reduction 47.7 -> 48.2
+  // us, k/v pass 113.3 -> 100.2 us; keeping k and v both, 233 us: reduction
+  // 53.0, k/v pass 97.7; v alone 232 us)
   if (launch_reduce(fp, dtype, false, k, v, fwd_parts, nullptr, nullptr, 0, stream, fmap,
                     true) != hipSuccess)
     return SANA_ERR_HIP;

@@ -84,13 +84,13 @@ int block_waves(KernelKind kind, int dtype);  // waves per block
 // also folds them into `state`, without (bf16) the partials are the result
 // and launch_apply_partials sums them where it needs them.
 // fmap is the feature map (sana_fmap_t; the bf16 fold is ReLU only).
-// keep_kv (bf16 partials only): k and v are read with ordinary loads, which
-// leave part of them in the Infinity Cache for a later pass that reads them
-// again (the backward's k/v pass); otherwise with streaming loads.
+// keep_k (bf16 partials only): k is read with ordinary loads, which leave
+// much of it in the Infinity Cache for a later pass that reads it again (the
+// backward's k/v pass); otherwise k and v with streaming loads.
 hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, const void* v,
                          float* partials, float* state, unsigned long long* ctl,
                          unsigned long long epoch, hipStream_t stream, int fmap = 0,
-                         bool keep_kv = false);
+                         bool keep_k = false);
 // Apply from a folded [B][H][d][d+1] state.
 hipError_t launch_apply(const Plan& p, int dtype, const void* q, const float* state,
                         void* out, float eps, hipStream_t stream, int fmap = 0);

@@ -252,7 +252,7 @@ __device__ __forceinline__ void put(float* p, float x) {
 // exists (H odd leaves the last pair with one head: its lanes then read the
 // first head's half-line again, which stays inside the tensor, and the second
 // head's sums are discarded).
-template <int U, int Fm = kFmapRelu, bool Temporal = false>
+template <int U, int Fm = kFmapRelu, bool KeepK = false, bool KeepV = false>
 __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V,
                                                  int64_t row, int64_t base, int64_t n_lo,
@@ -279,8 +279,8 @@ __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restric
     for (int h2 = 0; h2 < 2; ++h2) {
       const int64_t n = n0 + 8 * h2;
       const int64_t off = base + (n < n_hi ? n : n_lo) * row + 8 * jl;
-      kd[h2] = Temporal ? ld16_keep(K + off) : ld16_stream(K + off);
-      vd[h2] = Temporal ? ld16_keep(V + off) : ld16_stream(V + off);
+      kd[h2] = KeepK ? ld16_keep(K + off) : ld16_stream(K + off);
+      vd[h2] = KeepV ? ld16_keep(V + off) : ld16_stream(V + off);
     }
   };
 #pragma unroll
@@ -1051,10 +1051,10 @@ __device__ __forceinline__ Item xcd_item(int64_t units, int64_t C, int64_t X) {
 // the state; without, the partials are the result (the apply sums them).
 // Partials: [units][slots][2 heads][d][d+1]. Element (b, n, h, c) of k and
 // v is at b * N * ld + n * ld + h * d + c (ld = H * d when contiguous).
-// Temporal: k and v are read with ordinary loads instead of streaming ones,
-// for a caller that reads them again after a pass over other tensors (the
+// KeepK: k is read with ordinary loads instead of streaming ones, for a
+// caller that reads it again after a pass over other tensors (the
 // backward's k/v pass).
-template <int S, int U, bool Fold, int Fm = kFmapRelu, bool Temporal = false>
+template <int S, int U, bool Fold, int Fm = kFmapRelu, bool KeepK = false>
 __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const unsigned short* __restrict__ K, const unsigned short* __restrict__ V,
     float* __restrict__ partials, float* __restrict__ state, unsigned long long* __restrict__ ctl,
@@ -1081,8 +1081,8 @@ __global__ __launch_bounds__(64 * S) void reduce_bf16_kernel(
     const int64_t base = sg.b * N * ld + sg.h * kD;
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
-    reduce_pair_wave<U, Fm, Temporal>(K, V, ld, base, sg.n_lo, sg.n_hi, sub, S, sg.two,
-                                      lds.slot[sub], acc, ks);
+    reduce_pair_wave<U, Fm, KeepK>(K, V, ld, base, sg.n_lo, sg.n_hi, sub, S, sg.two,
+                                   lds.slot[sub], acc, ks);
     int64_t slot, count;
     if (C > 0) {
       slot = chunk;
@@ -1904,10 +1904,12 @@ __device__ __forceinline__ void load_acc_state(const float* src, f32x16 (&acc)[2
 }
 
 constexpr int kCausalStateU = 1;  // tiles a states wave issues ahead (2 measured slower)
-// The states read k and v with ordinary loads, so that part of them is
-// still in the Infinity Cache when the apply reads them again (2 x 16384 x
-// 70 token-causal step 171.1 -> 161.0 us: apply 113.7 -> 99.6 us by events;
-// walking each chunk backwards as well made no further difference).
+// The states read v with ordinary loads, so that much of it is still in the
+// Infinity Cache when the apply reads it again (2 x 16384 x 70 token-causal
+// step 171.1 -> 157.4 us: apply 113.7 -> 99.2 us by events, states 48.3 ->
+// 51.4 us). Keeping k and v both: states 56.7 us, apply as with v alone
+// (161 us); k alone 160-163 us. Walking each chunk backwards made no
+// difference.
 
 template <int S>
 __global__ __launch_bounds__(64 * S) void causal_states_kernel(
@@ -1920,7 +1922,7 @@ __global__ __launch_bounds__(64 * S) void causal_states_kernel(
   if (!cw.valid) return;  // the whole wave; no block barrier below
   f32x16 acc[2] = {(f32x16)0, (f32x16)0};
   float ks[2] = {0.0f, 0.0f};
-  reduce_pair_wave<kCausalStateU, kFmapRelu, true>(K, V, H * kD, (cw.b * N * H + cw.h) * kD,
+  reduce_pair_wave<kCausalStateU, kFmapRelu, false, true>(K, V, H * kD, (cw.b * N * H + cw.h) * kD,
                                                    cw.n_lo, cw.n_hi, 0, 1, cw.two, slots[sub],
                                                    acc, ks);
   store_acc_state(parts + (cw.unit * chunks + cw.chunk) * 2 * kSF, acc, ks);
@@ -2424,7 +2426,7 @@ hipError_t with_fmap(int fmap, F&& f) {
 
 hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, const void* v,
                          float* partials, float* state, unsigned long long* ctl,
-                         unsigned long long epoch, hipStream_t stream, int fmap, bool keep_kv) {
+                         unsigned long long epoch, hipStream_t stream, int fmap, bool keep_k) {
   const int64_t BH = p.B * p.H;
   if (dtype == 1 && fold && fmap != kFmapRelu) return hipErrorInvalidValue;
   if (dtype != 1 && !fold) return hipErrorInvalidValue;
@@ -2432,7 +2434,7 @@ hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, con
     constexpr int Fm = decltype(fm)::value;
     if (dtype == 1) {
       auto* kernel = fold      ? reduce_bf16_kernel<kRedS, kRedU, true, kFmapRelu>
-                     : keep_kv ? reduce_bf16_kernel<kRedS, kRedU, false, Fm, true>
+                     : keep_k  ? reduce_bf16_kernel<kRedS, kRedU, false, Fm, true>
                                : reduce_bf16_kernel<kRedS, kRedU, false, Fm>;
       const bool chunked = p.red_cb > 0;
       const int64_t X = apply_xcds(p);
