@@ -83,6 +83,19 @@ def _bwd_case(B, N, H):
                 ws, call)
 
 
+def _bwd_fmap_case(B, N, H, fmap):
+    lib = R.lib()
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_bwd_workspace_size, B, N, H, 32, BF16)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_bwd_fmap(_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["g"]),
+                                         _p(t["dq"]), _p(t["dk"]), _p(t["dv"]), B, N, H, 32, 1e-6,
+                                         BF16, fmap, _p(ws_t), ws_t.numel(), None, 0, _stream())
+    return Case({c: (shape, BF16) for c in "qkvg"}, {c: (shape, BF16) for c in ("dq", "dk", "dv")},
+                ws, call)
+
+
 def _block_causal_case(B, N, H, L, dt):
     lib = R.lib()
     shape = (B, N, H, 32)
@@ -129,6 +142,8 @@ CASES = {
     "fwd_bf16_split": lambda: _fwd_case(1, 8192, 6, BF16),
     "fwd_bf16_fused": lambda: _fwd_case(2, 700, 9, BF16, variant=R.VARIANT_FUSED),
     "bwd_bf16": lambda: _bwd_case(1, 3000, 5),
+    # the backward with ELU + 1 (the feature-map instantiations of the same passes)
+    "bwd_bf16_elu1": lambda: _bwd_fmap_case(1, 3000, 5, 1),
     # fp32 block-causal: the folding reduction over blocks, the scan, the apply
     "block_causal_f32": lambda: _block_causal_case(2, 2048, 3, 512, F32),
     "qkv_bf16": lambda: _qkv_case(1, 700, 200, 5),
