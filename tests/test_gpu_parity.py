@@ -100,13 +100,15 @@ def test_ragged_shapes(B, N, H, dtype):
 
 
 @pytest.mark.parametrize("B,N,H", [(16, 1000, 65), (32, 77, 33), (40, 300, 27), (16, 1024, 64),
-                                   (8, 1000, 65), (9, 300, 57), (8, 1024, 64), (4, 1024, 70)])
+                                   (8, 1000, 65), (9, 300, 57), (8, 1024, 64), (4, 1024, 70),
+                                   (600, 1, 2), (300, 17, 3)])
 def test_fused_block_shapes(B, N, H):
     """The fused kernel's block shape follows the head-pair units per CU
     (MI355X: 256 CUs): 4-wave blocks with one tile in flight from 512 units,
     8-wave blocks with one tile from 256, with two below. Ragged token counts,
     odd head counts (a one-head last pair) and unit counts of exactly 512 and
-    256 against the oracle, and repeat calls bit for bit."""
+    256 against the oracle, sequences shorter than a block's waves (N = 1,
+    N = 17 over 600 units), and repeat calls bit for bit."""
     w = W.custom(f"fused_{B}_{N}_{H}", B, N, H, seed=300 + N + H,
                  q=W.Dist("normal", 0.1, 1.0), k=W.Dist("normal", 0.1, 1.0))
     print(f"\n[case] fused block shape B={B} N={N} H={H}", flush=True)
