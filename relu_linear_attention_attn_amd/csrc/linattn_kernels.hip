@@ -251,7 +251,9 @@ __device__ __forceinline__ void put(float* p, float x) {
 // element stride between tokens. `two` says whether the pair's second head
 // exists (H odd leaves the last pair with one head: its lanes then read the
 // first head's half-line again, which stays inside the tensor, and the second
-// head's sums are discarded).
+// head's sums are discarded). KeepK / KeepV: that tensor is read with
+// ordinary loads, which leave it in the caches (the Infinity Cache included)
+// for a later pass; otherwise with streaming loads.
 template <int U, int Fm = kFmapRelu, bool KeepK = false, bool KeepV = false>
 __device__ __forceinline__ void reduce_pair_wave(const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V,
@@ -1922,9 +1924,9 @@ __global__ __launch_bounds__(64 * S) void causal_states_kernel(
   if (!cw.valid) return;  // the whole wave; no block barrier below
   f32x16 acc[2] = {(f32x16)0, (f32x16)0};
   float ks[2] = {0.0f, 0.0f};
-  reduce_pair_wave<kCausalStateU, kFmapRelu, false, true>(K, V, H * kD, (cw.b * N * H + cw.h) * kD,
-                                                   cw.n_lo, cw.n_hi, 0, 1, cw.two, slots[sub],
-                                                   acc, ks);
+  reduce_pair_wave<kCausalStateU, kFmapRelu, false, true>(
+      K, V, H * kD, (cw.b * N * H + cw.h) * kD, cw.n_lo, cw.n_hi, 0, 1, cw.two, slots[sub], acc,
+      ks);
   store_acc_state(parts + (cw.unit * chunks + cw.chunk) * 2 * kSF, acc, ks);
 }
 
