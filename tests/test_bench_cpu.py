@@ -46,6 +46,14 @@ def test_cpu_baseline_backward_and_block_causal():
     _check_record(bench.cpu_baseline_block_causal(w, x, 64, 0.02), w)
 
 
+@pytest.mark.parametrize("fmap", ["elu1", "cos"])
+def test_cpu_baseline_backward_feature_maps(fmap):
+    w = W.custom("bench_cpu_bwd_fm", 1, 256, 2, dtype="bf16", seed=7)
+    rec = bench.cpu_baseline_bwd(w, W.generate(w, grad=True), 0.02, fmap)
+    _check_record(rec, w)
+    assert fmap in rec["sample"]
+
+
 def test_cpu_baseline_qkv():
     w = W.custom("bench_cpu_qkv", 1, 128, 2, dtype="bf16", seed=6)
     x = W.projection_inputs(w, 64)
