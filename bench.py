@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--layout", default="contiguous", choices=["contiguous", "packed"],
                     help="forward inputs as three [B][N][H][d] tensors, or read in place "
                          "from one packed [B][N][3][H][d] projection output (strided entry)")
+    ap.add_argument("--saved-state", action="store_true",
+                    help="--op bwd: take the forward's saved state (sana_linattn_bwd_state, "
+                         "the state made once per input set outside the timed region) instead "
+                         "of recomputing it")
     ap.add_argument("--block", type=int, default=65536,
                     help="tokens per block for --op block_causal")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -368,17 +372,28 @@ def run_bwd(args, w):
     n_sets = n_input_sets(args, 7 * elem)
     sets = device_sets(x, "qkvg", "bf16", ("dq", "dk", "dv"), n_sets)
     ws = torch.empty(R.bwd_workspace_size(w.B, w.N, w.H), dtype=torch.uint8, device="cuda")
+    saved = args.saved_state
+    if saved:
+        if args.fmap != "relu":
+            raise SystemExit("--saved-state: the ReLU backward only")
+        # the state a training step keeps from its forward pass, once per input set,
+        # outside the timed region
+        for d in sets:
+            d["state"] = R.kv_state(d["k"], d["v"])
+        torch.cuda.synchronize()
 
     def step(i, events=None):
         d = sets[i % n_sets]
         R.backward(d["q"], d["k"], d["v"], d["g"], eps=w.eps, grads=(d["dq"], d["dk"], d["dv"]),
-                   workspace=ws, events=events, fmap=args.fmap)
+                   workspace=ws, events=events, fmap=args.fmap,
+                   state=d["state"] if saved else None)
 
-    names = ["reduce", "bwd_q", "bwd_kv"]
+    names = ["bwd_q", "bwd_kv"] if saved else ["reduce", "bwd_q", "bwd_kv"]
     log(args, f"warmup {args.warmup} steps ({len(names)} kernels per step, {n_sets} input sets)")
     for i in range(args.warmup):
         step(i)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     stream = torch.cuda.current_stream()
     for ev in events:
         for e in ev:
@@ -391,8 +406,9 @@ def run_bwd(args, w):
     ms_one_set = time_steps(lambda i: step(0), args.steps)
     per_kernel = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events]))
                   for j, n in enumerate(names)}
-    step_ms = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
+    step_ms = sorted(ev[0].elapsed_time(ev[len(names)]) for ev in events)
     alg_bytes = {"reduce": 2 * elem, "bwd_q": 3 * elem, "bwd_kv": 4 * elem}
+    alg_bytes = {n: alg_bytes[n] for n in names}
     total_bytes = sum(alg_bytes.values())
     dominant = max(per_kernel, key=per_kernel.get)
     achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-3) / 1e9
@@ -411,7 +427,8 @@ def run_bwd(args, w):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "op": "bwd", "B": w.B, "N": w.N, "H": w.H, "d": w.d,
-                   "D": w.D, "fmap": args.fmap, "eps": w.eps, "input_sets": n_sets},
+                   "D": w.D, "fmap": args.fmap, "eps": w.eps, "input_sets": n_sets,
+                   "state": "saved" if saved else "recomputed"},
         "achieved_hbm_gbps": path_gbps,
         "hbm_roofline_frac": path_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": total_bytes,
@@ -422,7 +439,7 @@ def run_bwd(args, w):
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": (measured_traffic(dominant, w.name, "bwd")
-                                 if args.fmap == "relu" else None)},
+                                 if args.fmap == "relu" and not saved else None)},
     }
     if args.copy_mib == 0:
         ceil = copy_ceiling(ws.device)

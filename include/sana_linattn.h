@@ -344,6 +344,28 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
                                         hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
+ * sana_linattn_bwd from a saved forward state: `state` is the fp32
+ * [B][H][d][d+1] state of the same k and v, as sana_linattn_kv_state writes
+ * it (KV in the first d columns, ksum in the last; 16-byte aligned,
+ * sana_linattn_state_size bytes, read only). The state is the only part of
+ * the forward a training step needs to keep (d (d + 1) floats per head,
+ * independent of N); with it the backward skips the state reduction and
+ * reads k and v once (two kernels: the q pass and the k/v pass). With the
+ * state of sana_linattn_kv_state(k, v) the gradients are bitwise those of
+ * sana_linattn_bwd. Tensors, workspace (sana_linattn_bwd_workspace_size),
+ * checks and errors as sana_linattn_bwd; a NULL state is
+ * SANA_ERR_INVALID_ARG, an output or the workspace overlapping it too.
+ * events may be NULL; otherwise n_events >= 3 and events[0..2] are recorded
+ * before the q pass, after it and after the k/v pass.
+ */
+sana_status_t sana_linattn_bwd_state(const void* q, const void* k, const void* v,
+                                     const void* dout, const float* state, void* dq, void* dk,
+                                     void* dv, int64_t B, int64_t N, int64_t H, int64_t d,
+                                     float eps, sana_dtype_t dtype, void* workspace,
+                                     size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                     hipStream_t stream);
+
+/*
  * The backward pass of sana_linattn_fwd_fmap (bf16 only): the gradients of
  * sana_linattn_bwd with feature map `fmap` (sana_fmap_t) in place of ReLU,
  * the map's derivative in place of the mask [x > 0]:

@@ -42,6 +42,7 @@ EXPORTS = (
     "sana_linattn_bwd",
     "sana_linattn_bwd_profiled",
     "sana_linattn_bwd_fmap",
+    "sana_linattn_bwd_state",
     "sana_linattn_block_causal_workspace_size",
     "sana_linattn_fwd_block_causal",
     "sana_linattn_fwd_block_causal_profiled",
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
                                                                 _vp, _sz, _vp]
         L.sana_linattn_bwd_profiled.argtypes = [_vp] * 7 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+        L.sana_linattn_bwd_state.argtypes = [_vp] * 8 + [_i64] * 4 + [
+            ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         L.sana_linattn_bwd_fmap.argtypes = [_vp] * 7 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
             ctypes.c_int, _vp]
@@ -142,7 +145,8 @@ def lib() -> ctypes.CDLL:
         for name in ("sana_linattn_block_causal_workspace_size", "sana_linattn_fwd_block_causal",
                      "sana_linattn_fwd_block_causal_profiled", "sana_linattn_causal_workspace_size",
                      "sana_linattn_fwd_causal", "sana_linattn_fwd_fmap",
-                     "sana_linattn_bwd_fmap", "sana_linattn_fwd_strided",
+                     "sana_linattn_bwd_fmap", "sana_linattn_bwd_state",
+                     "sana_linattn_fwd_strided",
                      "sana_linattn_qkv_workspace_size", "sana_linattn_qkv_fwd"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("sana_linattn_workspace_size", "sana_linattn_state_size",
@@ -361,17 +365,22 @@ def bwd_workspace_size(B: int, N: int, H: int, d: int = HEAD_DIM, dtype: int = D
 
 
 def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grads=None,
-             workspace=None, events=None, fmap: str = "relu"):
+             workspace=None, events=None, fmap: str = "relu", state=None):
     """(dq, dk, dv) of the forward pass for the upstream gradient dout (bf16).
 
     q, k, v, dout: contiguous bf16 GPU tensors of one shape. grads: optional
-    preallocated (dq, dk, dv). events: optional list of 4 torch.cuda.Event
-    (enable_timing=True) recorded before the first and after each of the
-    three kernels. fmap: the forward's feature map ("relu", "elu1", "cos";
-    anything but "relu" calls sana_linattn_bwd_fmap). Enqueued on torch's
-    current stream; no synchronisation."""
+    preallocated (dq, dk, dv). events: optional list of torch.cuda.Event
+    (enable_timing=True) recorded before the first and after each kernel (4
+    events; 3 with a state). fmap: the forward's feature map ("relu",
+    "elu1", "cos"; anything but "relu" calls sana_linattn_bwd_fmap). state:
+    optional saved forward state, the fp32 (B, H, d, d + 1) tensor of
+    kv_state(k, v) (ReLU only; calls sana_linattn_bwd_state, which skips the
+    state reduction). Enqueued on torch's current stream; no
+    synchronisation."""
     if fmap not in FMAPS:
         raise ValueError(f"unknown feature map {fmap!r}; one of {sorted(FMAPS)}")
+    if state is not None and fmap != "relu":
+        raise ValueError("a saved state is taken by the ReLU backward only")
     torch = _torch()
     B, N, H, d = _shape(q, heads)
     _check_tensor(q, "q")
@@ -388,7 +397,16 @@ def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grad
                                 device=q.device)
     wb = workspace.numel() * workspace.element_size()
     ptrs = [t.data_ptr() for t in (q, k, v, dout, *grads)]
-    if fmap != "relu":
+    if state is not None:
+        if (not state.is_cuda or state.dtype != torch.float32 or not state.is_contiguous()
+                or state.numel() * 4 != state_size(B, H, d) or state.device != q.device):
+            raise ValueError("state must be a contiguous float32 tensor of kv_state's size on "
+                             "q's device")
+        arr, n = _event_array(events)
+        _check(lib().sana_linattn_bwd_state(*ptrs[:4], state.data_ptr(), *ptrs[4:], B, N, H, d,
+                                            float(eps), dt, workspace.data_ptr(), wb, arr, n,
+                                            _stream(q)), "sana_linattn_bwd_state")
+    elif fmap != "relu":
         arr, n = _event_array(events)
         _check(lib().sana_linattn_bwd_fmap(*ptrs, B, N, H, d, float(eps), dt, FMAPS[fmap],
                                            workspace.data_ptr(), wb, arr, n, _stream(q)),

@@ -727,20 +727,27 @@ sana_status_t qkv_forward(const void* x, const void* w, void* q, void* out, int6
 
 // The backward pass (bf16): the forward state reduction (partials only),
 // bwd_q (dq and the [dS | dz] partials), bwd_kv (dk, dv). events (may be
-// NULL) are recorded before the first kernel and after each of the three.
+// NULL) are recorded before the first kernel and after each one. With a
+// saved forward state (state != NULL: fp32 [B][H][d][d+1], ReLU), the
+// reduction is skipped and bwd_q reads that state.
 sana_status_t backward(const void* q, const void* k, const void* v, const void* g, void* dq,
                        void* dk, void* dv, int64_t B, int64_t N, int64_t H, int64_t d, float eps,
                        int dtype, void* workspace, size_t workspace_bytes, hipEvent_t* events,
-                       int n_events, hipStream_t stream, int fmap = SANA_FMAP_RELU) {
+                       int n_events, hipStream_t stream, int fmap = SANA_FMAP_RELU,
+                       const float* state = nullptr, bool with_state = false) {
   size_t tb = 0;
   sana_status_t s = check_shape(B, N, H, d, dtype, &tb);
   if (s != SANA_OK) return s;
   if (dtype != SANA_DTYPE_BF16 || !valid_fmap(fmap)) return SANA_ERR_UNSUPPORTED;
+  const int kernels = with_state ? kBwdKernels - 1 : kBwdKernels;
   if (events) {
-    if (n_events < kBwdKernels + 1) return SANA_ERR_INVALID_ARG;
-    for (int i = 0; i <= kBwdKernels; ++i)
+    if (n_events < kernels + 1) return SANA_ERR_INVALID_ARG;
+    for (int i = 0; i <= kernels; ++i)
       if (!events[i]) return SANA_ERR_INVALID_ARG;
   }
+  if (with_state && !state) return SANA_ERR_INVALID_ARG;
+  if (with_state && misaligned(state)) return SANA_ERR_ALIGNMENT;
+  const size_t sbytes = static_cast<size_t>(B * H) * kStateFloats * 4;
   const void* in[] = {q, k, v, g};
   void* outs[] = {dq, dk, dv};
   for (const void* p : in)
@@ -766,7 +773,9 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
     for (int j = i + 1; j < 3; ++j)
       if (overlaps(outs[i], tb, outs[j], tb)) return SANA_ERR_INVALID_ARG;
     if (overlaps(outs[i], tb, workspace, wb)) return SANA_ERR_INVALID_ARG;
+    if (with_state && overlaps(outs[i], tb, state, sbytes)) return SANA_ERR_INVALID_ARG;
   }
+  if (with_state && overlaps(workspace, wb, state, sbytes)) return SANA_ERR_INVALID_ARG;
 
   (void)hipGetLastError();
   Plan fp = p;
@@ -776,6 +785,15 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
   float* grad_parts =
       reinterpret_cast<float*>(static_cast<char*>(workspace) + fp.bf16_partial_bytes);
   if (!mark(0)) return SANA_ERR_HIP;
+  if (with_state) {
+    // k and v are read once, by the k/v pass
+    if (launch_bwd_q(fp, q, g, dq, nullptr, state, grad_parts, eps, stream, fmap) != hipSuccess)
+      return SANA_ERR_HIP;
+    if (!mark(1)) return SANA_ERR_HIP;
+    if (launch_bwd_kv(fp, k, v, dk, dv, grad_parts, stream, fmap) != hipSuccess)
+      return SANA_ERR_HIP;
+    return mark(2) ? SANA_OK : SANA_ERR_HIP;
+  }
   // k and v are read again by the k/v pass after the q pass: the reduction
   // reads k with ordinary loads so that much of it is still in the Infinity
   // Cache then (2 x 16384 x 70 step 243 -> 230.6 us: reduction 47.7 -> 48.2
@@ -785,7 +803,8 @@ sana_status_t backward(const void* q, const void* k, const void* v, const void* 
                     true) != hipSuccess)
     return SANA_ERR_HIP;
   if (!mark(1)) return SANA_ERR_HIP;
-  if (launch_bwd_q(fp, q, g, dq, fwd_parts, grad_parts, eps, stream, fmap) != hipSuccess)
+  if (launch_bwd_q(fp, q, g, dq, fwd_parts, nullptr, grad_parts, eps, stream, fmap) !=
+      hipSuccess)
     return SANA_ERR_HIP;
   if (!mark(2)) return SANA_ERR_HIP;
   if (launch_bwd_kv(fp, k, v, dk, dv, grad_parts, stream, fmap) != hipSuccess)
@@ -939,6 +958,16 @@ sana_status_t sana_linattn_bwd_fmap(const void* q, const void* k, const void* v,
                                     hipStream_t stream) {
   return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
                         workspace_bytes, events, n_events, stream, fmap);
+}
+
+sana_status_t sana_linattn_bwd_state(const void* q, const void* k, const void* v,
+                                     const void* dout, const float* state, void* dq, void* dk,
+                                     void* dv, int64_t B, int64_t N, int64_t H, int64_t d,
+                                     float eps, sana_dtype_t dtype, void* workspace,
+                                     size_t workspace_bytes, hipEvent_t* events, int n_events,
+                                     hipStream_t stream) {
+  return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
+                        workspace_bytes, events, n_events, stream, SANA_FMAP_RELU, state, true);
 }
 
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,

@@ -113,9 +113,11 @@ hipError_t launch_qkv_state(const void* x, const void* w, void* q, float* partia
 // red_rule), writes dq and writes [dS | dz] partials in the same slots (same
 // rule); bwd_kv sums those and writes dk and dv.
 // fmap: the feature map (sana_fmap_t values) whose backward the passes take
+// state: a folded fp32 [B][H][d][d+1] forward state to take instead of the
+// partials fwd_parts (NULL: the partials).
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
-                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream,
-                        int fmap);
+                        const float* fwd_parts, const float* state, float* grad_parts, float eps,
+                        hipStream_t stream, int fmap);
 hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv,
                          const float* grad_parts, hipStream_t stream, int fmap);
 // Block-causal attention: p's batch items are the F blocks of each of the

@@ -1761,14 +1761,15 @@ struct StateOps {
 // bwd_q over one block's range of the flattened (unit, tile) index, on the
 // state reduction's grid: one (unit, chunk) item in XCD runs when C > 0,
 // else balanced ranges of Qb tiles. The forward state of a unit is the sum
-// of the reduction's partials fwd_parts (slots by rule Qf, see slot_count),
-// and the block writes its [dS | dz] partial of each unit it touches to
-// grad_parts in the reduction's slot (the chunk, or g - first), so the
-// partials follow the same slot rule.
+// of `slot_count(unit, T, Qf)` consecutive [2][d][d+1] slots at
+// src + b * sb + p * sp (pair p of batch item b): the reduction's partials
+// (rule Qf), or with Qf = 0 one folded state; and the block writes its
+// [dS | dz] partial of each unit it touches to grad_parts in the reduction's
+// slot (the chunk, or g - first), so the partials follow the same slot rule.
 template <int S, int U, int Fm = kFmapRelu>
 __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
     const unsigned short* __restrict__ Q, const unsigned short* __restrict__ G,
-    unsigned short* __restrict__ dQ, const float* __restrict__ fwd_parts,
+    unsigned short* __restrict__ dQ, const float* __restrict__ src, int64_t sb, int64_t sp,
     float* __restrict__ grad_parts, float eps, int64_t N, int64_t H, int64_t pairs, int64_t T,
     int64_t Qb, int64_t F, int64_t slots, int64_t Qf, int64_t C, int64_t X) {
   static_assert(2 * kWave * S >= 2 * kSF / 4, "two state elements per thread cover a pair");
@@ -1796,7 +1797,7 @@ __global__ __launch_bounds__(64 * S) void bwd_q_bf16_kernel(
   for (int64_t unit = f_lo / T; unit * T < f_hi; ++unit) {
     const Segment sg = segment_of(unit, f_lo, f_hi, T, N, H, pairs);
     const int64_t slot = C > 0 ? chunk : g - slot_range(unit, T, Qb).first;
-    const StateOps ops{reinterpret_cast<const f32x4*>(fwd_parts + unit * slots * 2 * kSF),
+    const StateOps ops{reinterpret_cast<const f32x4*>(src + sg.b * sb + (sg.h >> 1) * sp),
                        slot_count(unit, T, Qf), sg.two, stage};
     f32x16 acc[2] = {(f32x16)0, (f32x16)0};
     float ks[2] = {0.0f, 0.0f};
@@ -2554,8 +2555,8 @@ hipError_t launch_apply_slots(const Plan& p, const void* q, const float* partial
 }
 
 hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
-                        const float* fwd_parts, float* grad_parts, float eps, hipStream_t stream,
-                        int fmap) {
+                        const float* fwd_parts, const float* state, float* grad_parts, float eps,
+                        hipStream_t stream, int fmap) {
   // the reduction's grid: (unit, chunk) items when the plan has them, else
   // balanced ranges; the [dS | dz] partials then follow the same slot rule
   const bool chunked = p.red_cb > 0;
@@ -2566,8 +2567,11 @@ hipError_t launch_bwd_q(const Plan& p, const void* q, const void* g, void* dq,
     hipLaunchKernelGGL((bwd_q_bf16_kernel<kBwqS, kBwqU, Fm>), dim3((unsigned)blocks),
                        dim3(64 * kBwqS), 0, stream, static_cast<const unsigned short*>(q),
                        static_cast<const unsigned short*>(g), static_cast<unsigned short*>(dq),
-                       fwd_parts, grad_parts, eps, p.N, p.H, p.pairs, p.tiles,
-                       chunked ? p.red_cq : p.red_q, p.units * p.tiles, p.slots, red_rule(p),
+                       state ? state : fwd_parts,
+                       state ? p.H * kSF : p.pairs * p.slots * 2 * kSF,
+                       state ? int64_t(2 * kSF) : p.slots * 2 * kSF, grad_parts, eps, p.N, p.H,
+                       p.pairs, p.tiles, chunked ? p.red_cq : p.red_q, p.units * p.tiles,
+                       p.slots, state ? int64_t(0) : red_rule(p),
                        chunked ? p.red_cb : int64_t(0), X);
     return hipGetLastError();
   });

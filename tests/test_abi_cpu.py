@@ -257,6 +257,37 @@ def test_bwd_fmap_rejects_invalid_arguments(L):
     assert bwd_fmap(L, events=events, n_events=3) == INVALID
 
 
+def bwd_state(L, state=P_W + (1 << 29), q=P_Q, k=P_K, v=P_V, g=P_G, dq=P_DQ, dk=P_DK, dv=P_DV,
+              B=1, N=64, H=2, d=32, eps=1e-6, dt=BF16, ws=P_W, wsb=1 << 20, events=None,
+              n_events=0):
+    return L.sana_linattn_bwd_state(q, k, v, g, state, dq, dk, dv, B, N, H, d, eps, dt, ws, wsb,
+                                    events, n_events, None)
+
+
+def test_bwd_state_rejects_invalid_arguments(L):
+    """The saved-state backward runs sana_linattn_bwd's checks, plus the
+    state's: present, 16-byte aligned, overlapping no output and not the
+    workspace (inputs may share memory with it: it is read only)."""
+    assert bwd_state(L, B=0) == INVALID
+    assert bwd_state(L, d=16) == UNSUPPORTED
+    assert bwd_state(L, dt=F32) == UNSUPPORTED
+    assert bwd_state(L, state=None) == INVALID
+    assert bwd_state(L, state=P_W + (1 << 29) + 8) == ALIGNMENT
+    for name in ("q", "k", "v", "g", "dq", "dk", "dv"):
+        assert bwd_state(L, **{name: None}) == INVALID, name
+    # a state overlapping an output or the workspace (its 8448 B for B = 1, H = 2)
+    assert bwd_state(L, state=P_DQ + 64) == INVALID
+    assert bwd_state(L, state=P_DV) == INVALID
+    assert bwd_state(L, state=P_W + 256) == INVALID
+    need = bws(L, 1, 64, 2)[1]
+    assert bwd_state(L, wsb=need - 1) == WORKSPACE
+    # two kernels: three events
+    events = (ctypes.c_void_p * 2)(None, None)
+    assert bwd_state(L, events=events, n_events=2) == INVALID
+    events3 = (ctypes.c_void_p * 3)(None, None, None)
+    assert bwd_state(L, events=events3, n_events=3) == INVALID  # NULL events
+
+
 def bcws(L, B, N, H, blk, d=32, dt=BF16):
     n = ctypes.c_size_t(123)
     st = L.sana_linattn_block_causal_workspace_size(B, N, H, d, blk, dt, ctypes.byref(n))

@@ -194,3 +194,27 @@ def test_bwd_profiled_matches_plain():
     for s, t in zip(a, grads):
         assert np.array_equal(s, to_host(t, "bf16"))
     assert all(ev[i].elapsed_time(ev[i + 1]) > 0 for i in range(3))
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 1, 1), (2, 257, 3), (2, 5000, 7), (1, 33000, 3),
+                                   (16, 1024, 70), (2, 16384, 70)])
+def test_bwd_from_saved_state_is_the_recomputing_backward_bitwise(B, N, H):
+    """sana_linattn_bwd_state with the state of sana_linattn_kv_state(k, v)
+    skips the state reduction and gives sana_linattn_bwd's bits: the fold
+    sums the same partials in the same order as the q pass would. Shapes on
+    the (head pair, chunk) grid and on balanced ranges (16 x 1024 x 70),
+    odd head counts, one token; the event form records its two kernels."""
+    w = W.custom(f"bwd_state_{B}_{N}_{H}", B, N, H, seed=500 + N + H,
+                 q=W.Dist("normal", 0.1, 1.0), k=W.Dist("normal", 0.1, 1.0))
+    print(f"\n[case] bwd from saved state B={B} N={N} H={H}", flush=True)
+    x, dev = _inputs(w)
+    ref = _run(w, dev)
+    state = R.kv_state(dev["k"], dev["v"])
+    ev = [torch().cuda.Event(enable_timing=True) for _ in range(3)]
+    for events in (None, ev):
+        grads = R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps, state=state,
+                           events=events)
+        torch().cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), ref, grads):
+            assert np.array_equal(a, to_host(b, "bf16")), (name, events is not None)
+    assert all(ev[i].elapsed_time(ev[i + 1]) > 0 for i in range(2))
