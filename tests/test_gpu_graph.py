@@ -96,6 +96,21 @@ def _bwd_fmap_case(B, N, H, fmap):
                 ws, call)
 
 
+def _bwd_state_case(B, N, H):
+    lib = R.lib()
+    shape = (B, N, H, 32)
+    ws = _size(lib.sana_linattn_bwd_workspace_size, B, N, H, 32, BF16)
+
+    def call(t, ws_t):
+        return lib.sana_linattn_bwd_state(_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["g"]),
+                                          _p(t["s"]), _p(t["dq"]), _p(t["dk"]), _p(t["dv"]), B, N,
+                                          H, 32, 1e-6, BF16, _p(ws_t), ws_t.numel(), None, 0,
+                                          _stream())
+    inputs = {c: (shape, BF16) for c in "qkvg"}
+    inputs["s"] = ((B, H, 32, 33), F32)  # a state; replays only need it fixed per replay
+    return Case(inputs, {c: (shape, BF16) for c in ("dq", "dk", "dv")}, ws, call)
+
+
 def _block_causal_case(B, N, H, L, dt):
     lib = R.lib()
     shape = (B, N, H, 32)
@@ -144,6 +159,8 @@ CASES = {
     "bwd_bf16": lambda: _bwd_case(1, 3000, 5),
     # the backward with ELU + 1 (the feature-map instantiations of the same passes)
     "bwd_bf16_elu1": lambda: _bwd_fmap_case(1, 3000, 5, 1),
+    # the backward from a saved state: the q pass and the k/v pass
+    "bwd_bf16_state": lambda: _bwd_state_case(2, 3000, 5),
     # fp32 block-causal: the folding reduction over blocks, the scan, the apply
     "block_causal_f32": lambda: _block_causal_case(2, 2048, 3, 512, F32),
     "qkv_bf16": lambda: _qkv_case(1, 700, 200, 5),
