@@ -2,7 +2,7 @@
 oracles: the forward (each variant and dtype), the strided forward on a
 packed projection output with a random row padding, the other feature maps,
 block-causal attention with a random block length, token-causal attention,
-the backward (ReLU, ELU + 1, cos), and the QKV projection path. The shapes are drawn from a fixed seed, with token
+the backward (ReLU, ELU + 1, cos; from a saved state bitwise as recomputing), and the QKV projection path. The shapes are drawn from a fixed seed, with token
 counts near the kernels' boundaries (multiples of the 16-token tile, the
 256-token projection tile, the fused variant's 1024-token limit) more often
 than elsewhere, and small enough for the oracle to finish in seconds.
@@ -188,6 +188,23 @@ def test_backward_fmap_random(i):
     got = [to_host(t, "bf16") for t in (dq, dk, dv)]
     ref = LBF.linattn_bwd_fmap_from_inputs(x["q"], x["k"], x["v"], x["g"], w.eps, "bf16", fmap)
     _check_fmap(got, ref, x, w.eps, fmap, f"{fmap} B={B} N={N} H={H}")
+
+
+@pytest.mark.parametrize("i", range(COUNT))
+def test_backward_saved_state_random(i):
+    """The backward from kv_state's saved state gives the recomputing
+    backward's bits."""
+    B, N, H = _draw(1009)[i]
+    w = _workload("bwdst", B, N, H, "bf16", 7000 + i)
+    print(f"\n[case] random backward from a saved state B={B} N={N} H={H}", flush=True)
+    x = W.generate(w, grad=True)
+    dev = {t: to_device(x[t], "bf16") for t in "qkvg"}
+    a = R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps)
+    b = R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps,
+                   state=R.kv_state(dev["k"], dev["v"]))
+    torch().cuda.synchronize()
+    for name, s, t in zip(("dq", "dk", "dv"), a, b):
+        assert np.array_equal(to_host(s, "bf16"), to_host(t, "bf16")), name
 
 
 @pytest.mark.parametrize("i", range(COUNT))
