@@ -374,12 +374,10 @@ def run_bwd(args, w):
     ws = torch.empty(R.bwd_workspace_size(w.B, w.N, w.H), dtype=torch.uint8, device="cuda")
     saved = args.saved_state
     if saved:
-        if args.fmap != "relu":
-            raise SystemExit("--saved-state: the ReLU backward only")
         # the state a training step keeps from its forward pass, once per input set,
         # outside the timed region
         for d in sets:
-            d["state"] = R.kv_state(d["k"], d["v"])
+            d["state"] = R.kv_state(d["k"], d["v"], fmap=args.fmap)
         torch.cuda.synchronize()
 
     def step(i, events=None):

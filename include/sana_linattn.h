@@ -287,6 +287,20 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state,
                                     hipStream_t stream);
 
 /*
+ * sana_linattn_kv_state with feature map `fmap` (sana_fmap_t) in place of
+ * ReLU: KV = phi(K)^T V and ksum = phi(K)^T 1 of that map (in bf16, phi of
+ * ELU + 1 and cos is evaluated in fp32 and split into bf16 hi + lo parts for
+ * the MFMAs, as in sana_linattn_fwd_fmap). The state a training step keeps
+ * for sana_linattn_bwd_state with the same map. Tensors, workspace, checks
+ * and errors as sana_linattn_kv_state; an fmap outside sana_fmap_t returns
+ * SANA_ERR_UNSUPPORTED. SANA_FMAP_RELU is sana_linattn_kv_state.
+ */
+sana_status_t sana_linattn_kv_state_fmap(const void* k, const void* v, float* state,
+                                         int64_t B, int64_t N, int64_t H, int64_t d,
+                                         sana_dtype_t dtype, sana_fmap_t fmap, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Second half of the forward pass: out_i = phi(q_i) KV / (phi(q_i) . ksum + eps)
  * for every token of every (b, h), reading `state` (fp32 [B][H][d][d+1], as
  * written by sana_linattn_kv_state or computed elsewhere, e.g. summed over
@@ -344,16 +358,18 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
                                         hipEvent_t* events, int n_events, hipStream_t stream);
 
 /*
- * sana_linattn_bwd from a saved forward state: `state` is the fp32
- * [B][H][d][d+1] state of the same k and v, as sana_linattn_kv_state writes
+ * sana_linattn_bwd (fmap = SANA_FMAP_RELU) or sana_linattn_bwd_fmap from a
+ * saved forward state: `state` is the fp32 [B][H][d][d+1] state of the same
+ * k, v and map, as sana_linattn_kv_state / sana_linattn_kv_state_fmap write
  * it (KV in the first d columns, ksum in the last; 16-byte aligned,
  * sana_linattn_state_size bytes, read only). The state is the only part of
  * the forward a training step needs to keep (d (d + 1) floats per head,
  * independent of N); with it the backward skips the state reduction and
  * reads k and v once (two kernels: the q pass and the k/v pass). With the
- * state of sana_linattn_kv_state(k, v) the gradients are bitwise those of
- * sana_linattn_bwd. Tensors, workspace (sana_linattn_bwd_workspace_size),
- * checks and errors as sana_linattn_bwd; a NULL state is
+ * state of sana_linattn_kv_state_fmap(k, v, fmap) the gradients are bitwise
+ * those of the recomputing backward. Tensors, workspace
+ * (sana_linattn_bwd_workspace_size), checks and errors as sana_linattn_bwd;
+ * an fmap outside sana_fmap_t is SANA_ERR_UNSUPPORTED; a NULL state is
  * SANA_ERR_INVALID_ARG, an output or the workspace overlapping it too.
  * events may be NULL; otherwise n_events >= 3 and events[0..2] are recorded
  * before the q pass, after it and after the k/v pass.
@@ -361,9 +377,9 @@ sana_status_t sana_linattn_bwd_profiled(const void* q, const void* k, const void
 sana_status_t sana_linattn_bwd_state(const void* q, const void* k, const void* v,
                                      const void* dout, const float* state, void* dq, void* dk,
                                      void* dv, int64_t B, int64_t N, int64_t H, int64_t d,
-                                     float eps, sana_dtype_t dtype, void* workspace,
-                                     size_t workspace_bytes, hipEvent_t* events, int n_events,
-                                     hipStream_t stream);
+                                     float eps, sana_dtype_t dtype, sana_fmap_t fmap,
+                                     void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                                     int n_events, hipStream_t stream);
 
 /*
  * The backward pass of sana_linattn_fwd_fmap (bf16 only): the gradients of

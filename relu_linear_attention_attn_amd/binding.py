@@ -36,6 +36,7 @@ EXPORTS = (
     "sana_linattn_fwd_variant",
     "sana_linattn_fwd_profiled",
     "sana_linattn_kv_state",
+    "sana_linattn_kv_state_fmap",
     "sana_linattn_apply",
     "sana_linattn_state_size",
     "sana_linattn_bwd_workspace_size",
@@ -119,7 +120,10 @@ def lib() -> ctypes.CDLL:
         L.sana_linattn_bwd_profiled.argtypes = [_vp] * 7 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
         L.sana_linattn_bwd_state.argtypes = [_vp] * 8 + [_i64] * 4 + [
-            ctypes.c_float, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp), ctypes.c_int, _vp]
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
+            ctypes.c_int, _vp]
+        L.sana_linattn_kv_state_fmap.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                                 ctypes.c_int, ctypes.c_int, _vp, _sz, _vp]
         L.sana_linattn_bwd_fmap.argtypes = [_vp] * 7 + [_i64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _sz, ctypes.POINTER(_vp),
             ctypes.c_int, _vp]
@@ -146,6 +150,7 @@ def lib() -> ctypes.CDLL:
                      "sana_linattn_fwd_block_causal_profiled", "sana_linattn_causal_workspace_size",
                      "sana_linattn_fwd_causal", "sana_linattn_fwd_fmap",
                      "sana_linattn_bwd_fmap", "sana_linattn_bwd_state",
+                     "sana_linattn_kv_state_fmap",
                      "sana_linattn_fwd_strided",
                      "sana_linattn_qkv_workspace_size", "sana_linattn_qkv_fwd"):
             getattr(L, name).restype = ctypes.c_int
@@ -316,8 +321,11 @@ def forward_profiled(q, k, v, events, eps: float = 1e-6, heads: Optional[int] = 
     return out, nk.value
 
 
-def kv_state(k, v, heads: Optional[int] = None, state=None, workspace=None):
-    """The fp32 [B, H, d, d+1] state phi(K)^T [V | 1] of every (b, h)."""
+def kv_state(k, v, heads: Optional[int] = None, state=None, workspace=None, fmap: str = "relu"):
+    """The fp32 [B, H, d, d+1] state phi(K)^T [V | 1] of every (b, h), for
+    the feature map fmap ("relu", "elu1", "cos")."""
+    if fmap not in FMAPS:
+        raise ValueError(f"unknown feature map {fmap!r}; one of {sorted(FMAPS)}")
     torch = _torch()
     B, N, H, d = _shape(k, heads)
     _check_tensor(k, "k")
@@ -330,11 +338,18 @@ def kv_state(k, v, heads: Optional[int] = None, state=None, workspace=None):
         raise ValueError("state must be a contiguous fp32 tensor of B*H*d*(d+1) elements")
     if workspace is None:
         workspace = alloc_workspace(B, N, H, dt, k.device)
-    _check(lib().sana_linattn_kv_state(k.data_ptr(), v.data_ptr(), state.data_ptr(), B, N, H, d,
-                                       dt, workspace.data_ptr(),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream(k)),
-           "sana_linattn_kv_state")
+    if fmap == "relu":
+        _check(lib().sana_linattn_kv_state(k.data_ptr(), v.data_ptr(), state.data_ptr(), B, N, H,
+                                           d, dt, workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(k)),
+               "sana_linattn_kv_state")
+    else:
+        _check(lib().sana_linattn_kv_state_fmap(k.data_ptr(), v.data_ptr(), state.data_ptr(), B,
+                                                N, H, d, dt, FMAPS[fmap], workspace.data_ptr(),
+                                                workspace.numel() * workspace.element_size(),
+                                                _stream(k)),
+               "sana_linattn_kv_state_fmap")
     return state
 
 
@@ -374,13 +389,11 @@ def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grad
     events; 3 with a state). fmap: the forward's feature map ("relu",
     "elu1", "cos"; anything but "relu" calls sana_linattn_bwd_fmap). state:
     optional saved forward state, the fp32 (B, H, d, d + 1) tensor of
-    kv_state(k, v) (ReLU only; calls sana_linattn_bwd_state, which skips the
+    kv_state(k, v, fmap=fmap) (calls sana_linattn_bwd_state, which skips the
     state reduction). Enqueued on torch's current stream; no
     synchronisation."""
     if fmap not in FMAPS:
         raise ValueError(f"unknown feature map {fmap!r}; one of {sorted(FMAPS)}")
-    if state is not None and fmap != "relu":
-        raise ValueError("a saved state is taken by the ReLU backward only")
     torch = _torch()
     B, N, H, d = _shape(q, heads)
     _check_tensor(q, "q")
@@ -404,8 +417,8 @@ def backward(q, k, v, dout, eps: float = 1e-6, heads: Optional[int] = None, grad
                              "q's device")
         arr, n = _event_array(events)
         _check(lib().sana_linattn_bwd_state(*ptrs[:4], state.data_ptr(), *ptrs[4:], B, N, H, d,
-                                            float(eps), dt, workspace.data_ptr(), wb, arr, n,
-                                            _stream(q)), "sana_linattn_bwd_state")
+                                            float(eps), dt, FMAPS[fmap], workspace.data_ptr(), wb,
+                                            arr, n, _stream(q)), "sana_linattn_bwd_state")
     elif fmap != "relu":
         arr, n = _event_array(events)
         _check(lib().sana_linattn_bwd_fmap(*ptrs, B, N, H, d, float(eps), dt, FMAPS[fmap],

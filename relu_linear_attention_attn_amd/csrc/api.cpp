@@ -728,7 +728,7 @@ sana_status_t qkv_forward(const void* x, const void* w, void* q, void* out, int6
 // The backward pass (bf16): the forward state reduction (partials only),
 // bwd_q (dq and the [dS | dz] partials), bwd_kv (dk, dv). events (may be
 // NULL) are recorded before the first kernel and after each one. With a
-// saved forward state (state != NULL: fp32 [B][H][d][d+1], ReLU), the
+// saved forward state (with_state: fp32 [B][H][d][d+1] of the same map), the
 // reduction is skipped and bwd_q reads that state.
 sana_status_t backward(const void* q, const void* k, const void* v, const void* g, void* dq,
                        void* dk, void* dv, int64_t B, int64_t N, int64_t H, int64_t d, float eps,
@@ -880,9 +880,18 @@ sana_status_t sana_linattn_fwd(const void* q, const void* k, const void* v, void
 sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, int64_t B,
                                     int64_t N, int64_t H, int64_t d, sana_dtype_t dtype, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
+  return sana_linattn_kv_state_fmap(k, v, state, B, N, H, d, dtype, SANA_FMAP_RELU, workspace,
+                                    workspace_bytes, stream);
+}
+
+sana_status_t sana_linattn_kv_state_fmap(const void* k, const void* v, float* state, int64_t B,
+                                         int64_t N, int64_t H, int64_t d, sana_dtype_t dtype,
+                                         sana_fmap_t fmap, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
   size_t tb = 0;
   sana_status_t s = sana::check_shape(B, N, H, d, dtype, &tb);
   if (s != SANA_OK) return s;
+  if (!sana::valid_fmap(fmap)) return SANA_ERR_UNSUPPORTED;
   if (!k || !v || !state) return SANA_ERR_INVALID_ARG;
   if (sana::misaligned(k) || sana::misaligned(v) || sana::misaligned(state))
     return SANA_ERR_ALIGNMENT;
@@ -899,7 +908,7 @@ sana_status_t sana_linattn_kv_state(const void* k, const void* v, float* state, 
   sana::fit_plan_to_device(fp, dtype);
   const sana::WorkspaceParts w = sana::split_workspace(fp, workspace);
   return sana::to_status(sana::launch_reduce(fp, dtype, true, k, v, w.partials, state, w.ctl,
-                                             sana::next_epoch(), stream));
+                                             sana::next_epoch(), stream, fmap));
 }
 
 sana_status_t sana_linattn_apply(const void* q, const float* state, void* out, int64_t B,
@@ -963,11 +972,11 @@ sana_status_t sana_linattn_bwd_fmap(const void* q, const void* k, const void* v,
 sana_status_t sana_linattn_bwd_state(const void* q, const void* k, const void* v,
                                      const void* dout, const float* state, void* dq, void* dk,
                                      void* dv, int64_t B, int64_t N, int64_t H, int64_t d,
-                                     float eps, sana_dtype_t dtype, void* workspace,
-                                     size_t workspace_bytes, hipEvent_t* events, int n_events,
-                                     hipStream_t stream) {
+                                     float eps, sana_dtype_t dtype, sana_fmap_t fmap,
+                                     void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                                     int n_events, hipStream_t stream) {
   return sana::backward(q, k, v, dout, dq, dk, dv, B, N, H, d, eps, dtype, workspace,
-                        workspace_bytes, events, n_events, stream, SANA_FMAP_RELU, state, true);
+                        workspace_bytes, events, n_events, stream, fmap, state, true);
 }
 
 sana_status_t sana_linattn_block_causal_workspace_size(int64_t B, int64_t N, int64_t H,

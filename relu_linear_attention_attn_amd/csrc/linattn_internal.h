@@ -83,7 +83,7 @@ int block_waves(KernelKind kind, int dtype);  // waves per block
 // partials; with fold (always for fp32) the last block of each head pair
 // also folds them into `state`, without (bf16) the partials are the result
 // and launch_apply_partials sums them where it needs them.
-// fmap is the feature map (sana_fmap_t; the bf16 fold is ReLU only).
+// fmap is the feature map (sana_fmap_t).
 // keep_k (bf16 partials only): k is read with ordinary loads, which leave
 // much of it in the Infinity Cache for a later pass that reads it again (the
 // backward's k/v pass); otherwise k and v with streaming loads.

@@ -2431,12 +2431,11 @@ hipError_t launch_reduce(const Plan& p, int dtype, bool fold, const void* k, con
                          float* partials, float* state, unsigned long long* ctl,
                          unsigned long long epoch, hipStream_t stream, int fmap, bool keep_k) {
   const int64_t BH = p.B * p.H;
-  if (dtype == 1 && fold && fmap != kFmapRelu) return hipErrorInvalidValue;
   if (dtype != 1 && !fold) return hipErrorInvalidValue;
   return with_fmap(fmap, [&](auto fm) {
     constexpr int Fm = decltype(fm)::value;
     if (dtype == 1) {
-      auto* kernel = fold      ? reduce_bf16_kernel<kRedS, kRedU, true, kFmapRelu>
+      auto* kernel = fold      ? reduce_bf16_kernel<kRedS, kRedU, true, Fm>
                      : keep_k  ? reduce_bf16_kernel<kRedS, kRedU, false, Fm, true>
                                : reduce_bf16_kernel<kRedS, kRedU, false, Fm>;
       const bool chunked = p.red_cb > 0;

@@ -258,10 +258,10 @@ def test_bwd_fmap_rejects_invalid_arguments(L):
 
 
 def bwd_state(L, state=P_W + (1 << 29), q=P_Q, k=P_K, v=P_V, g=P_G, dq=P_DQ, dk=P_DK, dv=P_DV,
-              B=1, N=64, H=2, d=32, eps=1e-6, dt=BF16, ws=P_W, wsb=1 << 20, events=None,
+              B=1, N=64, H=2, d=32, eps=1e-6, dt=BF16, fmap=0, ws=P_W, wsb=1 << 20, events=None,
               n_events=0):
-    return L.sana_linattn_bwd_state(q, k, v, g, state, dq, dk, dv, B, N, H, d, eps, dt, ws, wsb,
-                                    events, n_events, None)
+    return L.sana_linattn_bwd_state(q, k, v, g, state, dq, dk, dv, B, N, H, d, eps, dt, fmap, ws,
+                                    wsb, events, n_events, None)
 
 
 def test_bwd_state_rejects_invalid_arguments(L):
@@ -286,6 +286,22 @@ def test_bwd_state_rejects_invalid_arguments(L):
     assert bwd_state(L, events=events, n_events=2) == INVALID
     events3 = (ctypes.c_void_p * 3)(None, None, None)
     assert bwd_state(L, events=events3, n_events=3) == INVALID  # NULL events
+    for fmap in (-1, 3):
+        assert bwd_state(L, fmap=fmap) == UNSUPPORTED
+    for fmap in (1, 2):
+        assert bwd_state(L, fmap=fmap, state=None) == INVALID
+
+
+def test_kv_state_fmap_rejects_invalid_arguments(L):
+    kv = L.sana_linattn_kv_state_fmap
+    for fmap in (-1, 3):
+        assert kv(P_K, P_V, P_O, 1, 64, 2, 32, BF16, fmap, P_W, 1 << 20, None) == UNSUPPORTED
+    for fmap in (0, 1, 2):
+        assert kv(P_K, P_V, P_O, 0, 64, 2, 32, BF16, fmap, P_W, 1 << 20, None) == INVALID
+        assert kv(None, P_V, P_O, 1, 64, 2, 32, BF16, fmap, P_W, 1 << 20, None) == INVALID
+        assert kv(P_K, P_V, P_O + 8, 1, 64, 2, 32, BF16, fmap, P_W, 1 << 20, None) == ALIGNMENT
+        assert kv(P_K, P_V, P_K, 1, 64, 2, 32, BF16, fmap, P_W, 1 << 20, None) == INVALID
+        assert kv(P_K, P_V, P_O, 1, 64, 2, 16, BF16, fmap, P_W, 1 << 20, None) == UNSUPPORTED
 
 
 def bcws(L, B, N, H, blk, d=32, dt=BF16):

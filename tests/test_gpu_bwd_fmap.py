@@ -180,3 +180,37 @@ def test_bwd_fmap_rejects_unknown_map():
     x, dev = _inputs(w)
     with pytest.raises(ValueError):
         R.backward(dev["q"], dev["k"], dev["v"], dev["g"], fmap="gelu")
+
+
+@pytest.mark.parametrize("fmap", ["elu1", "cos"])
+@pytest.mark.parametrize("B,N,H", [(1, 1, 1), (2, 257, 3), (2, 5000, 7), (16, 1024, 70)])
+def test_bwd_fmap_from_saved_state(B, N, H, fmap):
+    """kv_state with the map (the folding state reduction) against the oracle's
+    state, and the backward from that saved state bitwise as the recomputing
+    feature-map backward."""
+    import oracle.linattn_feature_maps as FM
+
+    w = W.custom(f"bwdfm_state_{B}_{N}_{H}", B, N, H, seed=950 + N + H,
+                 q=W.Dist("normal", 0.1, 1.0), k=W.Dist("normal", 0.1, 1.0))
+    print(f"\n[case] bwd {fmap} from saved state B={B} N={N} H={H}", flush=True)
+    x, dev = _inputs(w)
+    state = R.kv_state(dev["k"], dev["v"], fmap=fmap)
+    torch().cuda.synchronize()
+    got = state.cpu().numpy().astype(np.float64)
+    kd, vd = decode(x["k"], "bf16"), decode(x["v"], "bf16")
+    for b in range(B):
+        for h in range(H):
+            kv, ks = FM.state_head(kd[b, :, h], vd[b, :, h], fmap)
+            ref = np.concatenate([kv, ks[:, None]], axis=1)
+            ak = np.abs(_phi(kd[b, :, h], fmap))
+            scale = np.concatenate([ak.T @ np.abs(vd[b, :, h]), ak.sum(axis=0)[:, None]], axis=1)
+            # 1e-5 of the terms (hi + lo products, fp32 sums, exp within 2e-6 relative) plus
+            # 1e-6 per token of |v| (cos within 4e-7 absolute, also where cos is near 0)
+            absv = np.concatenate([np.abs(vd[b, :, h]).sum(axis=0), [float(N)]])[None, :]
+            err = np.abs(got[b, h] - ref)
+            assert np.all(err <= 1e-5 * scale + 1e-6 * absv), (b, h, float(err.max()))
+    a = _run(w, dev, fmap)
+    grads = R.backward(dev["q"], dev["k"], dev["v"], dev["g"], eps=w.eps, fmap=fmap, state=state)
+    torch().cuda.synchronize()
+    for name, s, t in zip(("dq", "dk", "dv"), a, grads):
+        assert np.array_equal(s, to_host(t, "bf16")), name

@@ -104,7 +104,7 @@ def _bwd_state_case(B, N, H):
     def call(t, ws_t):
         return lib.sana_linattn_bwd_state(_p(t["q"]), _p(t["k"]), _p(t["v"]), _p(t["g"]),
                                           _p(t["s"]), _p(t["dq"]), _p(t["dk"]), _p(t["dv"]), B, N,
-                                          H, 32, 1e-6, BF16, _p(ws_t), ws_t.numel(), None, 0,
+                                          H, 32, 1e-6, BF16, 0, _p(ws_t), ws_t.numel(), None, 0,
                                           _stream())
     inputs = {c: (shape, BF16) for c in "qkvg"}
     inputs["s"] = ((B, H, 32, 33), F32)  # a state; replays only need it fixed per replay
