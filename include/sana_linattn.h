@@ -110,7 +110,9 @@ typedef enum {
                               then apply; for short sequences */
 } sana_variant_t;
 
-/* Feature maps phi for sana_linattn_fwd_fmap (Sana course notes, "Linear
+/* Feature maps phi for sana_linattn_fwd_fmap, sana_linattn_fwd_strided,
+ * sana_linattn_bwd_fmap, sana_linattn_bwd_state and sana_linattn_kv_state_fmap
+ * (Sana course notes, "Linear
  * Attention 的原理": ReLU, or another non-linear kernel such as ELU + 1 or
  * cos, chosen by a kernel-function parameter). Applied element by element. */
 typedef enum {
